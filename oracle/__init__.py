@@ -1,0 +1,21 @@
+"""CPU oracle for the Mixture-of-Experts router.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark; never by the product package. It shares no
+code with the HIP library. The arithmetic lives in ``moero.c`` (plain C,
+fp64); this package only builds it and marshals numpy arrays.
+"""
+from .api import (  # noqa: F401
+    SIGMOID,
+    SOFTMAX,
+    affinities,
+    agg_entropy,
+    bias_update,
+    build_oracle,
+    layout,
+    load_stats,
+    num_threads,
+    route,
+    scores,
+    select,
+)

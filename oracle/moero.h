@@ -1,0 +1,106 @@
+/*
+ * moero.h — CPU oracle for the Mixture-of-Experts router.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this code: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it. It shares no code with the HIP library.
+ *
+ * Plain, slow and obviously correct: fp64 wherever the pages do not fix a
+ * precision; fp32 only where the routing decision itself is defined on fp32
+ * values (selection keys, group scores, the bias update), so that a GPU given
+ * the same fp32 scores must reproduce the decision bit for bit.
+ *
+ * Sources (the five web pages the method is described on):
+ *  [P1] dailyaiworld.com, "MoE Routing Entropy vs Expert Saturation:
+ *       Optimizing DeepSeek V4 Load Balancing" — section "The Mathematics:
+ *       Router Entropy and Gating Imbalance" (logits h = x·W_g, softmax,
+ *       Shannon routing entropy in bits) and the code listing "Dynamic Expert
+ *       Bias Routing Controller" (top-k, renormalisation, bincount, bias).
+ *  [P2] blog.hotdry.top, "DeepSeek V4 MoE load balancing" — sections on
+ *       token routing / top-K (sigmoid gating, weighted combine) and on
+ *       auxiliary-loss-free balancing (per-expert bias added to the affinity
+ *       score for the routing decision; lowered when overloaded, raised when
+ *       underloaded); deployment section (std/mean of activation frequency).
+ *  [P3] cnnetsun.cn, "DeepSeek-V3 Group-Limited Expert Routing" — section 1
+ *       (256 experts in 8 groups of 32, keep the best 4 groups, pick 8 of
+ *       their 128), section 3 (Gate.forward: view scores as groups, top-k
+ *       groups, mask the other groups, top-k experts), section 4 (decode:
+ *       no groups, the shared expert counted as a routed slot, 9 per token).
+ *  [P4] tech-blog-chi.vercel.app, "A minimal experiment in expert-load
+ *       imbalance" — "Run the example" (total, mean, max/mean imbalance,
+ *       capacity = max·N) and "Expected output" (the worked example).
+ *  [P5] hiascend.com, MindIE "expert parallelism load balancer" — forcible
+ *       load balancing: replace the top-k output by supplied indices.
+ */
+#ifndef MOERO_H
+#define MOERO_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MOERO_SOFTMAX = 0, MOERO_SIGMOID = 1 };
+
+typedef struct {
+  int32_t T;            /* tokens */
+  int32_t N;            /* routed experts */
+  int32_t K;            /* routed experts chosen per token */
+  int32_t n_groups;     /* G: contiguous expert groups (1 = no group limit) */
+  int32_t topk_groups;  /* Gk: groups kept per token */
+  int32_t n_shared;     /* shared-expert slots appended after the K routed */
+} moero_cfg;
+
+typedef struct {
+  int64_t total, max_load, argmax, capacity;
+  double mean, imbalance, h_load_bits, cv;
+} moero_stats;
+
+/* Gate affinities, [P1] Mathematics: h[t][e] = sum_k x[t][k]*W[e][k] (+ o[e]).
+ * x [T][d], W [N][d] (fp32 holding exactly the bf16/fp32 input values),
+ * offset [N] or NULL; h [T][N] fp64, summed in ascending k. */
+void moero_affinities(const float* x, const float* W, const float* offset,
+                      int32_t T, int32_t d, int32_t N, double* h);
+
+/* Scores from affinities: softmax over experts ([P1] Mathematics) or the
+ * element-wise logistic sigmoid ([P2] routing section). fp64 in and out. */
+void moero_scores(const double* h, int32_t T, int32_t N, int32_t score_fn, double* s);
+
+/* Selection for every token ([P3] s.1/s.3/s.4, [P2] bias, [P1] renorm).
+ * s32 [T][N]: the fp32 scores the decision is taken on; s64 [T][N]: the same
+ * scores at full precision (weights, entropy); bias [N] or NULL.
+ * Outputs (each may be NULL): idx [T][Kt] int32, w [T][Kt] fp32,
+ * tok_H [T] fp64 bits, gap [T] fp64 (smallest score margin that decides the
+ * selection or its order; +inf when nothing competes). Returns 0, or -1 when
+ * the configuration is invalid. */
+int moero_select(const moero_cfg* cfg, const float* s32, const double* s64,
+                 const float* bias, int32_t* idx, float* w, double* tok_H,
+                 double* gap);
+
+/* Aggregate routing entropy ([P1] Mathematics and compute_routing_entropy):
+ * the entropy in bits of the batch-mean of the per-token distributions
+ * q[t][e] = s[t][e] / sum_e s[t][e]. 0 for T == 0. */
+double moero_agg_entropy(const double* s64, int32_t T, int32_t N);
+
+/* Dispatch layout over Nb buckets for idx [T][Kt]: counts [Nb], exclusive
+ * offsets [Nb+1], perm [T*Kt] ordered by (expert, token, slot) holding flat
+ * slot ids t*Kt+k, and inv_perm [T*Kt] (may be NULL). Entries outside
+ * [0, Nb) are not placed; their inv_perm is -1 and the unused tail of perm
+ * is -1. */
+void moero_layout(const int32_t* idx, int32_t T, int32_t Kt, int32_t Nb,
+                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm);
+
+/* Load statistics over routed experts [P4] Run the example, [P1] entropy,
+ * [P2] deployment section (std/mean). */
+void moero_load_stats(const int32_t* counts, int32_t N, moero_stats* out);
+
+/* Sign-step bias update ([P2] auxiliary-loss-free balancing):
+ * b[e] += u * sign(mean_load - load[e]), sign(0) = 0, in fp32. */
+void moero_bias_update(float* bias, const int32_t* counts, int32_t N, float u);
+
+int moero_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
