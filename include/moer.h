@@ -1,0 +1,183 @@
+/*
+ * moer.h — C ABI of the MI355X (gfx950) Mixture-of-Experts router.
+ *
+ * Three calls make up the router's hot path:
+ *   moer_route        gate affinities -> scores -> bias-aware group-limited
+ *                     top-k -> combine weights -> routing entropy ->
+ *                     dispatch layout (counts, offsets, stable permutation)
+ *   moer_load_stats   load statistics of the realised per-expert counts
+ *   moer_bias_update  sign-step update of the per-expert selection bias
+ *
+ * The method is the one described on these web pages (cited by title and
+ * section throughout):
+ *  - "MoE Routing Entropy vs Expert Saturation: Optimizing DeepSeek V4 Load
+ *    Balancing" (dailyaiworld.com): section "The Mathematics: Router Entropy
+ *    and Gating Imbalance" (h = x·W_g, softmax, Shannon entropy in bits) and
+ *    the listing "Dynamic Expert Bias Routing Controller" (top-k,
+ *    renormalised weights, per-expert bincount, bias buffer).
+ *  - "DeepSeek V4 MoE load balancing" (blog.hotdry.top): token routing and
+ *    top-K section (sigmoid gating, weighted combine), auxiliary-loss-free
+ *    balancing section (per-expert bias added to the affinity score for the
+ *    routing decision; lowered for overloaded, raised for underloaded
+ *    experts), DeepEP section (dispatch groups tokens by destination expert).
+ *  - "DeepSeek-V3 Group-Limited Expert Routing" (cnnetsun.cn): section 1
+ *    (256 experts in 8 groups of 32; keep the best 4 groups; choose 8 experts
+ *    among their 128), section 3 (Gate.forward: view the scores as groups,
+ *    top-k groups, mask the rest, top-k experts), section 4 (decode: no
+ *    group limit; the shared expert counts as a routed slot, 9 per token).
+ *  - "A minimal experiment in expert-load imbalance" (tech-blog-chi):
+ *    "Run the example" (imbalance = max/mean, capacity = max x experts).
+ *  - MindIE "expert parallelism load balancer" (hiascend.com): forcible
+ *    balancing replaces the top-k output with supplied indices.
+ *
+ * Conventions for every call
+ *  - All array arguments are DEVICE pointers, owned by the caller, row-major
+ *    and contiguous. The library allocates nothing and keeps no state other
+ *    than a thread-local error string; scratch memory is the caller's
+ *    workspace (size from moer_route_workspace_bytes).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *    enqueue work on it and never wait for the device; outputs are valid
+ *    once the stream has reached them.
+ *  - Arguments are validated on the host before anything is enqueued. On
+ *    error nothing is enqueued, the status is returned and moer_last_error()
+ *    says why. Nothing throws across this ABI.
+ *  - Identical inputs give bitwise-identical outputs (fixed reduction
+ *    orders, no floating-point atomics).
+ *  - Inputs must be finite; NaN or infinite scores give unspecified (but
+ *    memory-safe) results.
+ */
+#ifndef MOER_H
+#define MOER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOER_ABI_VERSION 1
+#define MOER_MAX_EXPERTS 256 /* N */
+#define MOER_MAX_SLOTS 16    /* Kt = K + n_shared */
+
+typedef enum {
+  MOER_OK = 0,
+  MOER_EINVAL = 1,       /* invalid argument (see moer_last_error) */
+  MOER_EUNSUPPORTED = 2, /* valid, but a shape these kernels do not take */
+  MOER_EWORKSPACE = 3,   /* workspace missing or smaller than required */
+  MOER_EHIP = 4          /* the HIP runtime refused a launch */
+} moer_status;
+
+typedef enum {
+  MOER_SOFTMAX = 0, /* p_e = exp(h_e) / sum_j exp(h_j)  (dailyaiworld, Mathematics) */
+  MOER_SIGMOID = 1  /* s_e = 1 / (1 + exp(-h_e))        (hotdry, token routing)    */
+} moer_score_fn;
+
+typedef enum { MOER_BF16 = 0, MOER_F32 = 1 } moer_dtype;
+
+typedef enum {
+  MOER_IN_HIDDEN = 0,  /* x and W_g given: full path from the gate GEMM      */
+  MOER_IN_SCORES = 1,  /* fp32 scores s [L][T][N] given: the GEMM is skipped */
+  MOER_IN_INDICES = 2  /* expert ids idx_in [L][T][Kt] given (MindIE's
+                          forcible balancing): only the layout is built      */
+} moer_input;
+
+/* Shape of one call. n_layers independent routers (each with its own x,
+ * W_g and bias) are processed by one call. */
+typedef struct {
+  int32_t n_layers;    /* L >= 1 */
+  int32_t T;           /* tokens per layer, >= 0 (0 = empty batch) */
+  int32_t d;           /* hidden size (HIDDEN mode); bf16 needs d % 8 == 0 */
+  int32_t N;           /* routed experts, 1..256 */
+  int32_t K;           /* routed experts chosen per token, 1..N */
+  int32_t n_groups;    /* G: N/G contiguous experts per group; 1 = no limit */
+  int32_t topk_groups; /* Gk: groups kept per token, 1..G, Gk*(N/G) >= K */
+  int32_t n_shared;    /* shared-expert slots appended after the K routed */
+  int32_t score_fn;    /* moer_score_fn */
+  int32_t dtype;       /* moer_dtype of x and W_g (HIDDEN mode) */
+  int32_t input;       /* moer_input */
+} moer_route_desc;
+
+/* Buffers of one call (device pointers; Kt = K + n_shared, Nb = N + n_shared).
+ * "req" = required in the modes that produce it; "opt" = may be NULL. */
+typedef struct {
+  const void* x;             /* HIDDEN: [L][T][d] bf16 or fp32 hidden states */
+  const void* w_gate;        /* HIDDEN: [L][N][d] gate weights, same dtype;
+                                row e is expert e's vector (nn.Linear layout) */
+  const float* scores;       /* SCORES: [L][T][N] fp32 scores s (or p) */
+  const int32_t* idx_in;     /* INDICES: [L][T][Kt] expert ids; ids outside
+                                [0, Nb) are not placed (see perm) */
+  const float* bias;         /* opt [L][N] fp32 selection bias b_e (NULL = 0) */
+  const float* logit_offset; /* opt [N] fp32 added to every layer's h (HIDDEN) */
+  float* h_out;              /* opt [L][T][N] fp32 affinities h (HIDDEN) */
+  float* topk_w;             /* req [L][T][Kt] combine weights (not INDICES) */
+  float* tok_entropy;        /* opt [L][T] per-token routing entropy, bits */
+  float* agg_entropy;        /* opt [L] entropy of the batch-mean distribution */
+  int32_t* topk_idx;         /* req [L][T][Kt] expert ids (not INDICES) */
+  int32_t* counts;           /* req [L][Nb] assignments per expert */
+  int32_t* offsets;          /* req [L][Nb+1] exclusive prefix of counts;
+                                offsets[Nb] = assignments placed */
+  int32_t* perm;             /* req [L][T*Kt] flat slot ids t*Kt+k ordered by
+                                (expert, token, slot); positions past
+                                offsets[Nb] hold -1 */
+  int32_t* inv_perm;         /* opt [L][T*Kt] position of each slot in perm,
+                                -1 for ids that were not placed */
+  void* ev_gemm_begin;       /* opt hipEvent_t recorded just before the gate */
+  void* ev_gemm_end;         /* GEMM launch and just after it (profiling)   */
+} moer_route_io;
+
+/* Per-layer record written by moer_load_stats (device memory, 64 bytes). */
+typedef struct {
+  int64_t total;      /* sum of counts over the N routed experts */
+  int64_t max_load;   /* largest count */
+  int64_t argmax;     /* expert with the largest count (lowest id on ties) */
+  int64_t capacity;   /* max_load * N: fixed per-expert capacity that fits */
+  double mean;        /* total / N */
+  double imbalance;   /* max_load / mean, 0 when mean == 0 */
+  double h_load_bits; /* entropy (bits) of counts/total, 0 when total == 0 */
+  double cv;          /* population std of counts / mean, 0 when mean == 0 */
+} moer_load_stats_t;
+
+/* Bytes of workspace moer_route needs for `desc` (0 on an invalid desc). */
+size_t moer_route_workspace_bytes(const moer_route_desc* desc);
+
+/* The router: for each layer l and token t
+ *   h      = x[t] . W_g^T (+ logit_offset)         fp32 accumulation (MFMA)
+ *   s      = softmax(h) or sigmoid(h)              (or the given scores)
+ *   key_e  = s_e + b_e                             fp32, selection only
+ *   if G > 1: group score = sum of the group's two largest keys; keep the
+ *             Gk best groups (score desc, group id asc); others ineligible
+ *   slots 0..K-1 = the K best eligible keys (key desc, expert id asc)
+ *   slots K..Kt-1 = shared experts N..Nb-1 with weight 1
+ *   w_k    = s_k / sum of the chosen s            (unbiased scores)
+ *   tok_entropy = entropy (bits) of s / sum_e s over the N experts
+ *   agg_entropy = entropy (bits) of the mean over tokens of s / sum_e s
+ * then the dispatch layout over Nb buckets (counts, offsets, perm,
+ * inv_perm), stable in (token, slot) order within an expert.
+ * Workspace: device memory of at least moer_route_workspace_bytes(desc)
+ * bytes, any contents; it is clobbered. Returns MOER_OK or an error status. */
+moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Load statistics ("A minimal experiment in expert-load imbalance", Run the
+ * example; entropy per the dailyaiworld Mathematics section; std/mean per
+ * the hotdry deployment section) of counts[l*stride + e], e < N, for each of
+ * n_layers layers, written to out_dev[l] (device memory). stride >= N. */
+moer_status moer_load_stats(const int32_t* counts, int32_t n_layers, int32_t N,
+                            int32_t stride, moer_load_stats_t* out_dev, void* stream);
+
+/* Sign-step bias update (hotdry, auxiliary-loss-free balancing), in place:
+ *   bias[l*N + e] += u * sign(mean_l - counts[l*stride + e])
+ * with mean_l = (sum_e counts) / N compared exactly (in integers) and
+ * sign(0) = 0; one fp32 rounding per expert. stride >= N. */
+moer_status moer_bias_update(float* bias, const int32_t* counts, int32_t n_layers,
+                             int32_t N, int32_t stride, float u, void* stream);
+
+const char* moer_status_str(moer_status status);
+const char* moer_last_error(void);
+int moer_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOER_H */

@@ -1,0 +1,112 @@
+"""MI355X-native Mixture-of-Experts router (gfx950 HIP kernels behind a C ABI).
+
+The C-ABI entry points (include/moer.h) are re-exported under their own names
+(``moer_route``, ``moer_load_stats``, ``moer_bias_update``, ...). ``route``,
+``load_stats`` and ``bias_update`` are conveniences that allocate the output
+tensors with torch and pass the current stream; all routing work runs in the
+library's kernels.
+"""
+import torch
+
+from ._moer import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    LOAD_STATS_FIELDS,
+    MOER_BF16,
+    MOER_EHIP,
+    MOER_EINVAL,
+    MOER_EUNSUPPORTED,
+    MOER_EWORKSPACE,
+    MOER_F32,
+    MOER_IN_HIDDEN,
+    MOER_IN_INDICES,
+    MOER_IN_SCORES,
+    MOER_MAX_EXPERTS,
+    MOER_MAX_SLOTS,
+    MOER_OK,
+    MOER_SIGMOID,
+    MOER_SOFTMAX,
+    MoerError,
+    MoerRouteDesc,
+    decode_load_stats,
+    make_desc,
+    moer_abi_version,
+    moer_bias_update,
+    moer_load_stats,
+    moer_route,
+    moer_route_workspace_bytes,
+)
+
+_SCORE_FN = {"softmax": MOER_SOFTMAX, "sigmoid": MOER_SIGMOID}
+
+
+def _layers(t, rank):
+    """View a [T,...] tensor as [1,T,...] (a single router layer)."""
+    return t if t is None or t.dim() == rank else t.unsqueeze(0)
+
+
+def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups=1, n_shared=0,
+          bias=None, logit_offset=None, scores=None, idx_in=None, N=None, want_h=False,
+          want_inv_perm=True, want_entropy=True, workspace=None, stream=None):
+    """Route a batch; returns a dict of device tensors, each with a leading
+    layer dimension L.
+
+    Input (one of): x [L,T,d] with w_gate [L,N,d] (bf16 or fp32), scores
+    [L,T,N] fp32, or idx_in [L,T,K+n_shared] int32 (N must then be given).
+    """
+    x, w_gate = _layers(x, 3), _layers(w_gate, 3)
+    scores, idx_in, bias = _layers(scores, 3), _layers(idx_in, 3), _layers(bias, 2)
+    if x is not None:
+        mode, (L, T, d), N = MOER_IN_HIDDEN, x.shape, w_gate.shape[1]
+        dev = x.device
+        dtype = MOER_BF16 if x.dtype == torch.bfloat16 else MOER_F32
+    elif scores is not None:
+        mode, (L, T, N), d, dev, dtype = MOER_IN_SCORES, scores.shape, 0, scores.device, MOER_BF16
+    else:
+        mode, (L, T, _), d, dev, dtype = MOER_IN_INDICES, idx_in.shape, 0, idx_in.device, MOER_BF16
+        if N is None:
+            raise ValueError("N is required with idx_in")
+    Kt, Nb = K + n_shared, N + n_shared
+    desc = make_desc(n_layers=L, T=T, d=d, N=N, K=K, n_groups=n_groups, topk_groups=topk_groups,
+                     n_shared=n_shared, score_fn=_SCORE_FN.get(score_fn, score_fn), dtype=dtype,
+                     input=mode)
+    i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+    out = {"counts": torch.empty(L, Nb, **i32), "offsets": torch.empty(L, Nb + 1, **i32),
+           "perm": torch.empty(L, T * Kt, **i32)}
+    if want_inv_perm:
+        out["inv_perm"] = torch.empty(L, T * Kt, **i32)
+    if mode != MOER_IN_INDICES:
+        out["topk_idx"] = torch.empty(L, T, Kt, **i32)
+        out["topk_w"] = torch.empty(L, T, Kt, **f32)
+        if want_entropy:
+            out["tok_entropy"] = torch.empty(L, T, **f32)
+            out["agg_entropy"] = torch.empty(L, **f32)
+    if want_h and mode == MOER_IN_HIDDEN:
+        out["h"] = torch.empty(L, T, N, **f32)
+    if workspace is None:
+        workspace = torch.empty(max(1, moer_route_workspace_bytes(desc)), dtype=torch.uint8,
+                                device=dev)
+    moer_route(desc, workspace=workspace, stream=stream, x=x, w_gate=w_gate, scores=scores,
+               idx_in=idx_in, bias=bias, logit_offset=logit_offset, h_out=out.get("h"),
+               topk_w=out.get("topk_w"), tok_entropy=out.get("tok_entropy"),
+               agg_entropy=out.get("agg_entropy"), topk_idx=out.get("topk_idx"),
+               counts=out["counts"], offsets=out["offsets"], perm=out["perm"],
+               inv_perm=out.get("inv_perm"))
+    return out
+
+
+def load_stats(counts, N, stream=None):
+    """Load statistics of counts [L, stride] over the first N columns; returns
+    the raw device records (uint8 [L, 64])."""
+    counts = _layers(counts, 2)
+    L, stride = counts.shape
+    out = torch.empty(L, 64, dtype=torch.uint8, device=counts.device)
+    moer_load_stats(counts, L, N, stride, out, stream)
+    return out
+
+
+def bias_update(bias, counts, u=1e-3, stream=None):
+    """In-place sign-step update of bias [L, N] from counts [L, stride]."""
+    bias2, counts2 = _layers(bias, 2), _layers(counts, 2)
+    moer_bias_update(bias2, counts2, bias2.shape[0], bias2.shape[1], counts2.shape[1], u, stream)
+    return bias

@@ -1,0 +1,176 @@
+"""ctypes binding of libmoer.so — argument marshalling only.
+
+The names match the C ABI in include/moer.h (moer_route, moer_load_stats,
+moer_bias_update, ...). Torch supplies device memory and the current stream;
+every step of the router runs in the library's HIP kernels. There is no
+fallback: if the library is not built, importing this module raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoer.so")
+
+MOER_OK, MOER_EINVAL, MOER_EUNSUPPORTED, MOER_EWORKSPACE, MOER_EHIP = range(5)
+MOER_SOFTMAX, MOER_SIGMOID = 0, 1
+MOER_BF16, MOER_F32 = 0, 1
+MOER_IN_HIDDEN, MOER_IN_SCORES, MOER_IN_INDICES = 0, 1, 2
+MOER_MAX_EXPERTS, MOER_MAX_SLOTS = 256, 16
+
+EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats", "moer_bias_update",
+            "moer_status_str", "moer_last_error", "moer_abi_version")
+
+
+class MoerRouteDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_layers", "T", "d", "N", "K", "n_groups", "topk_groups", "n_shared",
+                 "score_fn", "dtype", "input")]
+
+
+class MoerRouteIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("x", "w_gate", "scores", "idx_in", "bias", "logit_offset", "h_out", "topk_w",
+                 "tok_entropy", "agg_entropy", "topk_idx", "counts", "offsets", "perm",
+                 "inv_perm", "ev_gemm_begin", "ev_gemm_end")]
+
+
+class MoerLoadStats(ctypes.Structure):
+    _fields_ = [("total", ctypes.c_int64), ("max_load", ctypes.c_int64),
+                ("argmax", ctypes.c_int64), ("capacity", ctypes.c_int64),
+                ("mean", ctypes.c_double), ("imbalance", ctypes.c_double),
+                ("h_load_bits", ctypes.c_double), ("cv", ctypes.c_double)]
+
+
+LOAD_STATS_FIELDS = [n for n, _ in MoerLoadStats._fields_]
+assert ctypes.sizeof(MoerLoadStats) == 64
+
+
+class MoerError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(or python top_expert_routing_gate_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.moer_route_workspace_bytes.argtypes = [ctypes.POINTER(MoerRouteDesc)]
+    lib.moer_route_workspace_bytes.restype = ctypes.c_size_t
+    lib.moer_route.argtypes = [ctypes.POINTER(MoerRouteDesc), ctypes.POINTER(MoerRouteIO), P,
+                               ctypes.c_size_t, P]
+    lib.moer_route.restype = ctypes.c_int
+    lib.moer_load_stats.argtypes = [P, i32, i32, i32, P, P]
+    lib.moer_load_stats.restype = ctypes.c_int
+    lib.moer_bias_update.argtypes = [P, P, i32, i32, i32, ctypes.c_float, P]
+    lib.moer_bias_update.restype = ctypes.c_int
+    lib.moer_status_str.argtypes = [ctypes.c_int]
+    lib.moer_status_str.restype = ctypes.c_char_p
+    lib.moer_last_error.restype = ctypes.c_char_p
+    lib.moer_abi_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def _status_name(st):
+    return _lib.moer_status_str(st).decode()
+
+
+def _check(st):
+    if st != MOER_OK:
+        raise MoerError(st, _lib.moer_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("router buffers must be device tensors")
+    if not t.is_contiguous():
+        raise ValueError("router buffers must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def moer_abi_version():
+    return int(_lib.moer_abi_version())
+
+
+def make_desc(*, T, N, K, n_layers=1, d=0, n_groups=1, topk_groups=1, n_shared=0,
+              score_fn=MOER_SIGMOID, dtype=MOER_BF16, input=MOER_IN_HIDDEN):
+    return MoerRouteDesc(n_layers, T, d, N, K, n_groups, topk_groups, n_shared, score_fn, dtype,
+                         input)
+
+
+def moer_route_workspace_bytes(desc):
+    return int(_lib.moer_route_workspace_bytes(ctypes.byref(desc)))
+
+
+def moer_route(desc, *, workspace, stream=None, x=None, w_gate=None, scores=None, idx_in=None,
+               bias=None, logit_offset=None, h_out=None, topk_w=None, tok_entropy=None,
+               agg_entropy=None, topk_idx=None, counts=None, offsets=None, perm=None,
+               inv_perm=None, ev_gemm_begin=None, ev_gemm_end=None):
+    """Calls moer_route on device tensors (shapes and dtypes as in moer.h)."""
+    for name, t, dt in (("x", x, None), ("w_gate", w_gate, None), ("scores", scores, torch.float32),
+                        ("idx_in", idx_in, torch.int32), ("bias", bias, torch.float32),
+                        ("logit_offset", logit_offset, torch.float32),
+                        ("h_out", h_out, torch.float32), ("topk_w", topk_w, torch.float32),
+                        ("tok_entropy", tok_entropy, torch.float32),
+                        ("agg_entropy", agg_entropy, torch.float32),
+                        ("topk_idx", topk_idx, torch.int32), ("counts", counts, torch.int32),
+                        ("offsets", offsets, torch.int32), ("perm", perm, torch.int32),
+                        ("inv_perm", inv_perm, torch.int32)):
+        if t is not None and dt is not None and t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+    if x is not None:
+        want = torch.bfloat16 if desc.dtype == MOER_BF16 else torch.float32
+        if x.dtype != want or (w_gate is not None and w_gate.dtype != want):
+            raise TypeError(f"x and w_gate must be {want}")
+    io = MoerRouteIO(_ptr(x), _ptr(w_gate), _ptr(scores), _ptr(idx_in), _ptr(bias),
+                     _ptr(logit_offset), _ptr(h_out), _ptr(topk_w), _ptr(tok_entropy),
+                     _ptr(agg_entropy), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
+                     _ptr(inv_perm), ev_gemm_begin, ev_gemm_end)
+    ws = workspace
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.moer_route(ctypes.byref(desc), ctypes.byref(io), _ptr(ws), nbytes,
+                           _stream(stream)))
+
+
+def moer_load_stats(counts, n_layers, N, stride, out, stream=None):
+    """out: uint8 device tensor of n_layers*64 bytes (moer_load_stats_t records)."""
+    if counts.dtype != torch.int32:
+        raise TypeError("counts must be int32")
+    if out.numel() * out.element_size() < 64 * n_layers:
+        raise ValueError("out needs 64 bytes per layer")
+    _check(_lib.moer_load_stats(_ptr(counts), n_layers, N, stride, _ptr(out), _stream(stream)))
+
+
+def moer_bias_update(bias, counts, n_layers, N, stride, u, stream=None):
+    if bias.dtype != torch.float32 or counts.dtype != torch.int32:
+        raise TypeError("bias must be float32 and counts int32")
+    _check(_lib.moer_bias_update(_ptr(bias), _ptr(counts), n_layers, N, stride, u,
+                                 _stream(stream)))
+
+
+def decode_load_stats(raw):
+    """Host view of moer_load_stats_t records (raw: CPU uint8 tensor)."""
+    b = bytes(raw.contiguous().numpy().tobytes())
+    out = []
+    for i in range(len(b) // 64):
+        rec = MoerLoadStats.from_buffer_copy(b[i * 64:(i + 1) * 64])
+        out.append({n: getattr(rec, n) for n in LOAD_STATS_FIELDS})
+    return out

@@ -1,0 +1,258 @@
+// Host side of the C ABI (include/moer.h): argument validation, workspace
+// carving, and the stream-ordered launch sequence. No host synchronisation,
+// no allocation, no global state besides the thread-local error string.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/moer.h"
+#include "moer_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moer_status fail(moer_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moer_status ok() {
+  g_err[0] = '\0';
+  return MOER_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Workspace regions (byte offsets) for a validated descriptor.
+struct Plan {
+  int Kt, Nb, nsb, nlb;
+  size_t off_h, off_colpart, off_colpart2, off_cnt, total;
+};
+
+Plan make_plan(const moer_route_desc& d, bool want_h_ws, bool want_agg) {
+  Plan p{};
+  const size_t L = (size_t)d.n_layers;
+  p.Kt = d.K + d.n_shared;
+  p.Nb = d.N + d.n_shared;
+  p.nsb = (d.T + moer::kScoreTokens - 1) / moer::kScoreTokens;
+  p.nlb = d.T > 0 ? (d.T + moer::kLayoutTokens - 1) / moer::kLayoutTokens : 1;
+  size_t o = 0;
+  p.off_h = o;
+  if (want_h_ws) o += align_up(L * d.T * d.N * sizeof(float));
+  p.off_colpart = o;
+  if (want_agg) o += align_up(L * p.nsb * d.N * sizeof(float) + 4);
+  p.off_colpart2 = o;
+  if (want_agg) o += align_up(L * p.nlb * d.N * sizeof(float));
+  p.off_cnt = o;
+  o += align_up(L * p.nlb * p.Nb * sizeof(int32_t));
+  p.total = o;
+  return p;
+}
+
+moer_status validate_desc(const moer_route_desc* d) {
+  if (d == nullptr) return fail(MOER_EINVAL, "desc is NULL");
+  if (d->n_layers < 1) return fail(MOER_EINVAL, "n_layers must be >= 1 (got %d)", d->n_layers);
+  if (d->T < 0) return fail(MOER_EINVAL, "T must be >= 0 (got %d)", d->T);
+  if (d->N < 1 || d->N > MOER_MAX_EXPERTS)
+    return fail(MOER_EINVAL, "N must be in [1, %d] (got %d)", MOER_MAX_EXPERTS, d->N);
+  if (d->K < 1 || d->K > d->N) return fail(MOER_EINVAL, "K must be in [1, N] (got %d)", d->K);
+  if (d->n_shared < 0) return fail(MOER_EINVAL, "n_shared must be >= 0");
+  if (d->K + d->n_shared > MOER_MAX_SLOTS)
+    return fail(MOER_EINVAL, "K + n_shared must be <= %d", MOER_MAX_SLOTS);
+  if ((long long)d->T * (d->K + d->n_shared) >= (1LL << 31))
+    return fail(MOER_EINVAL, "T * (K + n_shared) must be < 2^31");
+  if (d->n_groups < 1 || d->N % d->n_groups != 0)
+    return fail(MOER_EINVAL, "n_groups must divide N (N=%d, n_groups=%d)", d->N, d->n_groups);
+  if (d->topk_groups < 1 || d->topk_groups > d->n_groups)
+    return fail(MOER_EINVAL, "topk_groups must be in [1, n_groups]");
+  const int gsz = d->N / d->n_groups;
+  if (d->n_groups > 1 && gsz < 2)
+    return fail(MOER_EINVAL, "groups need at least 2 experts (top-2 group score)");
+  if ((long long)d->topk_groups * gsz < d->K)
+    return fail(MOER_EINVAL, "topk_groups * N/n_groups must be >= K");
+  if (d->score_fn != MOER_SOFTMAX && d->score_fn != MOER_SIGMOID)
+    return fail(MOER_EINVAL, "unknown score_fn %d", d->score_fn);
+  if (d->input != MOER_IN_HIDDEN && d->input != MOER_IN_SCORES && d->input != MOER_IN_INDICES)
+    return fail(MOER_EINVAL, "unknown input mode %d", d->input);
+  if (d->input == MOER_IN_HIDDEN) {
+    if (d->dtype != MOER_BF16 && d->dtype != MOER_F32)
+      return fail(MOER_EINVAL, "unknown dtype %d", d->dtype);
+    if (d->d < 1) return fail(MOER_EINVAL, "d must be >= 1 (got %d)", d->d);
+    if (d->dtype == MOER_BF16 && d->d % 8 != 0)
+      return fail(MOER_EINVAL, "bf16 inputs need d %% 8 == 0 (got %d)", d->d);
+    if ((long long)d->T * d->d >= (1LL << 40) || (long long)d->N * d->d >= (1LL << 40))
+      return fail(MOER_EINVAL, "hidden size too large");
+  }
+  if (d->n_groups > 1) {
+    const int E = moer::experts_per_lane(d->N);
+    if (gsz % E != 0 || !is_pow2(gsz / E))
+      return fail(MOER_EUNSUPPORTED,
+                  "group size %d: these kernels need N/n_groups to be a power of two "
+                  "and a multiple of %d for N=%d",
+                  gsz, E, d->N);
+  }
+  return MOER_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moer_abi_version(void) { return MOER_ABI_VERSION; }
+
+const char* moer_last_error(void) { return g_err; }
+
+const char* moer_status_str(moer_status s) {
+  switch (s) {
+    case MOER_OK: return "MOER_OK";
+    case MOER_EINVAL: return "MOER_EINVAL";
+    case MOER_EUNSUPPORTED: return "MOER_EUNSUPPORTED";
+    case MOER_EWORKSPACE: return "MOER_EWORKSPACE";
+    case MOER_EHIP: return "MOER_EHIP";
+  }
+  return "MOER_UNKNOWN";
+}
+
+size_t moer_route_workspace_bytes(const moer_route_desc* desc) {
+  if (validate_desc(desc) != MOER_OK) return 0;
+  // Upper bound over the optional outputs: h in workspace and the entropy
+  // partials are always budgeted.
+  return make_plan(*desc, desc->input == MOER_IN_HIDDEN, desc->input != MOER_IN_INDICES).total;
+}
+
+moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  moer_status st = validate_desc(desc);
+  if (st != MOER_OK) return st;
+  if (io == nullptr) return fail(MOER_EINVAL, "io is NULL");
+  const moer_route_desc& d = *desc;
+  const bool hidden = d.input == MOER_IN_HIDDEN;
+  const bool scores = d.input == MOER_IN_SCORES;
+  const bool indices = d.input == MOER_IN_INDICES;
+  // Arrays whose size is proportional to T may be NULL for an empty batch.
+  const bool some = d.T > 0;
+  if (hidden && some && (io->x == nullptr || io->w_gate == nullptr))
+    return fail(MOER_EINVAL, "HIDDEN input needs x and w_gate");
+  if (scores && some && io->scores == nullptr)
+    return fail(MOER_EINVAL, "SCORES input needs scores");
+  if (indices && some && io->idx_in == nullptr)
+    return fail(MOER_EINVAL, "INDICES input needs idx_in");
+  if (!indices && some && (io->topk_idx == nullptr || io->topk_w == nullptr))
+    return fail(MOER_EINVAL, "topk_idx and topk_w are required");
+  if (io->counts == nullptr || io->offsets == nullptr || (some && io->perm == nullptr))
+    return fail(MOER_EINVAL, "counts, offsets and perm are required");
+  if ((io->ev_gemm_begin == nullptr) != (io->ev_gemm_end == nullptr))
+    return fail(MOER_EINVAL, "ev_gemm_begin and ev_gemm_end go together");
+
+  const bool want_agg = !indices && io->agg_entropy != nullptr;
+  const bool h_in_ws = hidden && io->h_out == nullptr;
+  const Plan p = make_plan(d, h_in_ws, want_agg);
+  if (workspace == nullptr && p.total > 0) return fail(MOER_EWORKSPACE, "workspace is NULL");
+  if (workspace_bytes < p.total)
+    return fail(MOER_EWORKSPACE, "workspace too small: need %zu bytes, got %zu", p.total,
+                workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int L = d.n_layers;
+  hipError_t he = hipSuccess;
+#define MOER_CHECK(expr)                                                        \
+  do {                                                                          \
+    he = (expr);                                                                \
+    if (he != hipSuccess)                                                       \
+      return fail(MOER_EHIP, "%s: %s", #expr, hipGetErrorString(he));           \
+  } while (0)
+
+  // a1: gate affinities
+  const float* h = nullptr;
+  if (hidden && d.T > 0) {
+    float* hbuf = h_in_ws ? reinterpret_cast<float*>(ws + p.off_h) : io->h_out;
+    if (io->ev_gemm_begin) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_begin), s));
+    if (d.dtype == MOER_BF16)
+      MOER_CHECK(moer::launch_gate_gemm_bf16(io->x, io->w_gate, io->logit_offset, hbuf, L, d.T,
+                                             d.d, d.N, s));
+    else
+      MOER_CHECK(moer::launch_gate_gemm_f32(static_cast<const float*>(io->x),
+                                            static_cast<const float*>(io->w_gate),
+                                            io->logit_offset, hbuf, L, d.T, d.d, d.N, s));
+    if (io->ev_gemm_end) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_end), s));
+    h = hbuf;
+  }
+
+  // a2-a5: scores, selection, weights, entropy
+  float* colpart = want_agg ? reinterpret_cast<float*>(ws + p.off_colpart) : nullptr;
+  if (!indices && d.T > 0) {
+    moer::ScoreArgs a{};
+    a.in = hidden ? h : io->scores;
+    a.bias = io->bias;
+    a.idx = io->topk_idx;
+    a.w = io->topk_w;
+    a.tok_entropy = io->tok_entropy;
+    a.colpart = colpart;
+    a.T = d.T;
+    a.N = d.N;
+    a.K = d.K;
+    a.G = d.n_groups;
+    a.Gk = d.topk_groups;
+    a.n_shared = d.n_shared;
+    a.score_fn = d.score_fn;
+    a.apply_score = hidden ? 1 : 0;
+    MOER_CHECK(moer::launch_score_topk(a, L, s));
+  }
+
+  // a6-a8 (+ batch-mean entropy): layout
+  moer::LayoutArgs la{};
+  la.idx = indices ? io->idx_in : io->topk_idx;
+  la.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+  la.colpart = colpart;
+  la.colpart2 = want_agg ? reinterpret_cast<float*>(ws + p.off_colpart2) : nullptr;
+  la.agg_entropy = want_agg ? io->agg_entropy : nullptr;
+  la.counts = io->counts;
+  la.offsets = io->offsets;
+  la.perm = io->perm;
+  la.inv_perm = io->inv_perm;
+  la.T = d.T;
+  la.Kt = p.Kt;
+  la.Nb = p.Nb;
+  la.N = d.N;
+  la.nlb = p.nlb;
+  la.nsb = p.nsb;
+  la.fill_invalid = indices ? 1 : 0;
+  MOER_CHECK(moer::launch_layout(la, L, s));
+#undef MOER_CHECK
+  return ok();
+}
+
+moer_status moer_load_stats(const int32_t* counts, int32_t n_layers, int32_t N, int32_t stride,
+                            moer_load_stats_t* out_dev, void* stream) {
+  if (counts == nullptr || out_dev == nullptr)
+    return fail(MOER_EINVAL, "counts and out_dev are required");
+  if (n_layers < 1 || N < 1 || stride < N)
+    return fail(MOER_EINVAL, "need n_layers >= 1, N >= 1, stride >= N");
+  hipError_t he = moer::launch_load_stats(counts, n_layers, N, stride, out_dev,
+                                          static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(MOER_EHIP, "load_stats launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+moer_status moer_bias_update(float* bias, const int32_t* counts, int32_t n_layers, int32_t N,
+                             int32_t stride, float u, void* stream) {
+  if (bias == nullptr || counts == nullptr)
+    return fail(MOER_EINVAL, "bias and counts are required");
+  if (n_layers < 1 || N < 1 || stride < N)
+    return fail(MOER_EINVAL, "need n_layers >= 1, N >= 1, stride >= N");
+  if (!(u == u) || u < 0.f || u == __builtin_inff())
+    return fail(MOER_EINVAL, "u must be finite and >= 0");
+  hipError_t he = moer::launch_bias_update(bias, counts, n_layers, N, stride, u,
+                                           static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(MOER_EHIP, "bias_update launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+// Scoring, bias-aware group-limited top-k, combine weights and per-token
+// routing entropy: one wavefront per token, E consecutive experts per lane
+// (E = 4 for N <= 256, 2 for N <= 128, 1 for N <= 64), all N scores held in
+// registers.
+//
+// Steps, per token, in the order the pages give them:
+//  1. scores: sigmoid s = 1/(1+exp(-h)) ("DeepSeek V4 MoE load balancing",
+//     token routing: sigmoid gating) or softmax p = exp(h)/sum exp(h)
+//     ("MoE Routing Entropy vs Expert Saturation", Mathematics); in SCORES
+//     mode the scores are given.
+//  2. key = s + b in fp32 (auxiliary-loss-free balancing: the bias enters the
+//     routing decision only); -0 is made +0.
+//  3. G > 1 ("DeepSeek-V3 Group-Limited Expert Routing", s.1 and s.3): the N
+//     keys are G contiguous groups; group score = fp32 sum of the group's two
+//     largest keys; the Gk best groups (score desc, group id asc) stay
+//     eligible, the others are masked out.
+//  4. K rounds of a wave-wide argmax over the eligible keys, ordered by
+//     (key desc, expert id asc); the winner of round r fills slot r.
+//  5. Shared experts (same page, s.4: counted as routed slots) fill slots
+//     K..Kt-1 with ids N.. and weight 1.
+//  6. weights = chosen unbiased scores / their sum (the listing's top-k
+//     renormalisation; the weighted combine of the routing section).
+//  7. entropy of q = s / sum_e s in bits (Mathematics section), per token;
+//     each workgroup also writes the column sums of q over its tokens for
+//     the batch-mean entropy.
+#include <math.h>
+
+#include "moer_internal.hpp"
+
+namespace moer {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+template <int E, bool GROUPED>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(ScoreArgs a) {
+  __shared__ float colsum[kWavesPerBlock][kMaxExperts];
+
+  const int layer = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int N = a.N, K = a.K, T = a.T;
+  const int Kt = K + a.n_shared;
+  const float NEG_INF = -__builtin_inff();
+
+  float bias_r[E];
+  float col[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = lane * E + j;
+    bias_r[j] = (a.bias != nullptr && e < N) ? a.bias[(size_t)layer * N + e] : 0.f;
+    col[j] = 0.f;
+  }
+
+  // Group geometry (GROUPED only): lanes per group and this lane's group.
+  const int gsz = GROUPED ? N / a.G : N;
+  const int lpg = GROUPED ? gsz / E : kWave;
+  const int my_group = GROUPED ? lane / lpg : 0;
+
+  const int tbase = blockIdx.x * kScoreTokens;
+  for (int tt = wave; tt < kScoreTokens; tt += kWavesPerBlock) {
+    const int t = tbase + tt;
+    if (t >= T) break;
+    const float* row = a.in + ((size_t)layer * T + t) * N;
+
+    float v[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = lane * E + j;
+      v[j] = e < N ? row[e] : 0.f;
+    }
+
+    // 1. scores
+    float s[E];
+    if (!a.apply_score) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) s[j] = (lane * E + j < N) ? v[j] : 0.f;
+    } else if (a.score_fn == 1) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) s[j] = (lane * E + j < N) ? 1.f / (1.f + expf(-v[j])) : 0.f;
+    } else {
+      float m = NEG_INF;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (lane * E + j < N) m = fmaxf(m, v[j]);
+      m = wave_max(m);
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        s[j] = (lane * E + j < N) ? expf(v[j] - m) : 0.f;
+        z += s[j];
+      }
+      z = wave_sum(z);
+#pragma unroll
+      for (int j = 0; j < E; ++j) s[j] = s[j] / z;
+    }
+
+    // 2. biased keys
+    float key[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      key[j] = (lane * E + j < N) ? (s[j] + bias_r[j]) + 0.f : NEG_INF;
+    }
+
+    // 3. group-limited eligibility
+    if (GROUPED) {
+      float m1 = key[0], m2 = NEG_INF;
+#pragma unroll
+      for (int j = 1; j < E; ++j) {
+        m2 = fmaxf(m2, fminf(m1, key[j]));
+        m1 = fmaxf(m1, key[j]);
+      }
+      for (int o = 1; o < lpg; o <<= 1) {
+        const float b1 = __shfl_xor(m1, o, kWave);
+        const float b2 = __shfl_xor(m2, o, kWave);
+        const float n2 = fmaxf(fminf(m1, b1), fmaxf(m2, b2));
+        m1 = fmaxf(m1, b1);
+        m2 = n2;
+      }
+      const float gs = m1 + m2;
+      int rank = 0;
+      for (int g = 0; g < a.G; ++g) {
+        const float og = readlane_f(gs, g * lpg);
+        rank += (og > gs || (og == gs && g < my_group)) ? 1 : 0;
+      }
+      if (rank >= a.Gk) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) key[j] = NEG_INF;
+      }
+    }
+
+    // 4. top-K rounds
+    int sel_e[kMaxSlots];
+    float sel_s[kMaxSlots];
+#pragma unroll
+    for (int r = 0; r < kMaxSlots; ++r) {
+      sel_e[r] = 0;
+      sel_s[r] = 0.f;
+      if (r >= K) continue;
+      float bv = key[0];
+      int bj = 0;
+      float bs = s[0];
+#pragma unroll
+      for (int j = 1; j < E; ++j) {
+        if (key[j] > bv) { bv = key[j]; bj = j; bs = s[j]; }
+      }
+      const float M = wave_max(bv);
+      const unsigned long long hit = __ballot(bv == M);
+      const int L = hit ? __builtin_ctzll(hit) : 0;
+      const int jw = __builtin_amdgcn_readlane(bj, L);
+      sel_e[r] = L * E + jw;
+      sel_s[r] = readlane_f(bs, L);
+      if (lane == L) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+          if (j == jw) key[j] = NEG_INF;
+      }
+    }
+
+    // 6. renormalised weights (all lanes hold the same slot values)
+    float z = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxSlots; ++r)
+      if (r < K) z += sel_s[r];
+    if (lane < Kt) {
+      int my_e = N + (lane - K);
+      float my_w = 1.f;
+#pragma unroll
+      for (int r = 0; r < kMaxSlots; ++r) {
+        if (r < K && lane == r) {
+          my_e = sel_e[r];
+          my_w = z > 0.f ? sel_s[r] / z : 1.f / (float)K;
+        }
+      }
+      const size_t o = ((size_t)layer * T + t) * Kt + lane;
+      a.idx[o] = my_e;
+      a.w[o] = my_w;
+    }
+
+    // 7. entropy of q = s / sum s, and column sums of q
+    if (a.tok_entropy != nullptr || a.colpart != nullptr) {
+      float ssum = 0.f, slog = 0.f;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        ssum += s[j];
+        slog += s[j] > 0.f ? s[j] * log2f(s[j]) : 0.f;
+      }
+      ssum = wave_sum(ssum);
+      slog = wave_sum(slog);
+      if (a.tok_entropy != nullptr && lane == 0)
+        a.tok_entropy[(size_t)layer * T + t] = ssum > 0.f ? log2f(ssum) - slog / ssum : 0.f;
+      if (ssum > 0.f) {
+        const float inv = 1.f / ssum;
+#pragma unroll
+        for (int j = 0; j < E; ++j) col[j] += s[j] * inv;
+      }
+    }
+  }
+
+  if (a.colpart != nullptr) {
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = lane * E + j;
+      if (e < kMaxExperts) colsum[wave][e] = col[j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) acc += colsum[w][e];
+      a.colpart[((size_t)layer * gridDim.x + blockIdx.x) * N + e] = acc;
+    }
+  }
+}
+
+template <int E>
+hipError_t launch_e(const ScoreArgs& a, int L, hipStream_t s) {
+  dim3 grid((a.T + kScoreTokens - 1) / kScoreTokens, L);
+  if (a.G > 1)
+    hipLaunchKernelGGL((score_topk_kernel<E, true>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((score_topk_kernel<E, false>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_topk(const ScoreArgs& a, int L, hipStream_t s) {
+  switch (experts_per_lane(a.N)) {
+    case 4: return launch_e<4>(a, L, s);
+    case 2: return launch_e<2>(a, L, s);
+    default: return launch_e<1>(a, L, s);
+  }
+}
+
+}  // namespace moer
