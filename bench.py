@@ -1,0 +1,214 @@
+"""Router hot-path benchmark on one MI355X.
+
+One step = one pass of the whole hot path over one batch of the
+DeepSeek-V3-style router (16384 tokens, d=7168, 256 experts in 8 groups of
+32, keep 4 groups, top-8, sigmoid, selection bias):
+  moer_route (gate GEMM, scores, group-limited top-k, weights, per-token and
+  batch-mean entropy, counts/offsets/perm/inv_perm) -> moer_load_stats ->
+  moer_bias_update.
+Inputs are resident in HBM before timing; x rotates over three distinct
+batches (705 MB in all, larger than the 256 MB last-level cache) so each
+step streams its batch from HBM.
+
+Prints ONE JSON line with the throughput (routed tokens/s), the roofline of
+the dominant kernel (the gate GEMM, HIP events around its launch on the
+route's stream) and the CPU oracle timed on the host cores.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+GEMM_SRC = os.path.join(ROOT, "top_expert_routing_gate_amd", "csrc", "gate_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_gemm_dsv3_traffic.json")
+METRIC = "routed tokens/s, 16k tok × 256 experts top-8; % of MFMA/HBM roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="dsv3_group")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run one plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t pairs for timing one kernel inside the stream order."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a, b))
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float()
+        a, b = self.pairs[i]
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
+def gemm_source_hash():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate-GEMM launch from the committed counter summary, if
+    it was taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gate_gemm_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp):
+    """The oracle, as it stands, on one full batch of the workload."""
+    import numpy as np
+
+    import oracle
+
+    x = inp["x"][0].float().numpy()
+    W = inp["W"][0].float().numpy()
+    b = inp["bias"][0].numpy()
+    t0 = time.perf_counter()
+    out = oracle.route(x=x, W=W, bias=b, K=wl.K, score_fn=wl.score_fn, n_groups=wl.n_groups,
+                       topk_groups=wl.topk_groups, n_shared=wl.n_shared)
+    oracle.load_stats(out["counts"][:wl.N])
+    oracle.bias_update(b, out["counts"][:wl.N], 1e-3)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": wl.T / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"one full batch ({wl.T} tokens, d={wl.d}, N={wl.N}): fp64 affinities, "
+                      f"scores, selection, entropy, layout, load stats, bias update; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the router is measured "
+              "at one GPU's share; multi-GPU sharding is a design note, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import top_expert_routing_gate_amd as moer
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating inputs for {wl.name}", file=sys.stderr, flush=True)
+    W, b0, off, gen = workloads.make_router(wl)
+    xs_cpu = [workloads.make_hidden(wl, gen=gen)]
+    xs_cpu += [workloads.make_hidden(wl, seed=wl.seed + 1 + i) for i in range(2)]
+    xs = [x.to(dev) for x in xs_cpu]
+    Wd, bias = W.to(dev), b0.clone().to(dev)
+    offd = None if off is None else off.to(dev)
+    L, T, N, Kt, Nb = wl.n_layers, wl.T, wl.N, wl.Kt, wl.Nb
+    desc = moer.make_desc(n_layers=L, T=T, d=wl.d, N=N, K=wl.K, n_groups=wl.n_groups,
+                          topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                          score_fn=wl.score_fn, dtype=wl.dtype, input=moer.MOER_IN_HIDDEN)
+    i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+    outs = dict(topk_idx=torch.empty(L, T, Kt, **i32), topk_w=torch.empty(L, T, Kt, **f32),
+                tok_entropy=torch.empty(L, T, **f32), agg_entropy=torch.empty(L, **f32),
+                counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
+                perm=torch.empty(L, T * Kt, **i32), inv_perm=torch.empty(L, T * Kt, **i32))
+    stats = torch.empty(L, 64, dtype=torch.uint8, device=dev)
+    ws = torch.empty(moer.moer_route_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    ev = HipEvents(args.steps)
+
+    def step(i, events=None):
+        moer.moer_route(desc, workspace=ws, x=xs[i % len(xs)], w_gate=Wd, bias=bias,
+                        logit_offset=offd, ev_gemm_begin=events[0] if events else None,
+                        ev_gemm_end=events[1] if events else None, **outs)
+        moer.moer_load_stats(outs["counts"], L, N, Nb, stats)
+        moer.moer_bias_update(bias, outs["counts"], L, N, Nb, 1e-3)
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        del a, bcopy
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, ev.pairs[i])
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+    gemm_ms = sum(ev.elapsed_ms(i) for i in range(args.steps)) / args.steps
+    ev.close()
+    st = moer.decode_load_stats(stats.cpu())[0]
+    print(f"[bench] {ms_step * 1e3:.1f} us/step (wall {t_wall / args.steps * 1e6:.1f} us), "
+          f"gate GEMM {gemm_ms * 1e3:.1f} us; last imbalance {st['imbalance']:.3f}",
+          file=sys.stderr, flush=True)
+
+    alg_bytes = T * wl.d * 2 + N * wl.d * 2  # x + W_g per launch (bf16)
+    achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    line = {
+        "metric": METRIC,
+        "value": T * L / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "hidden": wl.d, "experts": N,
+                   "groups": wl.n_groups, "groups_kept": wl.topk_groups, "top_k": wl.K,
+                   "score": "sigmoid" if wl.score_fn == 1 else "softmax",
+                   "step": "route+load_stats+bias_update", "x_batches_rotated": len(xs)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one batch", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, {"x": xs_cpu[0], "W": W, "bias": b0})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

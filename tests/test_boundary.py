@@ -122,9 +122,10 @@ def test_missing_buffers_and_workspace():
 
 
 def test_workspace_sizes():
-    # dsv3 shape: h (16 MiB) + entropy partials + block histograms
+    # dsv3 shape: partial affinities (one or more depth ranges of 16 MiB each)
+    # + entropy partials + block histograms
     n = moer.moer_route_workspace_bytes(_desc())
-    assert 16384 * 256 * 4 < n < 20 * 2**20
+    assert 16384 * 256 * 4 < n < 5 * 16384 * 256 * 4
     n_scores = moer.moer_route_workspace_bytes(_desc(input=moer.MOER_IN_SCORES))
     assert n_scores < 2 * 2**20
     n_idx = moer.moer_route_workspace_bytes(_desc(input=moer.MOER_IN_INDICES))

@@ -5,17 +5,15 @@
 // DeepEP section). Within an expert, assignments keep (token, slot) order,
 // so the result is unique and deterministic.
 //
-// Two launches per call, both one workgroup per block of kLayoutTokens
-// tokens (all layers in one grid):
-//  layout_count:   LDS histogram of the block's ids -> cnt[l][blk][Nb];
-//                  also folds the score workgroups' column sums of q into
-//                  one row per block (for the batch-mean entropy).
-//  layout_scatter: every block reads all block histograms of its layer and
-//                  derives its base position per expert (prefix over experts
-//                  of the totals, plus the prefix over earlier blocks);
-//                  in-block stable ranks come from per-64-slot LDS bitmaps
-//                  (popcount of lower bits). One extra workgroup per layer
-//                  computes the entropy of the batch-mean distribution.
+// Histograms per 64-token block, cnt[l][e][b] (uint16, expert-major), come
+// from the selection kernel or, for supplied ids, from layout_count below.
+// layout_scatter then runs one workgroup per 128 tokens (two histogram
+// blocks): each workgroup reads its layer's histograms row by row for its
+// experts (contiguous 16-byte loads), derives expert totals, their exclusive
+// scan (the offsets) and its own prefix over earlier blocks, and places its
+// assignments; in-block stable ranks come from per-64-slot LDS membership
+// bitmaps (popcount of the lower bits). One extra workgroup per layer sums
+// the per-block column sums of q into the entropy of the batch mean.
 #include <math.h>
 
 #include "moer_internal.hpp"
@@ -24,16 +22,19 @@ namespace moer {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxSlotsPerBlock = kLayoutTokens * kMaxSlots;  // 2048
-constexpr int kMaxChunks = kMaxSlotsPerBlock / 64;            // 32
+constexpr int kBlocksPerLayoutBlock = kLayoutTokens / kRowTokens;  // 2
+constexpr int kMaxSlotsPerBlock = kLayoutTokens * kMaxSlots;       // 2048
+constexpr int kMaxChunks = kMaxSlotsPerBlock / 64;                 // 32
+static_assert(kLayoutTokens % kRowTokens == 0, "layout block = whole histogram blocks");
 
+// Histogram of supplied ids, one workgroup per 64-token block.
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
   __shared__ int hist[kMaxBuckets];
   const int layer = blockIdx.y;
   const int blk = blockIdx.x;
-  const int t0 = blk * kLayoutTokens;
-  const int nt = min(kLayoutTokens, a.T - t0);
-  const int nslot = nt * a.Kt;
+  const int t0 = blk * kRowTokens;
+  const int nt = min(kRowTokens, a.T - t0);
+  const int nslot = max(nt, 0) * a.Kt;
   const size_t base = (size_t)layer * a.T * a.Kt + (size_t)t0 * a.Kt;
 
   for (int e = threadIdx.x; e < a.Nb; e += kThreads) hist[e] = 0;
@@ -44,19 +45,8 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
     if (a.fill_invalid) a.perm[base + i] = -1;
   }
   __syncthreads();
-  int32_t* out = a.cnt + ((size_t)layer * a.nlb + blk) * a.Nb;
-  for (int e = threadIdx.x; e < a.Nb; e += kThreads) out[e] = hist[e];
-
-  if (a.colpart2 != nullptr) {
-    // rows of the score workgroups covering this block's tokens, summed in order
-    const int r0 = t0 / kScoreTokens;
-    const int r1 = min(a.nsb, (t0 + nt + kScoreTokens - 1) / kScoreTokens);
-    for (int e = threadIdx.x; e < a.N; e += kThreads) {
-      float acc = 0.f;
-      for (int r = r0; r < r1; ++r) acc += a.colpart[((size_t)layer * a.nsb + r) * a.N + e];
-      a.colpart2[((size_t)layer * a.nlb + blk) * a.N + e] = acc;
-    }
-  }
+  uint16_t* out = a.cnt + (size_t)layer * a.Nb * a.nsb + blk;
+  for (int e = threadIdx.x; e < a.Nb; e += kThreads) out[(size_t)e * a.nsb] = (uint16_t)hist[e];
 }
 
 // Exclusive scan of v[0..n) in LDS (n <= 2 * kThreads), deterministic.
@@ -80,19 +70,48 @@ __device__ void block_exclusive_scan(int* v, int* tmp, int n) {
   __syncthreads();
 }
 
+// Entropy (bits) of the batch mean of q: thread (quad of experts, row group)
+// sums its rows with 16-byte loads; row groups are then added in order.
 __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
+  constexpr int kQuads = kMaxExperts / 4;        // 64 expert quads
+  constexpr int kGroups = kThreads / kQuads;     // 4 row groups
+  __shared__ float4 part[kGroups][kQuads];
   __shared__ float red[kThreads];
-  // mean_e = (1/T) sum_t q[t][e]; H = entropy of mean / sum(mean)
-  float me[kMaxExperts / kThreads];
+  const int qd = threadIdx.x % kQuads;
+  const int rg = threadIdx.x / kQuads;
+  const float* cp = a.colpart + (size_t)layer * a.nsb * a.N;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int e = qd * 4;
+  if (e < a.N) {
+    if ((a.N & 3) == 0) {
+#pragma unroll 8
+      for (int r = rg; r < a.nsb; r += kGroups) {
+        const float4 q = *reinterpret_cast<const float4*>(cp + (size_t)r * a.N + e);
+        acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+      }
+    } else {
+      for (int r = rg; r < a.nsb; r += kGroups) {
+        const float* rowp = cp + (size_t)r * a.N;
+        acc.x += rowp[e];
+        if (e + 1 < a.N) acc.y += rowp[e + 1];
+        if (e + 2 < a.N) acc.z += rowp[e + 2];
+        if (e + 3 < a.N) acc.w += rowp[e + 3];
+      }
+    }
+  }
+  part[rg][qd] = acc;
+  __syncthreads();
+  float me[4] = {0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxExperts / kThreads; ++k) {
-    const int e = threadIdx.x + k * kThreads;
-    float acc = 0.f;
-    if (e < a.N)
-      for (int b = 0; b < a.nlb; ++b) acc += a.colpart2[((size_t)layer * a.nlb + b) * a.N + e];
-    me[k] = a.T > 0 ? acc / (float)a.T : 0.f;
-    z += me[k];
+  if (rg == 0) {
+    float4 tot = part[0][qd];
+    for (int g = 1; g < kGroups; ++g) {
+      tot.x += part[g][qd].x; tot.y += part[g][qd].y;
+      tot.z += part[g][qd].z; tot.w += part[g][qd].w;
+    }
+    const float invT = a.T > 0 ? 1.f / (float)a.T : 0.f;
+    me[0] = tot.x * invT; me[1] = tot.y * invT; me[2] = tot.z * invT; me[3] = tot.w * invT;
+    z = me[0] + me[1] + me[2] + me[3];
   }
   red[threadIdx.x] = z;
   __syncthreads();
@@ -103,8 +122,7 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
   const float Z = red[0];
   __syncthreads();
   float hpart = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxExperts / kThreads; ++k) {
+  for (int k = 0; k < 4; ++k) {
     const float q = Z > 0.f ? me[k] / Z : 0.f;
     hpart -= q > 0.f ? q * log2f(q) : 0.f;
   }
@@ -132,21 +150,38 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) 
   }
   const int Nb = a.Nb;
   const int t0 = blk * kLayoutTokens;
-  const int nt = min(kLayoutTokens, a.T - t0);
+  const int nt = max(0, min(kLayoutTokens, a.T - t0));
   const int nslot = nt * a.Kt;
   const int nchunk = (nslot + 63) / 64;
   const size_t lbase = (size_t)layer * a.T * a.Kt;
   const int flat0 = t0 * a.Kt;
+  const int b_first = blk * kBlocksPerLayoutBlock;  // first histogram block of this workgroup
 
-  // totals and prefix over earlier blocks, per expert
-  const int32_t* cnt = a.cnt + (size_t)layer * a.nlb * Nb;
+  // per expert: total over all histogram blocks, and over the blocks before ours
+  const uint16_t* cnt = a.cnt + (size_t)layer * Nb * a.nsb;
+  const bool vec = (a.nsb & 7) == 0;
   for (int e = threadIdx.x; e < 2 * kThreads; e += kThreads) {
     int tot = 0, p = 0;
     if (e < Nb) {
-      for (int b = 0; b < a.nlb; ++b) {
-        const int c = cnt[(size_t)b * Nb + e];
-        tot += c;
-        p += b < blk ? c : 0;
+      const uint16_t* row = cnt + (size_t)e * a.nsb;
+      if (vec) {
+#pragma unroll 8
+        for (int b = 0; b < a.nsb; b += 8) {
+          const uint4 w = *reinterpret_cast<const uint4*>(row + b);
+          const unsigned ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int lo = ww[k] & 0xFFFF, hi = ww[k] >> 16;
+            tot += lo + hi;
+            p += (b + 2 * k < b_first ? lo : 0) + (b + 2 * k + 1 < b_first ? hi : 0);
+          }
+        }
+      } else {
+        for (int b = 0; b < a.nsb; ++b) {
+          const int c = row[b];
+          tot += c;
+          p += b < b_first ? c : 0;
+        }
       }
       pre[e] = p;
     }
@@ -198,10 +233,12 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) 
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s) {
+  if (a.need_count) {
+    hipLaunchKernelGGL(layout_count_kernel, dim3(a.nsb, L), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // a.nlb >= 1 (an empty batch still writes zero counts and offsets)
-  hipLaunchKernelGGL(layout_count_kernel, dim3(a.nlb, L), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int extra = a.agg_entropy != nullptr ? 1 : 0;
   hipLaunchKernelGGL(layout_scatter_kernel, dim3(a.nlb + extra, L), dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -31,28 +31,37 @@ bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Workspace regions (byte offsets) for a validated descriptor.
 struct Plan {
-  int Kt, Nb, nsb, nlb;
-  size_t off_h, off_colpart, off_colpart2, off_cnt, total;
+  int Kt, Nb, nsb, nlb, ksplit;
+  size_t off_h, off_colpart, off_cnt, total;
 };
 
-Plan make_plan(const moer_route_desc& d, bool want_h_ws, bool want_agg) {
+Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   Plan p{};
   const size_t L = (size_t)d.n_layers;
   p.Kt = d.K + d.n_shared;
   p.Nb = d.N + d.n_shared;
-  p.nsb = (d.T + moer::kScoreTokens - 1) / moer::kScoreTokens;
+  p.nsb = (d.T + moer::kRowTokens - 1) / moer::kRowTokens;
   p.nlb = d.T > 0 ? (d.T + moer::kLayoutTokens - 1) / moer::kLayoutTokens : 1;
+  p.ksplit = hidden ? moer::gate_gemm_ksplit(d.dtype == MOER_BF16, d.n_layers, d.T, d.d, d.N) : 1;
   size_t o = 0;
-  p.off_h = o;
-  if (want_h_ws) o += align_up(L * d.T * d.N * sizeof(float));
-  p.off_colpart = o;
-  if (want_agg) o += align_up(L * p.nsb * d.N * sizeof(float) + 4);
-  p.off_colpart2 = o;
-  if (want_agg) o += align_up(L * p.nlb * d.N * sizeof(float));
-  p.off_cnt = o;
-  o += align_up(L * p.nlb * p.Nb * sizeof(int32_t));
+  p.off_h = o;  // partial affinities of the gate GEMM
+  if (hidden) o += align_up((size_t)p.ksplit * L * d.T * d.N * sizeof(float));
+  p.off_colpart = o;  // column sums of q per 64-token block
+  if (want_agg) o += align_up(L * p.nsb * d.N * sizeof(float) + 16);
+  p.off_cnt = o;  // expert histograms per 64-token block (uint16)
+  o += align_up(L * p.Nb * p.nsb * sizeof(uint16_t) + 16);
   p.total = o;
   return p;
+}
+
+// Which selection kernel takes this shape: 1 = one 16-lane row per token,
+// 2 = one wavefront per token, 0 = neither.
+int selection_path(const moer_route_desc& d) {
+  if (moer::route_rows_supports(d.N, d.n_groups)) return 1;
+  if (d.n_groups == 1) return 2;
+  const int gsz = d.N / d.n_groups;
+  const int E = moer::experts_per_lane(d.N);
+  return (gsz % E == 0 && is_pow2(gsz / E)) ? 2 : 0;
 }
 
 moer_status validate_desc(const moer_route_desc* d) {
@@ -89,14 +98,11 @@ moer_status validate_desc(const moer_route_desc* d) {
     if ((long long)d->T * d->d >= (1LL << 40) || (long long)d->N * d->d >= (1LL << 40))
       return fail(MOER_EINVAL, "hidden size too large");
   }
-  if (d->n_groups > 1) {
-    const int E = moer::experts_per_lane(d->N);
-    if (gsz % E != 0 || !is_pow2(gsz / E))
-      return fail(MOER_EUNSUPPORTED,
-                  "group size %d: these kernels need N/n_groups to be a power of two "
-                  "and a multiple of %d for N=%d",
-                  gsz, E, d->N);
-  }
+  if (d->input != MOER_IN_INDICES && selection_path(*d) == 0)
+    return fail(MOER_EUNSUPPORTED,
+                "group size %d with N=%d: these kernels need N/n_groups to be a power of two "
+                "multiple of the experts each lane holds",
+                gsz, d->N);
   return MOER_OK;
 }
 
@@ -151,8 +157,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     return fail(MOER_EINVAL, "ev_gemm_begin and ev_gemm_end go together");
 
   const bool want_agg = !indices && io->agg_entropy != nullptr;
-  const bool h_in_ws = hidden && io->h_out == nullptr;
-  const Plan p = make_plan(d, h_in_ws, want_agg);
+  const Plan p = make_plan(d, hidden, want_agg);
   if (workspace == nullptr && p.total > 0) return fail(MOER_EWORKSPACE, "workspace is NULL");
   if (workspace_bytes < p.total)
     return fail(MOER_EWORKSPACE, "workspace too small: need %zu bytes, got %zu", p.total,
@@ -172,24 +177,29 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   // a1: gate affinities
   const float* h = nullptr;
   if (hidden && d.T > 0) {
-    float* hbuf = h_in_ws ? reinterpret_cast<float*>(ws + p.off_h) : io->h_out;
+    float* hbuf = reinterpret_cast<float*>(ws + p.off_h);
     if (io->ev_gemm_begin) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_begin), s));
     if (d.dtype == MOER_BF16)
-      MOER_CHECK(moer::launch_gate_gemm_bf16(io->x, io->w_gate, io->logit_offset, hbuf, L, d.T,
-                                             d.d, d.N, s));
+      MOER_CHECK(moer::launch_gate_gemm_bf16(io->x, io->w_gate, hbuf, L, d.T, d.d, d.N, p.ksplit,
+                                             s));
     else
       MOER_CHECK(moer::launch_gate_gemm_f32(static_cast<const float*>(io->x),
-                                            static_cast<const float*>(io->w_gate),
-                                            io->logit_offset, hbuf, L, d.T, d.d, d.N, s));
+                                            static_cast<const float*>(io->w_gate), hbuf, L, d.T,
+                                            d.d, d.N, s));
     if (io->ev_gemm_end) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_end), s));
     h = hbuf;
   }
 
-  // a2-a5: scores, selection, weights, entropy
+  // a2-a6: scores, selection, weights, entropy, per-block expert histograms
   float* colpart = want_agg ? reinterpret_cast<float*>(ws + p.off_colpart) : nullptr;
+  uint16_t* cnt = reinterpret_cast<uint16_t*>(ws + p.off_cnt);
+  const int path = indices ? 0 : selection_path(d);
   if (!indices && d.T > 0) {
     moer::ScoreArgs a{};
     a.in = hidden ? h : io->scores;
+    a.offset = hidden ? io->logit_offset : nullptr;
+    a.h_out = hidden ? io->h_out : nullptr;
+    a.nsplit = p.ksplit;
     a.bias = io->bias;
     a.idx = io->topk_idx;
     a.w = io->topk_w;
@@ -203,15 +213,20 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     a.n_shared = d.n_shared;
     a.score_fn = d.score_fn;
     a.apply_score = hidden ? 1 : 0;
-    MOER_CHECK(moer::launch_score_topk(a, L, s));
+    if (path == 1) {
+      a.cnt = cnt;
+      MOER_CHECK(moer::launch_route_rows(a, L, s));
+    } else {
+      a.cnt = nullptr;
+      MOER_CHECK(moer::launch_score_topk(a, L, s));
+    }
   }
 
   // a6-a8 (+ batch-mean entropy): layout
   moer::LayoutArgs la{};
   la.idx = indices ? io->idx_in : io->topk_idx;
-  la.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+  la.cnt = cnt;
   la.colpart = colpart;
-  la.colpart2 = want_agg ? reinterpret_cast<float*>(ws + p.off_colpart2) : nullptr;
   la.agg_entropy = want_agg ? io->agg_entropy : nullptr;
   la.counts = io->counts;
   la.offsets = io->offsets;
@@ -224,6 +239,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   la.nlb = p.nlb;
   la.nsb = p.nsb;
   la.fill_invalid = indices ? 1 : 0;
+  la.need_count = (path != 1 && d.T > 0) ? 1 : 0;
   MOER_CHECK(moer::launch_layout(la, L, s));
 #undef MOER_CHECK
   return ok();

@@ -11,38 +11,48 @@ constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kMaxExperts = 256;    // N
 constexpr int kMaxSlots = 16;       // Kt
 constexpr int kMaxBuckets = kMaxExperts + kMaxSlots;
-constexpr int kScoreTokens = 16;    // tokens per score_topk workgroup
-constexpr int kLayoutTokens = 128;  // tokens per layout workgroup
+constexpr int kRowTokens = 64;      // tokens per selection workgroup (= histogram block)
+constexpr int kLayoutTokens = 128;  // tokens per scatter workgroup (2 histogram blocks)
 
 // Everything a score/select launch needs (passed by value).
 struct ScoreArgs {
-  const float* in;        // [L][T][N] affinities h (apply_score) or scores s
+  const float* in;        // [nsplit][L][T][N] partial affinities (apply_score) or scores s
+  const float* offset;    // [N] logit offset added to h, or nullptr
+  float* h_out;           // [L][T][N] summed affinities, or nullptr
   const float* bias;      // [L][N] or nullptr
   int32_t* idx;           // [L][T][Kt]
   float* w;               // [L][T][Kt]
   float* tok_entropy;     // [L][T] or nullptr
-  float* colpart;         // [L][nsb][N] per-workgroup sums of q, or nullptr
-  int T, N, K, G, Gk, n_shared, score_fn, apply_score;
+  float* colpart;         // [L][nsb][N] sums of q per 64-token block, or nullptr
+  uint16_t* cnt;          // [L][Nb][nsb] expert counts per 64-token block, or nullptr
+  int T, N, K, G, Gk, n_shared, score_fn, apply_score, nsplit;
 };
 
 struct LayoutArgs {
   const int32_t* idx;     // [L][T][Kt]
-  int32_t* cnt;           // workspace [L][nlb][Nb]
+  uint16_t* cnt;          // [L][Nb][nsb] expert counts per 64-token block
   const float* colpart;   // [L][nsb][N] or nullptr
-  float* colpart2;        // [L][nlb][N] or nullptr
   float* agg_entropy;     // [L] or nullptr
   int32_t* counts;        // [L][Nb]
   int32_t* offsets;       // [L][Nb+1]
   int32_t* perm;          // [L][T*Kt]
   int32_t* inv_perm;      // [L][T*Kt] or nullptr
-  int T, Kt, Nb, N, nlb, nsb, fill_invalid;
+  int T, Kt, Nb, N, nlb, nsb, fill_invalid, need_count;
 };
 
-hipError_t launch_gate_gemm_bf16(const void* x, const void* w, const float* offset, float* h,
-                                 int L, int T, int d, int N, hipStream_t s);
-hipError_t launch_gate_gemm_f32(const float* x, const float* w, const float* offset, float* h,
-                                int L, int T, int d, int N, hipStream_t s);
+// Depth ranges the bf16 gate GEMM splits d into (its partial sums are
+// part[0..ksplit) [L][T][N]); 1 for fp32 inputs.
+int gate_gemm_ksplit(int dtype_bf16, int L, int T, int d, int N);
+hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int L, int T, int d,
+                                 int N, int ksplit, hipStream_t s);
+hipError_t launch_gate_gemm_f32(const float* x, const float* w, float* h, int L, int T, int d,
+                                int N, hipStream_t s);
 hipError_t launch_score_topk(const ScoreArgs& a, int L, hipStream_t s);
+// Row-per-token selection (writes the block histograms itself).
+int route_rows_epl(int N);
+bool route_rows_supports(int N, int G);
+size_t route_rows_lds_bytes(int N);
+hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s);
 hipError_t launch_load_stats(const int32_t* counts, int L, int N, int stride, void* out,
                              hipStream_t s);

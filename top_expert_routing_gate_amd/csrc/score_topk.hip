@@ -73,17 +73,26 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
   const int lpg = GROUPED ? gsz / E : kWave;
   const int my_group = GROUPED ? lane / lpg : 0;
 
-  const int tbase = blockIdx.x * kScoreTokens;
-  for (int tt = wave; tt < kScoreTokens; tt += kWavesPerBlock) {
+  const int tbase = blockIdx.x * kRowTokens;
+  for (int tt = wave; tt < kRowTokens; tt += kWavesPerBlock) {
     const int t = tbase + tt;
     if (t >= T) break;
-    const float* row = a.in + ((size_t)layer * T + t) * N;
+    const size_t row_off = ((size_t)layer * T + t) * N;
+    const size_t split_stride = (size_t)gridDim.y * T * N;
 
+    // affinities: partial sums over depth ranges added in order, then the offset
     float v[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const int e = lane * E + j;
-      v[j] = e < N ? row[e] : 0.f;
+      float acc = 0.f;
+      if (e < N) {
+        acc = a.in[row_off + e];
+        for (int sp = 1; sp < a.nsplit; ++sp) acc += a.in[sp * split_stride + row_off + e];
+        if (a.offset != nullptr) acc += a.offset[e];
+        if (a.h_out != nullptr) a.h_out[row_off + e] = acc;
+      }
+      v[j] = acc;
     }
 
     // 1. scores
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
 
 template <int E>
 hipError_t launch_e(const ScoreArgs& a, int L, hipStream_t s) {
-  dim3 grid((a.T + kScoreTokens - 1) / kScoreTokens, L);
+  dim3 grid((a.T + kRowTokens - 1) / kRowTokens, L);
   if (a.G > 1)
     hipLaunchKernelGGL((score_topk_kernel<E, true>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
   else
