@@ -27,10 +27,10 @@
 // shuffle goes through the LDS crossbar.
 //
 // Exact top-K without K argmax rounds:
-//  - lo = the K-th largest of the row's lane maxima over eligible experts;
-//    these are keys of distinct eligible experts, so lo is at most the K-th
-//    largest eligible key: every chosen expert has key >= lo.
-//  - the eligible keys >= lo (typically 10-20 of 256) are compacted into
+//  - lo = the K-th largest of the row's per-lane top-2 eligible keys; these
+//    are keys of distinct eligible experts, so lo is at most the K-th largest
+//    eligible key: every chosen expert has key >= lo.
+//  - the eligible keys >= lo (typically K to K+4 of 256) are compacted into
 //    LDS as packed 64-bit words (orderable key bits, then inverted id), at
 //    positions from a row prefix scan of per-lane counts;
 //  - a candidate's slot is the number of candidates whose packed word is
@@ -174,10 +174,13 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   const int e0 = rl * EPL;
   const float NEG_INF = -__builtin_inff();
 
-  // LDS: candidates [rows][N] | slot ids [rows][16] | histogram [Nb]
-  unsigned long long* cand = smem + (size_t)row * a.N;
-  int* slot_id = reinterpret_cast<int*>(smem + (size_t)kRowTokens * a.N) + row * kMaxSlots;
-  int* hist = reinterpret_cast<int*>(smem + (size_t)kRowTokens * a.N) + kRowTokens * kMaxSlots;
+  // LDS: candidates [rows][N+1] (the pad word staggers rows across banks) |
+  // slot ids [rows][16] | histogram [Nb]. The candidate area is reused at the
+  // end for the per-wave column sums of q.
+  const int cstride = a.N + 1;
+  unsigned long long* cand = smem + (size_t)row * cstride;
+  int* slot_id = reinterpret_cast<int*>(smem + (size_t)kRowTokens * cstride) + row * kMaxSlots;
+  int* hist = reinterpret_cast<int*>(smem + (size_t)kRowTokens * cstride) + kRowTokens * kMaxSlots;
   for (int i = threadIdx.x; i < Nb; i += kThreads) hist[i] = 0;
 
   // 1. affinities / scores
@@ -280,18 +283,29 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
     eligible = g < a.G && rank < a.Gk;
   }
 
-  // lo: K-th largest eligible lane maximum
-  float lmax = NEG_INF;
-  if (eligible)
+  // lo: K-th largest of the eligible lanes' two largest keys (keys of up to 32
+  // distinct eligible experts, so lo is at most the K-th largest eligible key)
+  float l1 = NEG_INF, l2 = NEG_INF;
+  if (eligible) {
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) lmax = fmaxf(lmax, key[j]);
-  int cge = 1;
-#define MOER_CGE(n) cge += dpp_f<0x120 + (n)>(lmax) >= lmax ? 1 : 0;
+    for (int j = 0; j < EPL; ++j) {
+      l2 = fmaxf(l2, fminf(l1, key[j]));
+      l1 = fmaxf(l1, key[j]);
+    }
+  }
+  int c1 = 1 + (l2 >= l1 ? 1 : 0), c2 = 2;  // values >= l1 / >= l2, own pair included
+#define MOER_CGE(n)                                          \
+  {                                                          \
+    const float o1 = dpp_f<0x120 + (n)>(l1);                 \
+    const float o2 = dpp_f<0x120 + (n)>(l2);                 \
+    c1 += (o1 >= l1 ? 1 : 0) + (o2 >= l1 ? 1 : 0);           \
+    c2 += (o1 >= l2 ? 1 : 0) + (o2 >= l2 ? 1 : 0);           \
+  }
   MOER_CGE(1) MOER_CGE(2) MOER_CGE(3) MOER_CGE(4) MOER_CGE(5) MOER_CGE(6) MOER_CGE(7)
   MOER_CGE(8) MOER_CGE(9) MOER_CGE(10) MOER_CGE(11) MOER_CGE(12) MOER_CGE(13) MOER_CGE(14)
   MOER_CGE(15)
 #undef MOER_CGE
-  const float lo = row_max(cge >= K ? lmax : NEG_INF);
+  const float lo = row_max(fmaxf(c1 >= K ? l1 : NEG_INF, c2 >= K ? l2 : NEG_INF));
 
   // candidates: eligible keys >= lo, compacted by a row prefix scan
   unsigned bits = 0;
@@ -306,16 +320,17 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
 #pragma unroll
   for (int j = 0; j < EPL; ++j)
     if (bits & (1u << j)) cand[pos++] = pack_key(key[j], e0 + j);
-  __syncthreads();  // candidates of every row written; histogram cleared
+  // A row's candidates, slots and weights are private to its wavefront and a
+  // wavefront's LDS operations complete in order: no workgroup barrier here.
 
   // 4. slot of each candidate = number of candidates that beat it
   for (int c = rl; c < count; c += kRowLanes) {
     const unsigned long long my = cand[c];
     int r = 0;
+#pragma unroll 4
     for (int i = 0; i < count; ++i) r += cand[i] > my ? 1 : 0;
     if (r < K) slot_id[r] = 0xFFFF - (int)(my & 0xFFFF);
   }
-  __syncthreads();
 
   // 5. weights over the chosen slots (re-derived scores, same instructions)
   int my_e = 0;
@@ -331,6 +346,19 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
     }
   }
   const float zsel = row_sum(rl < K ? my_s : 0.f);
+
+  // column sums of q over the wavefront's 4 tokens (rows): rows 0+1 and 2+3,
+  // then the two pairs; both lanes of a pair add the same two operands, so
+  // every lane ends with the bitwise-same sum
+  float colq[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const float q = s[j] * inv_s;
+    const float h = q + __shfl_xor(q, 16, kWave);
+    colq[j] = h + __shfl_xor(h, 32, kWave);
+  }
+
+  __syncthreads();  // histogram cleared, every wavefront done with its candidates
   if (live && rl < Kt) {
     const size_t o = ((size_t)layer * T + t) * Kt + rl;
     if (rl < K) {
@@ -343,38 +371,26 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
       atomicAdd(&hist[N + (rl - K)], 1);
     }
   }
+  float* colw = reinterpret_cast<float*>(smem);  // [wave][j*16 + lane] in the candidate area
+  const int wave = threadIdx.x >> 6;
+  if (a.colpart != nullptr) {
+    // every lane stores (the 4 rows of a wavefront store identical sums), so
+    // the lane exchanges above are never moved under a lane-dependent branch
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) colw[wave * (kRowLanes * EPL) + j * kRowLanes + rl] = colq[j];
+  }
   __syncthreads();
   if (a.cnt != nullptr) {
     uint16_t* out = a.cnt + (size_t)layer * Nb * gridDim.x + blockIdx.x;
     for (int e = threadIdx.x; e < Nb; e += kThreads) out[(size_t)e * gridDim.x] = (uint16_t)hist[e];
   }
-
-  // column sums of q over this workgroup's tokens, in a fixed order
   if (a.colpart != nullptr) {
-    // q of every token in LDS, then 4 threads per expert add 16 rows each and
-    // the 4 partial sums are added in order
-    constexpr int kParts = kThreads / kMaxExperts;  // 4
-    float* col = reinterpret_cast<float*>(smem);    // reuse the candidate area
-    float* part = col + (size_t)kRowTokens * N;
-    __syncthreads();
+    constexpr int kWavesPerBlock = kThreads / kWave;
+    for (int e = threadIdx.x; e < N; e += kThreads) {
+      const int idx = (e % EPL) * kRowLanes + e / EPL;
+      float acc = colw[idx];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (full || e0 + j < N) col[(size_t)row * N + e0 + j] = s[j] * inv_s;
-    __syncthreads();
-    const int e = threadIdx.x % kMaxExperts;
-    const int pidx = threadIdx.x / kMaxExperts;
-    if (e < N) {
-      float acc = 0.f;
-#pragma unroll
-      for (int r = pidx * (kRowTokens / kParts); r < (pidx + 1) * (kRowTokens / kParts); ++r)
-        acc += col[(size_t)r * N + e];
-      part[pidx * N + e] = acc;
-    }
-    __syncthreads();
-    if (pidx == 0 && e < N) {
-      float acc = part[e];
-#pragma unroll
-      for (int p = 1; p < kParts; ++p) acc += part[p * N + e];
+      for (int w = 1; w < kWavesPerBlock; ++w) acc += colw[w * (kRowLanes * EPL) + idx];
       a.colpart[((size_t)layer * gridDim.x + blockIdx.x) * N + e] = acc;
     }
   }
@@ -417,9 +433,11 @@ bool route_rows_supports(int N, int G) {
 }
 
 size_t route_rows_lds_bytes(int N) {
-  // candidates (64-bit per expert per row), reused at the end for the q rows
-  // plus 4 partial rows; slot ids; histogram
-  const size_t cand = std::max((size_t)kRowTokens * N * 8, (size_t)(kRowTokens + 4) * N * 4);
+  // candidates (64-bit per expert per row, one pad word per row), reused at
+  // the end for the per-wave column sums; slot ids; histogram
+  const int epl = route_rows_epl(N);
+  const size_t cand = std::max((size_t)kRowTokens * (N + 1) * 8,
+                               (size_t)(kThreads / kWave) * kRowLanes * epl * 4);
   return cand + (size_t)kRowTokens * kMaxSlots * 4 + kMaxBuckets * 4;
 }
 
