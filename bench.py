@@ -4,8 +4,8 @@ One step = one pass of the whole hot path over one batch of the
 DeepSeek-V3-style router (16384 tokens, d=7168, 256 experts in 8 groups of
 32, keep 4 groups, top-8, sigmoid, selection bias):
   moer_route (gate GEMM, scores, group-limited top-k, weights, per-token and
-  batch-mean entropy, counts/offsets/perm/inv_perm) -> moer_load_stats ->
-  moer_bias_update.
+  batch-mean entropy, counts/offsets/perm/inv_perm, and, fused into the same
+  call, the load statistics and the in-place sign-step bias update).
 Inputs are resident in HBM before timing; x rotates over three distinct
 batches (705 MB in all, larger than the 256 MB last-level cache) so each
 step streams its batch from HBM.
@@ -40,7 +40,65 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="write a per-kernel table from a rocprofv3 --kernel-trace --stats dir")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="calibrated HBM bytes per gate-GEMM launch from two --pmc runs")
+    p.add_argument("--command", default="", help="profiling command recorded in a summary")
+    p.add_argument("--out", help="output file of a summary")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def summarize_trace(d, out, command):
+    import csv
+    import glob
+
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    rows = list(csv.DictReader(open(stats[0])))
+    lines = ["# Kernel trace: router step, DeepSeek-V3-style 16k-token batch", "",
+             "Command (from /tmp, TMPDIR=/tmp):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("|", "/")
+        name = name.split("(")[0] if "moer::" in name else name
+        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter_rows(d, counter):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    out = []
+    for fn in files:
+        for r in csv.DictReader(open(fn)):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_traffic(fetch_dir, write_dir, out, command):
+    res = {"gate_gemm_sha256_16": gemm_source_hash(), "command": command}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        gemm = [v for n, v in rows if "gate_gemm" in n]
+        copy = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        res[f"{key}_kib_per_launch"] = sum(gemm) / len(gemm)
+        res[f"{key}_kib_copy_1gib"] = max(copy)
+        # counter units: KiB; scale by what the counter reads for a known 1 GiB copy
+        res[f"{key}_scale"] = COPY_BYTES / (max(copy) * 1024.0)
+    res["bytes_per_launch"] = (res["fetch_kib_per_launch"] * 1024.0 * res["fetch_scale"] +
+                               res["write_kib_per_launch"] * 1024.0 * res["write_scale"])
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
 
 
 class HipEvents:
@@ -113,6 +171,12 @@ def cpu_baseline(wl, inp):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.out, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the router is measured "
               "at one GPU's share; multi-GPU sharding is a design note, not built.",
@@ -149,9 +213,8 @@ def main():
     def step(i, events=None):
         moer.moer_route(desc, workspace=ws, x=xs[i % len(xs)], w_gate=Wd, bias=bias,
                         logit_offset=offd, ev_gemm_begin=events[0] if events else None,
-                        ev_gemm_end=events[1] if events else None, **outs)
-        moer.moer_load_stats(outs["counts"], L, N, Nb, stats)
-        moer.moer_bias_update(bias, outs["counts"], L, N, Nb, 1e-3)
+                        ev_gemm_end=events[1] if events else None, load_stats=stats,
+                        bias_update=bias, bias_update_u=1e-3, **outs)
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -200,7 +263,7 @@ def main():
         "config": {"workload": wl.name, "tokens": T, "hidden": wl.d, "experts": N,
                    "groups": wl.n_groups, "groups_kept": wl.topk_groups, "top_k": wl.K,
                    "score": "sigmoid" if wl.score_fn == 1 else "softmax",
-                   "step": "route+load_stats+bias_update", "x_batches_rotated": len(xs)},
+                   "step": "route+load_stats+bias_update (fused)", "x_batches_rotated": len(xs)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
     }

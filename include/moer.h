@@ -98,6 +98,18 @@ typedef struct {
   int32_t input;       /* moer_input */
 } moer_route_desc;
 
+/* Per-layer record written by moer_load_stats (device memory, 64 bytes). */
+typedef struct {
+  int64_t total;      /* sum of counts over the N routed experts */
+  int64_t max_load;   /* largest count */
+  int64_t argmax;     /* expert with the largest count (lowest id on ties) */
+  int64_t capacity;   /* max_load * N: fixed per-expert capacity that fits */
+  double mean;        /* total / N */
+  double imbalance;   /* max_load / mean, 0 when mean == 0 */
+  double h_load_bits; /* entropy (bits) of counts/total, 0 when total == 0 */
+  double cv;          /* population std of counts / mean, 0 when mean == 0 */
+} moer_load_stats_t;
+
 /* Buffers of one call (device pointers; Kt = K + n_shared, Nb = N + n_shared).
  * "req" = required in the modes that produce it; "opt" = may be NULL. */
 typedef struct {
@@ -124,19 +136,16 @@ typedef struct {
                                 -1 for ids that were not placed */
   void* ev_gemm_begin;       /* opt hipEvent_t recorded just before the gate */
   void* ev_gemm_end;         /* GEMM launch and just after it (profiling)   */
+  moer_load_stats_t* load_stats; /* opt [L]: what moer_load_stats gives for this
+                                    call's counts (fused, no extra launch) */
+  float* bias_update;        /* opt [L][N]: moer_bias_update applied in place
+                                with this call's counts and step bias_update_u,
+                                after the selection has read `bias` (so it may
+                                be the same buffer): the auxiliary-loss-free
+                                balancing step of one training iteration */
+  float bias_update_u;       /* step u >= 0 for bias_update */
 } moer_route_io;
 
-/* Per-layer record written by moer_load_stats (device memory, 64 bytes). */
-typedef struct {
-  int64_t total;      /* sum of counts over the N routed experts */
-  int64_t max_load;   /* largest count */
-  int64_t argmax;     /* expert with the largest count (lowest id on ties) */
-  int64_t capacity;   /* max_load * N: fixed per-expert capacity that fits */
-  double mean;        /* total / N */
-  double imbalance;   /* max_load / mean, 0 when mean == 0 */
-  double h_load_bits; /* entropy (bits) of counts/total, 0 when total == 0 */
-  double cv;          /* population std of counts / mean, 0 when mean == 0 */
-} moer_load_stats_t;
 
 /* Bytes of workspace moer_route needs for `desc` (0 on an invalid desc). */
 size_t moer_route_workspace_bytes(const moer_route_desc* desc);

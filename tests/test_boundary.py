@@ -119,6 +119,11 @@ def test_missing_buffers_and_workspace():
     io.ev_gemm_begin = fake
     st, msg = _route_raw(d, io, fake, need)
     assert st == moer.MOER_EINVAL and "ev_gemm" in msg
+    io.ev_gemm_begin = None
+    for u in (float("nan"), -1e-3, float("inf")):
+        io.bias_update, io.bias_update_u = fake, u
+        st, msg = _route_raw(d, io, fake, need)
+        assert st == moer.MOER_EINVAL and "bias_update_u" in msg, u
 
 
 def test_workspace_sizes():

@@ -276,6 +276,37 @@ def test_bias_update_bit_exact():
     assert (got[1] == b[1].numpy()).all()
 
 
+def test_fused_stats_and_bias_update():
+    """moer_route's fused load statistics and in-place bias update (bias and
+    bias_update the same buffer: selection must read the old values) against
+    the oracle, over three consecutive training steps of a 2-layer router."""
+    wl = workloads.scaled(WL["collapse_balance"], T=700)
+    L = 2
+    _, b0, off, _ = workloads.make_router(wl)
+    b_gpu = b0.repeat(L, 1).contiguous().to(DEV)
+    b_gpu[1] *= -1
+    b_ref = [b_gpu[l].cpu().numpy().copy() for l in range(L)]
+    for step in range(3):
+        logits = workloads.make_logits(wl.T, wl.N, 300 + step, n_layers=L) + off
+        s32 = np.stack([_oracle_scores(logits[l], wl.score_fn) for l in range(L)])
+        out = moer.route(scores=torch.from_numpy(s32).to(DEV), K=wl.K, n_groups=8, topk_groups=4,
+                         bias=b_gpu, want_load_stats=True, bias_update=b_gpu,
+                         bias_update_u=2e-3)
+        torch.cuda.synchronize()
+        got = moer.decode_load_stats(out["load_stats"].cpu())
+        for l in range(L):
+            ref = oracle.route(s32=s32[l], bias=b_ref[l], K=wl.K, score_fn=wl.score_fn,
+                               n_groups=8, topk_groups=4)
+            assert (_np(out["topk_idx"][l]) == ref["idx"]).all(), (step, l)
+            st = oracle.load_stats(ref["counts"][:wl.N])
+            for k in ("total", "max_load", "argmax", "capacity"):
+                assert got[l][k] == st[k], (step, l, k)
+            for k in ("mean", "imbalance", "h_load_bits", "cv"):
+                assert got[l][k] == pytest.approx(st[k], rel=1e-9, abs=1e-12), (step, l, k)
+            b_ref[l] = oracle.bias_update(b_ref[l], ref["counts"][:wl.N], 2e-3)
+            assert (_np(b_gpu[l]) == b_ref[l]).all(), (step, l)
+
+
 def test_collapse_balancing_lockstep():
     """Celebrity experts (+3.0 logit offset) and 100 rounds of route -> count
     -> sign update, GPU and oracle in lockstep on identical fp32 scores: the

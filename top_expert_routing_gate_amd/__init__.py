@@ -47,12 +47,16 @@ def _layers(t, rank):
 
 def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups=1, n_shared=0,
           bias=None, logit_offset=None, scores=None, idx_in=None, N=None, want_h=False,
-          want_inv_perm=True, want_entropy=True, workspace=None, stream=None):
+          want_inv_perm=True, want_entropy=True, want_load_stats=False, bias_update=None,
+          bias_update_u=1e-3, workspace=None, stream=None):
     """Route a batch; returns a dict of device tensors, each with a leading
     layer dimension L.
 
     Input (one of): x [L,T,d] with w_gate [L,N,d] (bf16 or fp32), scores
     [L,T,N] fp32, or idx_in [L,T,K+n_shared] int32 (N must then be given).
+    want_load_stats adds the raw load-statistics records ("load_stats", uint8
+    [L,64]); bias_update [L,N] fp32 (may be `bias` itself) gets the sign-step
+    update with step bias_update_u from this call's counts, in place.
     """
     x, w_gate = _layers(x, 3), _layers(w_gate, 3)
     scores, idx_in, bias = _layers(scores, 3), _layers(idx_in, 3), _layers(bias, 2)
@@ -81,6 +85,8 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
         if want_entropy:
             out["tok_entropy"] = torch.empty(L, T, **f32)
             out["agg_entropy"] = torch.empty(L, **f32)
+    if want_load_stats:
+        out["load_stats"] = torch.empty(L, 64, dtype=torch.uint8, device=dev)
     if want_h and mode == MOER_IN_HIDDEN:
         out["h"] = torch.empty(L, T, N, **f32)
     if workspace is None:
@@ -91,7 +97,8 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
                topk_w=out.get("topk_w"), tok_entropy=out.get("tok_entropy"),
                agg_entropy=out.get("agg_entropy"), topk_idx=out.get("topk_idx"),
                counts=out["counts"], offsets=out["offsets"], perm=out["perm"],
-               inv_perm=out.get("inv_perm"))
+               inv_perm=out.get("inv_perm"), load_stats=out.get("load_stats"),
+               bias_update=_layers(bias_update, 2), bias_update_u=bias_update_u)
     return out
 
 

@@ -33,7 +33,8 @@ class MoerRouteIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("x", "w_gate", "scores", "idx_in", "bias", "logit_offset", "h_out", "topk_w",
                  "tok_entropy", "agg_entropy", "topk_idx", "counts", "offsets", "perm",
-                 "inv_perm", "ev_gemm_begin", "ev_gemm_end")]
+                 "inv_perm", "ev_gemm_begin", "ev_gemm_end", "load_stats", "bias_update")] + \
+        [("bias_update_u", ctypes.c_float)]
 
 
 class MoerLoadStats(ctypes.Structure):
@@ -123,7 +124,8 @@ def moer_route_workspace_bytes(desc):
 def moer_route(desc, *, workspace, stream=None, x=None, w_gate=None, scores=None, idx_in=None,
                bias=None, logit_offset=None, h_out=None, topk_w=None, tok_entropy=None,
                agg_entropy=None, topk_idx=None, counts=None, offsets=None, perm=None,
-               inv_perm=None, ev_gemm_begin=None, ev_gemm_end=None):
+               inv_perm=None, ev_gemm_begin=None, ev_gemm_end=None, load_stats=None,
+               bias_update=None, bias_update_u=0.0):
     """Calls moer_route on device tensors (shapes and dtypes as in moer.h)."""
     for name, t, dt in (("x", x, None), ("w_gate", w_gate, None), ("scores", scores, torch.float32),
                         ("idx_in", idx_in, torch.int32), ("bias", bias, torch.float32),
@@ -133,7 +135,8 @@ def moer_route(desc, *, workspace, stream=None, x=None, w_gate=None, scores=None
                         ("agg_entropy", agg_entropy, torch.float32),
                         ("topk_idx", topk_idx, torch.int32), ("counts", counts, torch.int32),
                         ("offsets", offsets, torch.int32), ("perm", perm, torch.int32),
-                        ("inv_perm", inv_perm, torch.int32)):
+                        ("inv_perm", inv_perm, torch.int32),
+                        ("bias_update", bias_update, torch.float32)):
         if t is not None and dt is not None and t.dtype != dt:
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
     if x is not None:
@@ -143,7 +146,10 @@ def moer_route(desc, *, workspace, stream=None, x=None, w_gate=None, scores=None
     io = MoerRouteIO(_ptr(x), _ptr(w_gate), _ptr(scores), _ptr(idx_in), _ptr(bias),
                      _ptr(logit_offset), _ptr(h_out), _ptr(topk_w), _ptr(tok_entropy),
                      _ptr(agg_entropy), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
-                     _ptr(inv_perm), ev_gemm_begin, ev_gemm_end)
+                     _ptr(inv_perm), ev_gemm_begin, ev_gemm_end, _ptr(load_stats),
+                     _ptr(bias_update), float(bias_update_u))
+    if load_stats is not None and load_stats.numel() * load_stats.element_size() < 64 * desc.n_layers:
+        raise ValueError("load_stats needs 64 bytes per layer")
     ws = workspace
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.moer_route(ctypes.byref(desc), ctypes.byref(io), _ptr(ws), nbytes,

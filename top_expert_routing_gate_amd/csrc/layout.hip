@@ -13,9 +13,12 @@
 // scan (the offsets) and its own prefix over earlier blocks, and places its
 // assignments; in-block stable ranks come from per-64-slot LDS membership
 // bitmaps (popcount of the lower bits). One extra workgroup per layer sums
-// the per-block column sums of q into the entropy of the batch mean.
+// the per-block column sums of q into the entropy of the batch mean, and
+// another (when asked) derives the load statistics and the bias update from
+// the same histograms, so neither waits for the other.
 #include <math.h>
 
+#include "load_balance.hpp"
 #include "moer_internal.hpp"
 
 namespace moer {
@@ -26,6 +29,7 @@ constexpr int kBlocksPerLayoutBlock = kLayoutTokens / kRowTokens;  // 2
 constexpr int kMaxSlotsPerBlock = kLayoutTokens * kMaxSlots;       // 2048
 constexpr int kMaxChunks = kMaxSlotsPerBlock / 64;                 // 32
 static_assert(kLayoutTokens % kRowTokens == 0, "layout block = whole histogram blocks");
+static_assert(kThreads == kBalanceThreads, "the first layout workgroup runs the balance routines");
 
 // Histogram of supplied ids, one workgroup per 64-token block.
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
@@ -135,29 +139,10 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
   if (threadIdx.x == 0) a.agg_entropy[layer] = a.T > 0 ? red[0] : 0.f;
 }
 
-__global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) {
-  __shared__ int total[2 * kThreads];
-  __shared__ int pre[kMaxBuckets];
-  __shared__ int scan_tmp[kThreads];
-  __shared__ unsigned long long bits[kMaxChunks][kMaxBuckets];
-  __shared__ unsigned short chunk_pre[kMaxChunks][kMaxBuckets];
-
-  const int layer = blockIdx.y;
-  const int blk = blockIdx.x;
-  if (blk == a.nlb) {
-    batch_mean_entropy(a, layer);
-    return;
-  }
+// Per expert e < Nb: total[e] = assignments over all histogram blocks of the
+// layer, pre[e] = those in blocks before b_first; total[e] = 0 for e >= Nb.
+__device__ void expert_totals(const LayoutArgs& a, int layer, int b_first, int* total, int* pre) {
   const int Nb = a.Nb;
-  const int t0 = blk * kLayoutTokens;
-  const int nt = max(0, min(kLayoutTokens, a.T - t0));
-  const int nslot = nt * a.Kt;
-  const int nchunk = (nslot + 63) / 64;
-  const size_t lbase = (size_t)layer * a.T * a.Kt;
-  const int flat0 = t0 * a.Kt;
-  const int b_first = blk * kBlocksPerLayoutBlock;  // first histogram block of this workgroup
-
-  // per expert: total over all histogram blocks, and over the blocks before ours
   const uint16_t* cnt = a.cnt + (size_t)layer * Nb * a.nsb;
   const bool vec = (a.nsb & 7) == 0;
   for (int e = threadIdx.x; e < 2 * kThreads; e += kThreads) {
@@ -187,13 +172,53 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) 
     }
     total[e] = tot;
   }
+}
+
+// Load statistics and the sign-step bias update of this call's routed counts
+// (one workgroup per layer, beside the scatter workgroups).
+__device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* total, int* pre) {
+  __shared__ BalanceScratch bal;
+  expert_totals(a, layer, 0, total, pre);
+  __syncthreads();
+  if (a.stats != nullptr) block_load_stats(total, a.N, a.stats + layer, bal);
+  if (a.bias_inout != nullptr)
+    block_bias_update(a.bias_inout + (size_t)layer * a.N, total, a.N, a.bias_step, bal);
+}
+
+// Workgroups [0, nlb) place 128 tokens each; then, if requested, one
+// workgroup for the batch-mean entropy and one for load balancing.
+__global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) {
+  __shared__ int total[2 * kThreads];
+  __shared__ int pre[kMaxBuckets];
+  __shared__ int scan_tmp[kThreads];
+  __shared__ unsigned long long bits[kMaxChunks][kMaxBuckets];
+  __shared__ unsigned short chunk_pre[kMaxChunks][kMaxBuckets];
+
+  const int layer = blockIdx.y;
+  const int blk = blockIdx.x;
+  if (blk >= a.nlb) {
+    if (blk == a.nlb && a.agg_entropy != nullptr)
+      batch_mean_entropy(a, layer);
+    else
+      balance_from_histograms(a, layer, total, pre);
+    return;
+  }
+  const int Nb = a.Nb;
+  const int t0 = blk * kLayoutTokens;
+  const int nt = max(0, min(kLayoutTokens, a.T - t0));
+  const int nslot = nt * a.Kt;
+  const int nchunk = (nslot + 63) / 64;
+  const size_t lbase = (size_t)layer * a.T * a.Kt;
+  const int flat0 = t0 * a.Kt;
+
+  // per expert: total over all histogram blocks, and over the blocks before ours
+  expert_totals(a, layer, blk * kBlocksPerLayoutBlock, total, pre);
   for (int c = 0; c < nchunk; ++c)
     for (int e = threadIdx.x; e < Nb; e += kThreads) bits[c][e] = 0ull;
   __syncthreads();
   const int last_count = total[Nb - 1];
-  if (blk == 0) {
+  if (blk == 0)
     for (int e = threadIdx.x; e < Nb; e += kThreads) a.counts[(size_t)layer * Nb + e] = total[e];
-  }
   block_exclusive_scan(total, scan_tmp, Nb);  // total[e] := offset of expert e
   if (blk == 0) {
     int32_t* off = a.offsets + (size_t)layer * (Nb + 1);
@@ -239,7 +264,8 @@ hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   // a.nlb >= 1 (an empty batch still writes zero counts and offsets)
-  const int extra = a.agg_entropy != nullptr ? 1 : 0;
+  const int extra = (a.agg_entropy != nullptr ? 1 : 0) +
+                    (a.stats != nullptr || a.bias_inout != nullptr ? 1 : 0);
   hipLaunchKernelGGL(layout_scatter_kernel, dim3(a.nlb + extra, L), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

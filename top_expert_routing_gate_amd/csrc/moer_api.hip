@@ -155,6 +155,10 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     return fail(MOER_EINVAL, "counts, offsets and perm are required");
   if ((io->ev_gemm_begin == nullptr) != (io->ev_gemm_end == nullptr))
     return fail(MOER_EINVAL, "ev_gemm_begin and ev_gemm_end go together");
+  if (io->bias_update != nullptr &&
+      (!(io->bias_update_u == io->bias_update_u) || io->bias_update_u < 0.f ||
+       io->bias_update_u == __builtin_inff()))
+    return fail(MOER_EINVAL, "bias_update_u must be finite and >= 0");
 
   const bool want_agg = !indices && io->agg_entropy != nullptr;
   const Plan p = make_plan(d, hidden, want_agg);
@@ -238,6 +242,9 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   la.N = d.N;
   la.nlb = p.nlb;
   la.nsb = p.nsb;
+  la.stats = io->load_stats;
+  la.bias_inout = io->bias_update;
+  la.bias_step = io->bias_update_u;
   la.fill_invalid = indices ? 1 : 0;
   la.need_count = (path != 1 && d.T > 0) ? 1 : 0;
   MOER_CHECK(moer::launch_layout(la, L, s));

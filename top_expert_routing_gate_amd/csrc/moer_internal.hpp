@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moer.h"
+
 namespace moer {
 
 constexpr int kWave = 64;           // CDNA wavefront width
@@ -37,6 +39,9 @@ struct LayoutArgs {
   int32_t* offsets;       // [L][Nb+1]
   int32_t* perm;          // [L][T*Kt]
   int32_t* inv_perm;      // [L][T*Kt] or nullptr
+  moer_load_stats_t* stats;  // [L] or nullptr
+  float* bias_inout;      // [L][N] updated in place, or nullptr
+  float bias_step;
   int T, Kt, Nb, N, nlb, nsb, fill_invalid, need_count;
 };
 
@@ -54,7 +59,7 @@ bool route_rows_supports(int N, int G);
 size_t route_rows_lds_bytes(int N);
 hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s);
-hipError_t launch_load_stats(const int32_t* counts, int L, int N, int stride, void* out,
+hipError_t launch_load_stats(const int32_t* counts, int L, int N, int stride, moer_load_stats_t* out,
                              hipStream_t s);
 hipError_t launch_bias_update(float* bias, const int32_t* counts, int L, int N, int stride,
                               float u, hipStream_t s);
