@@ -28,6 +28,7 @@ from ._moer import (  # noqa: F401
     MOER_SOFTMAX,
     MoerError,
     MoerRouteDesc,
+    PreparedRoute,
     decode_load_stats,
     make_desc,
     moer_abi_version,

@@ -121,12 +121,11 @@ def moer_route_workspace_bytes(desc):
     return int(_lib.moer_route_workspace_bytes(ctypes.byref(desc)))
 
 
-def moer_route(desc, *, workspace, stream=None, x=None, w_gate=None, scores=None, idx_in=None,
-               bias=None, logit_offset=None, h_out=None, topk_w=None, tok_entropy=None,
-               agg_entropy=None, topk_idx=None, counts=None, offsets=None, perm=None,
-               inv_perm=None, ev_gemm_begin=None, ev_gemm_end=None, load_stats=None,
-               bias_update=None, bias_update_u=0.0):
-    """Calls moer_route on device tensors (shapes and dtypes as in moer.h)."""
+def _route_io(desc, *, x=None, w_gate=None, scores=None, idx_in=None, bias=None,
+              logit_offset=None, h_out=None, topk_w=None, tok_entropy=None, agg_entropy=None,
+              topk_idx=None, counts=None, offsets=None, perm=None, inv_perm=None,
+              ev_gemm_begin=None, ev_gemm_end=None, load_stats=None, bias_update=None,
+              bias_update_u=0.0):
     for name, t, dt in (("x", x, None), ("w_gate", w_gate, None), ("scores", scores, torch.float32),
                         ("idx_in", idx_in, torch.int32), ("bias", bias, torch.float32),
                         ("logit_offset", logit_offset, torch.float32),
@@ -143,17 +142,44 @@ def moer_route(desc, *, workspace, stream=None, x=None, w_gate=None, scores=None
         want = torch.bfloat16 if desc.dtype == MOER_BF16 else torch.float32
         if x.dtype != want or (w_gate is not None and w_gate.dtype != want):
             raise TypeError(f"x and w_gate must be {want}")
-    io = MoerRouteIO(_ptr(x), _ptr(w_gate), _ptr(scores), _ptr(idx_in), _ptr(bias),
-                     _ptr(logit_offset), _ptr(h_out), _ptr(topk_w), _ptr(tok_entropy),
-                     _ptr(agg_entropy), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
-                     _ptr(inv_perm), ev_gemm_begin, ev_gemm_end, _ptr(load_stats),
-                     _ptr(bias_update), float(bias_update_u))
     if load_stats is not None and load_stats.numel() * load_stats.element_size() < 64 * desc.n_layers:
         raise ValueError("load_stats needs 64 bytes per layer")
+    return MoerRouteIO(_ptr(x), _ptr(w_gate), _ptr(scores), _ptr(idx_in), _ptr(bias),
+                       _ptr(logit_offset), _ptr(h_out), _ptr(topk_w), _ptr(tok_entropy),
+                       _ptr(agg_entropy), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
+                       _ptr(inv_perm), ev_gemm_begin, ev_gemm_end, _ptr(load_stats),
+                       _ptr(bias_update), float(bias_update_u))
+
+
+def moer_route(desc, *, workspace, stream=None, **buffers):
+    """Calls moer_route on device tensors (shapes and dtypes as in moer.h)."""
+    io = _route_io(desc, **buffers)
     ws = workspace
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.moer_route(ctypes.byref(desc), ctypes.byref(io), _ptr(ws), nbytes,
                            _stream(stream)))
+
+
+class PreparedRoute:
+    """One moer_route call whose arguments are marshalled once, for loops that
+    route into the same buffers again and again (the tensors must stay alive
+    and in place). Calling it enqueues moer_route with those arguments; only
+    the two profiling events may change per call."""
+
+    def __init__(self, desc, *, workspace, stream=None, **buffers):
+        self.desc = desc
+        self.io = _route_io(desc, **buffers)
+        self._keep = (workspace, buffers)
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._args = (ctypes.byref(self.desc), ctypes.byref(self.io), _ptr(workspace), nbytes,
+                      _stream(stream))
+
+    def __call__(self, ev_gemm_begin=None, ev_gemm_end=None):
+        self.io.ev_gemm_begin = ev_gemm_begin
+        self.io.ev_gemm_end = ev_gemm_end
+        st = _lib.moer_route(*self._args)
+        if st != MOER_OK:
+            _check(st)
 
 
 def moer_load_stats(counts, n_layers, N, stride, out, stream=None):

@@ -27,9 +27,10 @@ constexpr int kKStage = 64;           // reduction depth per LDS stage (bf16)
 constexpr int kChunks = kKStage / 8;  // 16-byte chunks per staged row
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt <= n and lgkmcnt == 0: this
-// wave's DMA stages up to the wanted one have landed and its own LDS reads of
-// earlier stages have completed.
+// wave's DMA stages up to the wanted one have landed and its own LDS reads
+// have completed.
 constexpr int wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+constexpr int kNoVmWait = 63;  // vmcnt field at its maximum: wait for LDS only
 
 // Workgroup barrier that orders LDS traffic at compile time only (asm memory
 // clobbers); the hardware side is the explicit s_waitcnt before it.
@@ -42,30 +43,44 @@ __device__ __forceinline__ void ring_barrier() {
 // ---------------------------------------------------------------------------
 // Pipelined kernel (d a multiple of 64 * ksplit).
 //
-// Workgroup tile: BT tokens x BE experts over one depth range; 4 waves
-// arranged WT x WE, each owning (BT/WT) x (BE/WE) in 16x16 MFMA blocks.
-// Operand tiles stream into an NSTAGE-deep LDS ring with
-// global_load_lds_dwordx4 (no VGPR staging): each wave instruction fills 64
-// consecutive 16-byte LDS slots, and each lane fetches the global chunk that
-// belongs in its slot under the XOR swizzle slot(r, q) = r*8 + (q ^ (r%8)),
-// which makes the 16-byte fragment reads of 8 consecutive rows conflict-free.
-// Rows past T or N are clamped to the last valid row (their results are never
-// stored); d must be a multiple of the stage depth so no chunk is partial.
+// Workgroup tile: BT tokens x BE experts over one depth range. The
+// workgroup's waves have two roles:
+//  - WT x WE consumer waves, each owning (BT/WT) x (BE/WE) in 16x16 MFMA
+//    blocks, read operand fragments from LDS and issue the MFMAs;
+//  - NP producer waves stream the operand tiles into an NSTAGE-deep LDS ring
+//    with global_load_lds_dwordx4 (no VGPR staging).
+// Splitting the roles matters on CDNA: a wave that issues a long run of
+// loads stalls in the issue stage while the memory pipeline back-pressures,
+// and a wave's MFMAs cannot issue past its own stalled loads. With separate
+// waves the matrix cores run while the producers wait.
+//
+// Each producer instruction fills 64 consecutive 16-byte LDS slots, and each
+// lane fetches the global chunk that belongs in its slot under the XOR
+// swizzle slot(r, q) = r*8 + (q ^ (r%8)), which makes the 16-byte fragment
+// reads of 8 consecutive rows conflict-free. Rows past T or N are clamped to
+// the last valid row (their results are never stored); d must be a multiple
+// of the stage depth so no chunk is partial.
+//
+// One workgroup barrier per stage orders the ring: before barrier k the
+// producers wait until their stage-k loads have landed, and the consumers
+// have finished reading stage k-1; after it the consumers read stage k and
+// the producers refill the buffer of stage k-1 with stage k+NSTAGE-1.
 //
 // Workgroups are numbered so that consecutive tiles of one (layer, depth
 // range) land on the same XCD (dispatch is round-robin over the 8 XCDs):
-// every XCD then streams one half of W_g through its own L2.
-template <int BT, int BE, int WT, int WE, int NSTAGE>
-__global__ __launch_bounds__(WT * WE * kWave, 1) void gate_gemm_dma_kernel(
+// every XCD then streams one part of W_g through its own L2.
+template <int BT, int BE, int WT, int WE, int NP, int NSTAGE>
+__global__ __launch_bounds__((WT * WE + NP) * kWave, 1) void gate_gemm_dma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
     int L, int T, int d, int N, int ksplit, int n_tt, int n_te, int n_work, int per_xcd) {
-  constexpr int kThreads = WT * WE * kWave;
+  constexpr int kConsumers = WT * WE;
   constexpr int kRows = BT + BE;
   constexpr int kStageSlots = kRows * kChunks;
-  constexpr int kLoads = kStageSlots / kThreads;  // DMA instructions per thread per stage
+  constexpr int kLoads = kStageSlots / (NP * kWave);  // DMA instructions per producer per stage
   constexpr int MT = BT / WT / 16;
   constexpr int ME = BE / WE / 16;
-  static_assert(kStageSlots % kThreads == 0, "stage must split evenly over the workgroup");
+  static_assert(kStageSlots % (NP * kWave) == 0, "stage must split evenly over the producers");
+  static_assert((NSTAGE - 2) * kLoads <= 63, "outstanding loads must fit the vmcnt field");
   static_assert(BT % (WT * 16) == 0 && BE % (WE * 16) == 0, "tile shape");
 
   __shared__ u32x4 ring[NSTAGE][kStageSlots];
@@ -87,58 +102,58 @@ __global__ __launch_bounds__(WT * WE * kWave, 1) void gate_gemm_dma_kernel(
   x += (size_t)layer * T * d;
   W += (size_t)layer * N * d;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wt = wave / WE;
-  const int we = wave % WE;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
 
-  // Source of every DMA slot this lane fills (fixed across stages).
-  const uint16_t* src[kLoads];
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int slot = (i * (kThreads / kWave) + wave) * kWave + lane;
-    const int r = slot / kChunks;
-    const int q = (slot % kChunks) ^ (r & 7);
-    const uint16_t* row;
-    if (r < BT) {
-      row = x + (size_t)min(t0 + r, T - 1) * d;
-    } else {
-      row = W + (size_t)min(e0 + r - BT, N - 1) * d;
-    }
-    src[i] = row + kbeg + q * 8;
-  }
-
-  auto issue = [&](int stage_k, int buf) {
+  if (wave >= kConsumers) {
+    // ---- producer ----
+    const int pw = wave - kConsumers;
+    const uint16_t* src[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      u32x4* dst = &ring[buf][(i * (kThreads / kWave) + wave) * kWave];
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + stage_k * kKStage),
-                                       LDS_PTR(dst), 16, 0, 0);
+      const int slot = (i * NP + pw) * kWave + lane;
+      const int r = slot / kChunks;
+      const int q = (slot % kChunks) ^ (r & 7);
+      const uint16_t* row = r < BT ? x + (size_t)min(t0 + r, T - 1) * d
+                                   : W + (size_t)min(e0 + r - BT, N - 1) * d;
+      src[i] = row + kbeg + q * 8;
     }
-  };
+    auto issue = [&](int stage_k, int buf) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + stage_k * kKStage),
+                                         LDS_PTR(&ring[buf][(i * NP + pw) * kWave]), 16, 0, 0);
+    };
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < nk) issue(s, s);
+    for (int k = 0; k < nk; ++k) {
+      // stage k has landed once at most the later issued stages are pending
+      if (k + NSTAGE - 2 < nk)
+        __builtin_amdgcn_s_waitcnt(wait_imm((NSTAGE - 2) * kLoads));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_imm(0));
+      ring_barrier();
+      if (k + NSTAGE - 1 < nk) issue(k + NSTAGE - 1, (k + NSTAGE - 1) % NSTAGE);
+    }
+    return;
+  }
 
+  // ---- consumer ----
+  const int wt = wave / WE;
+  const int we = wave % WE;
   floatx4 acc[ME][MT];
 #pragma unroll
   for (int i = 0; i < ME; ++i)
 #pragma unroll
     for (int j = 0; j < MT; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < nk) issue(s, s);
-
   const int frow = lane & 15;
   const int fq = lane >> 4;
   for (int k = 0; k < nk; ++k) {
-    // stage k has landed once at most the later issued stages are pending
-    if (k + NSTAGE - 2 < nk) {
-      __builtin_amdgcn_s_waitcnt(wait_imm((NSTAGE - 2) * kLoads));
-    } else {
-      __builtin_amdgcn_s_waitcnt(wait_imm(0));
-    }
-    ring_barrier();  // all waves' slots of stage k visible; stage k-1 fully read
-    if (k + NSTAGE - 1 < nk) issue(k + NSTAGE - 1, (k + NSTAGE - 1) % NSTAGE);
+    // own fragment reads of stage k-1 complete before its buffer is refilled
+    __builtin_amdgcn_s_waitcnt(wait_imm(kNoVmWait));
+    ring_barrier();
     const u32x4* buf = ring[k % NSTAGE];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -328,15 +343,15 @@ __global__ __launch_bounds__(256) void gate_gemm_f32_kernel(const float* __restr
   h[((size_t)layer * T + t) * N + e] = acc;
 }
 
-template <int BT, int BE, int WT, int WE, int NSTAGE>
+template <int BT, int BE, int WT, int WE, int NP, int NSTAGE>
 hipError_t launch_dma(const void* x, const void* w, float* part, int L, int T, int d, int N,
                       int ksplit, hipStream_t s) {
   const int n_tt = (T + BT - 1) / BT;
   const int n_te = (N + BE - 1) / BE;
   const int n_work = L * ksplit * n_te * n_tt;
   const int per_xcd = (n_work + 7) / 8;
-  hipLaunchKernelGGL((gate_gemm_dma_kernel<BT, BE, WT, WE, NSTAGE>), dim3(8 * per_xcd),
-                     dim3(WT * WE * kWave), 0, s, static_cast<const uint16_t*>(x),
+  hipLaunchKernelGGL((gate_gemm_dma_kernel<BT, BE, WT, WE, NP, NSTAGE>), dim3(8 * per_xcd),
+                     dim3((WT * WE + NP) * kWave), 0, s, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(w), part, L, T, d, N, ksplit, n_tt, n_te,
                      n_work, per_xcd);
   return hipGetLastError();
@@ -370,8 +385,8 @@ int gate_gemm_ksplit(int dtype_bf16, int L, int T, int d, int N) {
 hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int L, int T, int d,
                                  int N, int ksplit, hipStream_t s) {
   if (d % (kKStage * ksplit) == 0) {
-    if (small_n(N)) return launch_dma<64, 32, 4, 1, 3>(x, w, part, L, T, d, N, ksplit, s);
-    return launch_dma<128, 256, 2, 2, 3>(x, w, part, L, T, d, N, ksplit, s);
+    if (small_n(N)) return launch_dma<64, 32, 4, 1, 4, 3>(x, w, part, L, T, d, N, ksplit, s);
+    return launch_dma<128, 256, 2, 2, 4, 3>(x, w, part, L, T, d, N, ksplit, s);
   }
   if (ksplit != 1) return hipErrorInvalidValue;
   if (N <= 16) return launch_tile<16, 64, 1, 4>(x, w, part, L, T, d, N, s);

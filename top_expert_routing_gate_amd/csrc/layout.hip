@@ -180,9 +180,9 @@ __device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* tot
   __shared__ BalanceScratch bal;
   expert_totals(a, layer, 0, total, pre);
   __syncthreads();
-  if (a.stats != nullptr) block_load_stats(total, a.N, a.stats + layer, bal);
-  if (a.bias_inout != nullptr)
-    block_bias_update(a.bias_inout + (size_t)layer * a.N, total, a.N, a.bias_step, bal);
+  block_load_balance(total, a.N, a.stats != nullptr ? a.stats + layer : nullptr,
+                     a.bias_inout != nullptr ? a.bias_inout + (size_t)layer * a.N : nullptr,
+                     a.bias_step, bal);
 }
 
 // Workgroups [0, nlb) place 128 tokens each; then, if requested, one

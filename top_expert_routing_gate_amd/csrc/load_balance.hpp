@@ -1,6 +1,6 @@
 // Workgroup-level load statistics and sign-step bias update (256 threads),
 // used by the standalone moer_load_stats / moer_bias_update kernels and by the
-// layout's first workgroup when moer_route is asked for them.
+// layout launch's balance workgroup when moer_route is asked for them.
 //
 // Load statistics ("A minimal experiment in expert-load imbalance", Run the
 // example): total, mean = total/N, imbalance = max/mean (0 when the mean is
@@ -24,60 +24,69 @@
 namespace moer {
 
 constexpr int kBalanceThreads = 256;
+constexpr int kBalanceWaves = kBalanceThreads / kWave;
 
 struct BalanceScratch {
-  long long red_i[kBalanceThreads];
-  double red_d[kBalanceThreads];
-  long long red_v[kBalanceThreads];
-  int red_e[kBalanceThreads];
+  long long tot[kBalanceWaves];
+  unsigned long long best[kBalanceWaves];
+  double h[kBalanceWaves];
+  double v[kBalanceWaves];
 };
 
+// Xor butterfly over the 64 lanes of a wave: every lane ends with the same
+// bits (each step combines a lane with its partner using a commutative op).
 template <typename V, typename Op>
-__device__ V balance_reduce(V v, V* red, Op op) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = kBalanceThreads / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] = op(red[threadIdx.x], red[threadIdx.x + o]);
-    __syncthreads();
-  }
-  const V r = red[0];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ V wave_allreduce(V v, Op op) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = op(v, __shfl_xor(v, o, kWave));
+  return v;
 }
 
-// Sum of c[0..N); every thread receives it.
-__device__ inline long long block_count_total(const int32_t* c, int N, BalanceScratch& sh) {
+// Load statistics (out != nullptr) and/or the sign-step bias update
+// (bias != nullptr) of the counts c[0..N) (LDS or global memory). Reductions:
+// each thread takes experts tid, tid+256, ... in order, then a butterfly per
+// wave, then the four wave results in wave order: fixed, so deterministic.
+__device__ inline void block_load_balance(const int32_t* c, int N, moer_load_stats_t* out,
+                                          float* bias, float u, BalanceScratch& sh) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  // round 1: total, and the largest count with the lowest expert id on ties
+  // (packed as order-preserving count bits << 32 | ~id, so one unsigned max
+  // decides both)
   long long tot = 0;
-  for (int e = threadIdx.x; e < N; e += kBalanceThreads) tot += c[e];
-  return balance_reduce(tot, sh.red_i, [](long long x, long long y) { return x + y; });
-}
-
-// Load statistics of c[0..N) (c may live in LDS or global memory).
-__device__ inline void block_load_stats(const int32_t* c, int N, moer_load_stats_t* out,
-                                        BalanceScratch& sh) {
-  const long long tot = block_count_total(c, N, sh);
-  long long bv = -1;
-  int be = 0;
-  for (int e = threadIdx.x; e < N; e += kBalanceThreads)
-    if ((long long)c[e] > bv) { bv = c[e]; be = e; }
-  // max with the lowest expert id on ties, fixed pairwise order
-  sh.red_v[threadIdx.x] = bv;
-  sh.red_e[threadIdx.x] = be;
-  __syncthreads();
-  for (int o = kBalanceThreads / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
-      const long long ov = sh.red_v[threadIdx.x + o];
-      const int oe = sh.red_e[threadIdx.x + o];
-      if (ov > sh.red_v[threadIdx.x] || (ov == sh.red_v[threadIdx.x] && oe < sh.red_e[threadIdx.x])) {
-        sh.red_v[threadIdx.x] = ov;
-        sh.red_e[threadIdx.x] = oe;
-      }
-    }
-    __syncthreads();
+  unsigned long long best = 0;
+  for (int e = threadIdx.x; e < N; e += kBalanceThreads) {
+    tot += c[e];
+    const unsigned ord = (unsigned)c[e] ^ 0x80000000u;
+    const unsigned long long key =
+        ((unsigned long long)ord << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)e);
+    best = key > best ? key : best;
   }
-  const long long mx = sh.red_v[0];
-  const int am = sh.red_e[0];
+  tot = wave_allreduce(tot, [](long long x, long long y) { return x + y; });
+  best = wave_allreduce(best, [](unsigned long long x, unsigned long long y) { return x > y ? x : y; });
+  if (lane == 0) {
+    sh.tot[wave] = tot;
+    sh.best[wave] = best;
+  }
   __syncthreads();
+  tot = sh.tot[0];
+  best = sh.best[0];
+#pragma unroll
+  for (int w = 1; w < kBalanceWaves; ++w) {
+    tot += sh.tot[w];
+    best = sh.best[w] > best ? sh.best[w] : best;
+  }
+
+  if (bias != nullptr) {
+    for (int e = threadIdx.x; e < N; e += kBalanceThreads) {
+      const long long diff = tot - (long long)N * c[e];
+      const float step = diff > 0 ? u : (diff < 0 ? -u : 0.f);
+      bias[e] = bias[e] + step;
+    }
+  }
+  if (out == nullptr) return;
+
+  // round 2: entropy of the load distribution and the sum of squared deviations
   const double mean = (double)tot / (double)N;
   double hpart = 0.0, vpart = 0.0;
   for (int e = threadIdx.x; e < N; e += kBalanceThreads) {
@@ -88,9 +97,22 @@ __device__ inline void block_load_stats(const int32_t* c, int N, moer_load_stats
     }
     vpart += (v - mean) * (v - mean);
   }
-  const double H = balance_reduce(hpart, sh.red_d, [](double x, double y) { return x + y; });
-  const double var = balance_reduce(vpart, sh.red_d, [](double x, double y) { return x + y; });
+  hpart = wave_allreduce(hpart, [](double x, double y) { return x + y; });
+  vpart = wave_allreduce(vpart, [](double x, double y) { return x + y; });
+  if (lane == 0) {
+    sh.h[wave] = hpart;
+    sh.v[wave] = vpart;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
+    double H = sh.h[0], var = sh.v[0];
+#pragma unroll
+    for (int w = 1; w < kBalanceWaves; ++w) {
+      H += sh.h[w];
+      var += sh.v[w];
+    }
+    const long long mx = (long long)(int)((unsigned)(best >> 32) ^ 0x80000000u);
+    const int am = (int)(0xFFFFFFFFu - (unsigned)(best & 0xFFFFFFFFu));
     moer_load_stats_t r;
     r.total = tot;
     r.max_load = mx;
@@ -101,17 +123,6 @@ __device__ inline void block_load_stats(const int32_t* c, int N, moer_load_stats
     r.h_load_bits = H;
     r.cv = mean != 0.0 ? sqrt(var / (double)N) / mean : 0.0;
     *out = r;
-  }
-}
-
-// In-place sign-step update of bias[0..N) from c[0..N).
-__device__ inline void block_bias_update(float* bias, const int32_t* c, int N, float u,
-                                         BalanceScratch& sh) {
-  const long long tot = block_count_total(c, N, sh);
-  for (int e = threadIdx.x; e < N; e += kBalanceThreads) {
-    const long long diff = tot - (long long)N * c[e];
-    const float step = diff > 0 ? u : (diff < 0 ? -u : 0.f);
-    bias[e] = bias[e] + step;
   }
 }
 

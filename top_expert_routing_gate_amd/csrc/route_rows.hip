@@ -39,6 +39,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "moer_internal.hpp"
 
@@ -403,13 +406,29 @@ auto pick_kernel(const ScoreArgs& a) {
   return route_rows_kernel<EPL, GROUPED, kSoftmax>;
 }
 
+// Raise a kernel's dynamic LDS limit to what any N needs, once per kernel and
+// device (the attribute call is a host round trip; launches are hot).
+hipError_t allow_max_lds(const void* kernel) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& kd : done)
+    if (kd.first == kernel && kd.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)route_rows_lds_bytes(kMaxExperts));
+  if (e == hipSuccess) done.emplace_back(kernel, dev);
+  return e;
+}
+
 template <int EPL>
 hipError_t launch_epl(const ScoreArgs& a, int L, hipStream_t s) {
   const dim3 grid((a.T + kRowTokens - 1) / kRowTokens, L);
   const size_t lds = route_rows_lds_bytes(a.N);
   auto k = a.G > 1 ? pick_kernel<EPL, true>(a) : pick_kernel<EPL, false>(a);
-  const hipError_t e =
-      hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = allow_max_lds((const void*)k);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();

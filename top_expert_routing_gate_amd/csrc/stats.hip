@@ -8,13 +8,14 @@ namespace {
 __global__ __launch_bounds__(kBalanceThreads) void load_stats_kernel(
     const int32_t* __restrict__ counts, int N, int stride, moer_load_stats_t* out) {
   __shared__ BalanceScratch sh;
-  block_load_stats(counts + (size_t)blockIdx.x * stride, N, out + blockIdx.x, sh);
+  block_load_balance(counts + (size_t)blockIdx.x * stride, N, out + blockIdx.x, nullptr, 0.f, sh);
 }
 
 __global__ __launch_bounds__(kBalanceThreads) void bias_update_kernel(
     float* __restrict__ bias, const int32_t* __restrict__ counts, int N, int stride, float u) {
   __shared__ BalanceScratch sh;
-  block_bias_update(bias + (size_t)blockIdx.x * N, counts + (size_t)blockIdx.x * stride, N, u, sh);
+  block_load_balance(counts + (size_t)blockIdx.x * stride, N, nullptr, bias + (size_t)blockIdx.x * N,
+                     u, sh);
 }
 
 }  // namespace
