@@ -184,6 +184,37 @@ def test_ties_and_signed_zero_scores():
     assert _np(out["topk_idx"][0]).tolist() == [[0, 1], [1, 2]]
 
 
+@pytest.mark.parametrize("wl", [
+    workloads.scaled(WL["dsv3_group"], T=515),
+    workloads.scaled(WL["decode_layers"], T=200, n_layers=2),
+    workloads.scaled(WL["mixtral_top2"], T=300),
+], ids=lambda w: w.name)
+def test_heavy_ties_quantized_scores(wl):
+    """Scores drawn from a handful of values, so most tokens have dozens of
+    exactly tied keys (more than the kernels rank in LDS, which sends them to
+    the row-maximum rounds): ids and layout must still match the oracle bit
+    for bit under (key desc, id asc)."""
+    g = torch.Generator().manual_seed(77)
+    L, T, N = wl.n_layers, wl.T, wl.N
+    levels = torch.tensor([0.125, 0.25, 0.5, 0.75])
+    s32 = levels[torch.randint(0, 4, (L, T, N), generator=g)].numpy().astype(np.float32)
+    bias = None
+    if wl.bias_range:  # a bias on a coarse grid keeps keys tied
+        bias = (torch.randint(-2, 3, (L, N), generator=g).float() * 0.125)
+    out = moer.route(scores=torch.from_numpy(s32).to(DEV), K=wl.K, score_fn=wl.score_fn,
+                     n_groups=wl.n_groups, topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                     bias=None if bias is None else bias.to(DEV))
+    torch.cuda.synchronize()
+    for l in range(L):
+        ref = oracle.route(s32=s32[l], bias=None if bias is None else bias[l].numpy(), K=wl.K,
+                           score_fn=wl.score_fn, n_groups=wl.n_groups,
+                           topk_groups=wl.topk_groups, n_shared=wl.n_shared)
+        assert (_np(out["topk_idx"][l]) == ref["idx"]).all(), f"layer {l}"
+        assert np.allclose(_np(out["topk_w"][l]).astype(np.float64), ref["w"], rtol=1e-6,
+                           atol=1e-7)
+        _check_layout(out, l, ref["idx"], wl.Nb)
+
+
 def test_indices_mode_forcible_balance_and_invalid_ids():
     # MindIE's forcible balancing: supplied ids (t*K + k) mod N -> perfectly even load
     T, K, N = 1000, 8, 256

@@ -56,7 +56,6 @@ hipError_t launch_score_topk(const ScoreArgs& a, int L, hipStream_t s);
 // Row-per-token selection (writes the block histograms itself).
 int route_rows_epl(int N);
 bool route_rows_supports(int N, int G);
-size_t route_rows_lds_bytes(int N);
 hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s);
 hipError_t launch_load_stats(const int32_t* counts, int L, int N, int stride, moer_load_stats_t* out,

@@ -1,0 +1,383 @@
+// Per-token routing on one 16-lane DPP row: scores, bias-aware group-limited
+// top-k, combine weights, routing entropy and the block histogram.
+//
+// The method, per token (pages cited by title and section):
+//  1. scores: sigmoid s = 1/(1+exp(-h)) ("DeepSeek V4 MoE load balancing",
+//     token routing: sigmoid gating) or softmax p = exp(h)/sum exp(h)
+//     ("MoE Routing Entropy vs Expert Saturation", Mathematics); the given
+//     scores in SCORES mode. h includes the optional logit offset.
+//  2. key = s + b in fp32 (auxiliary-loss-free balancing: the bias steers the
+//     decision only); -0 is made +0.
+//  3. G > 1 ("DeepSeek-V3 Group-Limited Expert Routing", s.1 and s.3): group
+//     score = fp32 sum of the group's two largest keys; the Gk best groups
+//     (score desc, group id asc) stay eligible.
+//  4. the K best eligible keys (key desc, expert id asc) fill slots 0..K-1
+//     in that order; shared experts (same page, s.4) take slots K..Kt-1 with
+//     weight 1.
+//  5. weights: chosen unbiased scores over their sum (the top-k
+//     renormalisation of the dailyaiworld listing).
+//  6. entropy in bits of q = s / sum s (Mathematics section); q is returned
+//     for the callers' column sums (batch-mean entropy).
+//
+// Layout: a wavefront is 4 rows of 16 lanes; the row handles one token and
+// lane j of the row holds experts [j*EPL, (j+1)*EPL). Every cross-lane step
+// stays inside the row and is a DPP operation (quad permutes, half-row and
+// row mirrors, row shifts and rotations).
+//
+// Exact top-K without K argmax rounds:
+//  - lo = the K-th largest of the row's per-lane top-2 eligible keys; these
+//    are keys of distinct eligible experts, so lo is at most the K-th largest
+//    eligible key: every chosen expert has key >= lo.
+//  - the eligible keys >= lo (typically K to K+4) are compacted into LDS as
+//    packed 64-bit words (orderable key bits, then inverted id) with their
+//    scores, at positions from a row prefix scan of per-lane counts;
+//  - a candidate's slot is the number of candidates whose packed word is
+//    larger, i.e. that beat it under (key desc, id asc); slots < K are kept.
+//  - when more than kCandCap keys reach lo (heavy ties), the row instead runs
+//    K rounds of a row-wide maximum over the untaken eligible packed words.
+// Both give the unique answer under (key desc, id asc).
+#pragma once
+
+#include <math.h>
+
+#include "moer_internal.hpp"
+
+namespace moer {
+
+constexpr int kRowLanes = 16;
+constexpr int kCandCap = 32;                // candidates ranked in LDS per token
+constexpr int kCandStride = kCandCap + 1;   // words per row; the pad staggers banks
+
+// ---- DPP helpers (row = 16 lanes) -------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+// row shift right by n with zero fill (bound_ctrl)
+template <int N_>
+__device__ __forceinline__ int shr_zero(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N_, 0xF, 0xF, true);
+}
+
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kMirror = 0x140;     // lane i <-> 15-i within 16
+
+// All 16 lanes of a row receive max / min / sum of the row (bitwise equal in
+// every lane: each step combines a lane with a partner that combines the same
+// two operands).
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp_f<kXor1>(v));
+  v = fmaxf(v, dpp_f<kXor2>(v));
+  v = fmaxf(v, dpp_f<kHalfMirror>(v));
+  return fmaxf(v, dpp_f<kMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f<kXor1>(v);
+  v += dpp_f<kXor2>(v);
+  v += dpp_f<kHalfMirror>(v);
+  return v + dpp_f<kMirror>(v);
+}
+__device__ __forceinline__ int row_max_i(int v) {
+  v = max(v, dpp_i<kXor1>(v));
+  v = max(v, dpp_i<kXor2>(v));
+  v = max(v, dpp_i<kHalfMirror>(v));
+  return max(v, dpp_i<kMirror>(v));
+}
+// inclusive prefix sum over the row
+__device__ __forceinline__ int row_scan(int v) {
+  v += shr_zero<1>(v);
+  v += shr_zero<2>(v);
+  v += shr_zero<4>(v);
+  return v + shr_zero<8>(v);
+}
+// row maximum of 64-bit words held as (hi, lo) halves
+template <int CTRL>
+__device__ __forceinline__ void max_step_u64(unsigned& hi, unsigned& lo) {
+  const unsigned oh = (unsigned)dpp_i<CTRL>((int)hi);
+  const unsigned ol = (unsigned)dpp_i<CTRL>((int)lo);
+  if (oh > hi || (oh == hi && ol > lo)) {
+    hi = oh;
+    lo = ol;
+  }
+}
+__device__ __forceinline__ unsigned long long row_max_u64(unsigned long long v) {
+  unsigned hi = (unsigned)(v >> 32), lo = (unsigned)v;
+  max_step_u64<kXor1>(hi, lo);
+  max_step_u64<kXor2>(hi, lo);
+  max_step_u64<kHalfMirror>(hi, lo);
+  max_step_u64<kMirror>(hi, lo);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Orderable encoding: larger word <=> larger key, then smaller expert id.
+__device__ __forceinline__ unsigned long long pack_key(float key, int e) {
+  const unsigned f = __builtin_bit_cast(unsigned, key);
+  const unsigned u = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned)(0xFFFF - e);
+}
+
+// Score modes: the scores are given, or sigmoid / softmax of the affinities.
+enum { kGiven = 0, kSigmoid = 1, kSoftmax = 2 };
+
+// Hardware transcendentals (v_exp_f32, v_rcp_f32, v_log_f32: about 1 ulp):
+// the affinities already carry ~1e-6 GEMM rounding, so the scores only need
+// to be accurate well inside the 1e-3 weight and 1e-4 entropy tolerances.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int MODE>
+__device__ __forceinline__ float score_of(float v, float m, float inv_z) {
+  if (MODE == kGiven) return v;
+  if (MODE == kSigmoid) return rcp_hw(1.f + exp2_hw(-v * kLog2e));
+  return exp2_hw((v - m) * kLog2e) * inv_z;
+}
+
+// LDS scratch of one token row.
+struct RowLds {
+  unsigned long long* cand;  // [kCandStride]
+  float* cand_s;             // [kCandStride] score of each candidate
+  int* slot_id;              // [kMaxSlots]
+  float* slot_s;             // [kMaxSlots]
+};
+
+// Route token t of `layer` (live = t < T). v: the lane's EPL affinities (or
+// given scores), already summed over depth ranges, without the logit offset.
+// hist: the block histogram in LDS (cleared, and the clearing made visible by
+// a barrier, before the call). q: this lane's q = s / sum s (0 when dead).
+// All 16 lanes of the row must call together; rows are independent.
+template <int EPL, bool GROUPED, int MODE>
+__device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, bool live,
+                                          float (&v)[EPL], const RowLds& rs, int* hist,
+                                          float (&q)[EPL]) {
+  const int N = a.N, K = a.K, T = a.T;
+  const int Kt = K + a.n_shared;
+  const int rl = threadIdx.x & 15;  // lane within the row
+  const int e0 = rl * EPL;
+  const bool full = e0 + EPL <= N;  // every expert of this lane exists
+  const float NEG_INF = -__builtin_inff();
+  const size_t row_off = ((size_t)layer * T + (live ? t : 0)) * N;
+
+  if (rl < kMaxSlots) {
+    rs.slot_id[rl] = 0;
+    rs.slot_s[rl] = 0.f;
+  }
+  // 1. affinities (+ offset) and scores
+  if (MODE != kGiven) {
+    if (a.offset != nullptr) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[j] += a.offset[min(e0 + j, N - 1)];
+    }
+    if (live && a.h_out != nullptr) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (e0 + j < N) a.h_out[row_off + e0 + j] = v[j];
+    }
+  }
+  float m = 0.f, inv_z = 1.f;
+  if (MODE == kSoftmax) {
+    float lm = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) lm = fmaxf(lm, (full || e0 + j < N) ? v[j] : NEG_INF);
+    m = row_max(lm);
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) z += (full || e0 + j < N) ? exp2_hw((v[j] - m) * kLog2e) : 0.f;
+    inv_z = rcp_hw(row_sum(z));
+  }
+  float s[EPL], key[EPL];
+  if (full) {
+    const float* bias = a.bias != nullptr ? a.bias + (size_t)layer * N + e0 : nullptr;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      s[j] = score_of<MODE>(v[j], m, inv_z);
+      key[j] = (s[j] + (bias != nullptr ? bias[j] : 0.f)) + 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = e0 + j;
+      const float b = (a.bias != nullptr && e < N) ? a.bias[(size_t)layer * N + e] : 0.f;
+      s[j] = e < N ? score_of<MODE>(v[j], m, inv_z) : 0.f;
+      key[j] = e < N ? (s[j] + b) + 0.f : NEG_INF;
+    }
+  }
+
+  // 6. entropy of q = s / sum s
+  float ssum = 0.f, slog = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    ssum += s[j];
+    slog += s[j] > 0.f ? s[j] * log2_hw(s[j]) : 0.f;
+  }
+  ssum = row_sum(ssum);
+  slog = row_sum(slog);
+  if (live && rl == 0 && a.tok_entropy != nullptr)
+    a.tok_entropy[(size_t)layer * T + t] = ssum > 0.f ? log2f(ssum) - slog / ssum : 0.f;
+  const float inv_s = (live && ssum > 0.f) ? 1.f / ssum : 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) q[j] = s[j] * inv_s;
+
+  // 3. group-limited eligibility
+  bool eligible = true;
+  if (GROUPED) {
+    const int lpg = (N / a.G) / EPL;  // lanes per group (power of two, <= 16)
+    const int g = rl / lpg;
+    float m1 = key[0], m2 = NEG_INF;
+#pragma unroll
+    for (int j = 1; j < EPL; ++j) {
+      m2 = fmaxf(m2, fminf(m1, key[j]));
+      m1 = fmaxf(m1, key[j]);
+    }
+    // merge the group's lanes (lanes of a group are aligned, lpg a power of 2)
+    auto merge = [&](float b1, float b2) {
+      const float n2 = fmaxf(fminf(m1, b1), fmaxf(m2, b2));
+      m1 = fmaxf(m1, b1);
+      m2 = n2;
+    };
+    if (lpg >= 2) merge(dpp_f<kXor1>(m1), dpp_f<kXor1>(m2));
+    if (lpg >= 4) merge(dpp_f<kXor2>(m1), dpp_f<kXor2>(m2));
+    if (lpg >= 8) merge(dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
+    if (lpg >= 16) merge(dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
+    const float gs = (g < a.G) ? m1 + m2 : NEG_INF;
+    const int gid = g < a.G ? g : 0x7FFF;
+    // rank among the row's groups: rotate (score, id) by whole groups
+    int rank = 0;
+#define MOER_ROT(n)                                                                  \
+    if ((n) % lpg == 0) {                                                            \
+      const float og = dpp_f<0x120 + (n)>(gs);                                       \
+      const int oid = dpp_i<0x120 + (n)>(gid);                                       \
+      rank += (oid < a.G && (og > gs || (og == gs && oid < gid))) ? 1 : 0;           \
+    }
+    MOER_ROT(1) MOER_ROT(2) MOER_ROT(3) MOER_ROT(4) MOER_ROT(5) MOER_ROT(6) MOER_ROT(7)
+    MOER_ROT(8) MOER_ROT(9) MOER_ROT(10) MOER_ROT(11) MOER_ROT(12) MOER_ROT(13) MOER_ROT(14)
+    MOER_ROT(15)
+#undef MOER_ROT
+    eligible = g < a.G && rank < a.Gk;
+  }
+
+  // lo: K-th largest of the eligible lanes' two largest keys (keys of up to 32
+  // distinct eligible experts, so lo is at most the K-th largest eligible key)
+  float l1 = NEG_INF, l2 = NEG_INF;
+  if (eligible) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      l2 = fmaxf(l2, fminf(l1, key[j]));
+      l1 = fmaxf(l1, key[j]);
+    }
+  }
+  int c1 = 1 + (l2 >= l1 ? 1 : 0), c2 = 2;  // values >= l1 / >= l2, own pair included
+#define MOER_CGE(n)                                          \
+  {                                                          \
+    const float o1 = dpp_f<0x120 + (n)>(l1);                 \
+    const float o2 = dpp_f<0x120 + (n)>(l2);                 \
+    c1 += (o1 >= l1 ? 1 : 0) + (o2 >= l1 ? 1 : 0);           \
+    c2 += (o1 >= l2 ? 1 : 0) + (o2 >= l2 ? 1 : 0);           \
+  }
+  MOER_CGE(1) MOER_CGE(2) MOER_CGE(3) MOER_CGE(4) MOER_CGE(5) MOER_CGE(6) MOER_CGE(7)
+  MOER_CGE(8) MOER_CGE(9) MOER_CGE(10) MOER_CGE(11) MOER_CGE(12) MOER_CGE(13) MOER_CGE(14)
+  MOER_CGE(15)
+#undef MOER_CGE
+  const float lo = row_max(fmaxf(c1 >= K ? l1 : NEG_INF, c2 >= K ? l2 : NEG_INF));
+
+  // candidates: eligible keys >= lo
+  unsigned bits = 0;
+  if (eligible) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) bits |= (key[j] >= lo && key[j] > NEG_INF) ? 1u << j : 0u;
+  }
+  const int mine = __builtin_popcount(bits);
+  const int incl = row_scan(mine);
+  const int count = row_max_i(incl);
+  // A row's candidates and slots are private to its wavefront, and a
+  // wavefront's LDS operations complete in order: no barrier is needed.
+  if (count <= kCandCap) {
+    // 4. compact, then slot = number of candidates that beat this one
+    int pos = incl - mine;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (bits & (1u << j)) {
+        rs.cand[pos] = pack_key(key[j], e0 + j);
+        rs.cand_s[pos] = s[j];
+        ++pos;
+      }
+    for (int c = rl; c < count; c += kRowLanes) {
+      const unsigned long long my = rs.cand[c];
+      int r = 0;
+#pragma unroll 4
+      for (int i = 0; i < count; ++i) r += rs.cand[i] > my ? 1 : 0;
+      if (r < K) {
+        rs.slot_id[r] = 0xFFFF - (int)(my & 0xFFFF);
+        rs.slot_s[r] = rs.cand_s[c];
+      }
+    }
+  } else {
+    // heavy ties: K rounds of the row-wide best untaken candidate
+    unsigned taken = 0;
+    for (int r = 0; r < K; ++r) {
+      unsigned long long best = 0;
+      int bj = -1;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        if (!((bits >> j) & 1u) || ((taken >> j) & 1u)) continue;
+        const unsigned long long pk = pack_key(key[j], e0 + j);
+        if (pk > best) {
+          best = pk;
+          bj = j;
+        }
+      }
+      const unsigned long long win = row_max_u64(best);
+      if (bj >= 0 && best == win) {  // expert ids are unique: one owner lane
+        taken |= 1u << bj;
+        rs.slot_id[r] = e0 + bj;
+        float sb = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) sb = j == bj ? s[j] : sb;
+        rs.slot_s[r] = sb;
+      }
+    }
+  }
+
+  // 5. weights over the chosen slots, then the outputs and the histogram
+  int my_e = 0;
+  float my_s = 0.f;
+  if (rl < K) {
+    my_e = min(max(rs.slot_id[rl], 0), N - 1);  // in range even for non-finite input
+    my_s = rs.slot_s[rl];
+  }
+  const float zsel = row_sum(rl < K ? my_s : 0.f);
+  if (live && rl < Kt) {
+    const size_t o = ((size_t)layer * T + t) * Kt + rl;
+    if (rl < K) {
+      a.idx[o] = my_e;
+      a.w[o] = zsel > 0.f ? my_s / zsel : 1.f / (float)K;
+      atomicAdd(&hist[my_e], 1);
+    } else {
+      a.idx[o] = N + (rl - K);
+      a.w[o] = 1.f;
+      atomicAdd(&hist[N + (rl - K)], 1);
+    }
+  }
+}
+
+// Column sums of q over a wavefront's 4 rows: rows 0+1 and 2+3, then the two
+// pairs; both lanes of a pair add the same two operands, so every lane ends
+// with the bitwise-same sum. Must be called by all 64 lanes together.
+template <int EPL>
+__device__ __forceinline__ void wave_column_sums(const float (&q)[EPL], float (&col)[EPL]) {
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const float h = q[j] + __shfl_xor(q[j], 16, kWave);
+    col[j] = h + __shfl_xor(h, 32, kWave);
+  }
+}
+
+}  // namespace moer
