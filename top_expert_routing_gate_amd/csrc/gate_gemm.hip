@@ -1,200 +1,41 @@
-// Gate affinities h = x · W_g^T as fp32 partial sums over split ranges of d.
+// Gate affinities h = x · W_g^T as fp32 partial sums over split ranges of d
+// ("MoE Routing Entropy vs Expert Saturation", Mathematics: h_i = x · W_g;
+// W_g is [N][d], one row per expert).
 //
-// "MoE Routing Entropy vs Expert Saturation" (dailyaiworld), Mathematics:
-// the routing logits are h_i = x · W_g; its listing builds the gate as
-// nn.Linear(hidden, experts, bias=False), i.e. W_g is [N][d] with one row
-// per expert — the layout used here, so both operands are contiguous in the
-// reduction dimension d.
-//
-// bf16 products are exact in fp32 and are accumulated in fp32 by
-// v_mfma_f32_16x16x32_bf16. The MFMA "A" operand is a 16-expert slice of W_g
-// and "B" a 16-token slice of x, so a 16x16 result block holds D[e][t]: lane
-// l owns experts 4*(l/16)..+3 of token l%16 and stores them as one 16-byte
-// write. The depth d is split into `ksplit` equal ranges; range s writes
+// The depth d is split into `ksplit` equal ranges; range s writes
 // part[s][l][t][e]. The selection kernel adds the ranges in order s = 0, 1,
-// ... (and the logit offset), so the result is deterministic.
-#include "moer_internal.hpp"
+// ... (and the logit offset), so the result is deterministic. The pipelined
+// tile (gemm_pipeline.hpp) needs d to be a multiple of 64 per range; other d
+// take the register-staged kernel below, fp32 inputs a plain FMA kernel.
+#include "gemm_pipeline.hpp"
 
 namespace moer {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-constexpr int kKStage = 64;           // reduction depth per LDS stage (bf16)
-constexpr int kChunks = kKStage / 8;  // 16-byte chunks per staged row
-
-// s_waitcnt immediate (gfx9 encoding) for vmcnt <= n and lgkmcnt == 0: this
-// wave's DMA stages up to the wanted one have landed and its own LDS reads
-// have completed.
-constexpr int wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
-constexpr int kNoVmWait = 63;  // vmcnt field at its maximum: wait for LDS only
-
-// Workgroup barrier that orders LDS traffic at compile time only (asm memory
-// clobbers); the hardware side is the explicit s_waitcnt before it.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // ---------------------------------------------------------------------------
-// Pipelined kernel (d a multiple of 64 * ksplit).
-//
-// Workgroup tile: BT tokens x BE experts over one depth range. The
-// workgroup's waves have two roles:
-//  - WT x WE consumer waves, each owning (BT/WT) x (BE/WE) in 16x16 MFMA
-//    blocks, read operand fragments from LDS and issue the MFMAs;
-//  - NP producer waves stream the operand tiles into an NSTAGE-deep LDS ring
-//    with global_load_lds_dwordx4 (no VGPR staging).
-// Splitting the roles matters on CDNA: a wave that issues a long run of
-// loads stalls in the issue stage while the memory pipeline back-pressures,
-// and a wave's MFMAs cannot issue past its own stalled loads. With separate
-// waves the matrix cores run while the producers wait.
-//
-// Each producer instruction fills 64 consecutive 16-byte LDS slots, and each
-// lane fetches the global chunk that belongs in its slot under the XOR
-// swizzle slot(r, q) = r*8 + (q ^ (r%8)), which makes the 16-byte fragment
-// reads of 8 consecutive rows conflict-free. Rows past T or N are clamped to
-// the last valid row (their results are never stored); d must be a multiple
-// of the stage depth so no chunk is partial.
-//
-// One workgroup barrier per stage orders the ring: before barrier k the
-// producers wait until their stage-k loads have landed, and the consumers
-// have finished reading stage k-1; after it the consumers read stage k and
-// the producers refill the buffer of stage k-1 with stage k+NSTAGE-1.
-//
-// Workgroups are numbered so that consecutive tiles of one (layer, depth
-// range) land on the same XCD (dispatch is round-robin over the 8 XCDs):
-// every XCD then streams one part of W_g through its own L2.
+// Pipelined kernel: producer waves stream the tiles, consumer waves run the
+// MFMAs and store the depth range's partial affinities.
 template <int BT, int BE, int WT, int WE, int NP, int NSTAGE>
 __global__ __launch_bounds__((WT * WE + NP) * kWave, 1) void gate_gemm_dma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
     int L, int T, int d, int N, int ksplit, int n_tt, int n_te, int n_work, int per_xcd) {
-  constexpr int kConsumers = WT * WE;
-  constexpr int kRows = BT + BE;
-  constexpr int kStageSlots = kRows * kChunks;
-  constexpr int kLoads = kStageSlots / (NP * kWave);  // DMA instructions per producer per stage
-  constexpr int MT = BT / WT / 16;
-  constexpr int ME = BE / WE / 16;
-  static_assert(kStageSlots % (NP * kWave) == 0, "stage must split evenly over the producers");
-  static_assert((NSTAGE - 2) * kLoads <= 63, "outstanding loads must fit the vmcnt field");
-  static_assert(BT % (WT * 16) == 0 && BE % (WE * 16) == 0, "tile shape");
-
-  __shared__ u32x4 ring[NSTAGE][kStageSlots];
-
-  // XCD-aware work index: dispatch slot b runs on XCD b % 8.
-  const int b = blockIdx.x;
-  const int work = (b % 8) * per_xcd + b / 8;
-  if (work >= n_work) return;
-  int rest = work;
-  const int tt = rest % n_tt; rest /= n_tt;
-  const int te = rest % n_te; rest /= n_te;
-  const int ks = rest % ksplit; rest /= ksplit;
-  const int layer = rest;
-
-  const int t0 = tt * BT, e0 = te * BE;
+  using P = GemmPipeline<BT, BE, WT, WE, NP, NSTAGE>;
+  __shared__ u32x4 ring[NSTAGE][P::kStageSlots];
+  GemmWork w;
+  if (!decode_work(n_tt, n_te, ksplit, n_work, per_xcd, w)) return;
+  const int t0 = w.tt * BT, e0 = w.te * BE;
   const int krange = d / ksplit;
-  const int kbeg = ks * krange;
   const int nk = krange / kKStage;
-  x += (size_t)layer * T * d;
-  W += (size_t)layer * N * d;
-
-  const int lane = threadIdx.x & 63;
+  x += (size_t)w.layer * T * d;
+  W += (size_t)w.layer * N * d;
   const int wave = threadIdx.x >> 6;
-
-  if (wave >= kConsumers) {
-    // ---- producer ----
-    const int pw = wave - kConsumers;
-    const uint16_t* src[kLoads];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int slot = (i * NP + pw) * kWave + lane;
-      const int r = slot / kChunks;
-      const int q = (slot % kChunks) ^ (r & 7);
-      const uint16_t* row = r < BT ? x + (size_t)min(t0 + r, T - 1) * d
-                                   : W + (size_t)min(e0 + r - BT, N - 1) * d;
-      src[i] = row + kbeg + q * 8;
-    }
-    auto issue = [&](int stage_k, int buf) {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + stage_k * kKStage),
-                                         LDS_PTR(&ring[buf][(i * NP + pw) * kWave]), 16, 0, 0);
-    };
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-      if (s < nk) issue(s, s);
-    for (int k = 0; k < nk; ++k) {
-      // stage k has landed once at most the later issued stages are pending
-      if (k + NSTAGE - 2 < nk)
-        __builtin_amdgcn_s_waitcnt(wait_imm((NSTAGE - 2) * kLoads));
-      else
-        __builtin_amdgcn_s_waitcnt(wait_imm(0));
-      ring_barrier();
-      if (k + NSTAGE - 1 < nk) issue(k + NSTAGE - 1, (k + NSTAGE - 1) % NSTAGE);
-    }
+  if (wave >= P::kConsumers) {
+    P::produce(ring, x, W, t0, e0, T, N, d, w.ks * krange, nk, wave - P::kConsumers);
     return;
   }
-
-  // ---- consumer ----
-  const int wt = wave / WE;
-  const int we = wave % WE;
-  floatx4 acc[ME][MT];
-#pragma unroll
-  for (int i = 0; i < ME; ++i)
-#pragma unroll
-    for (int j = 0; j < MT; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int frow = lane & 15;
-  const int fq = lane >> 4;
-  for (int k = 0; k < nk; ++k) {
-    // own fragment reads of stage k-1 complete before its buffer is refilled
-    __builtin_amdgcn_s_waitcnt(wait_imm(kNoVmWait));
-    ring_barrier();
-    const u32x4* buf = ring[k % NSTAGE];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 a[ME], bb[MT];
-      const int q = kk * 4 + fq;
-#pragma unroll
-      for (int i = 0; i < ME; ++i) {
-        const int r = BT + (we * ME + i) * 16 + frow;
-        a[i] = __builtin_bit_cast(bf16x8, buf[r * kChunks + (q ^ (r & 7))]);
-      }
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        const int r = (wt * MT + j) * 16 + frow;
-        bb[j] = __builtin_bit_cast(bf16x8, buf[r * kChunks + (q ^ (r & 7))]);
-      }
-#pragma unroll
-      for (int i = 0; i < ME; ++i)
-#pragma unroll
-        for (int j = 0; j < MT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  float* out = part + ((size_t)ks * L + layer) * T * N;
-#pragma unroll
-  for (int i = 0; i < ME; ++i) {
-    const int e = e0 + (we * ME + i) * 16 + 4 * fq;
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int t = t0 + (wt * MT + j) * 16 + frow;
-      if (t >= T) continue;
-      float* row = out + (size_t)t * N;
-      if (e + 3 < N && (N & 3) == 0) {
-        *reinterpret_cast<floatx4*>(row + e) = acc[i][j];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (e + r < N) row[e + r] = acc[i][j][r];
-      }
-    }
-  }
+  floatx4 acc[P::ME][P::MT];
+  P::consume(ring, nk, wave / WE, wave % WE, acc);
+  P::store(acc, part + ((size_t)w.ks * L + w.layer) * T * N, t0, e0, T, N, wave / WE, wave % WE);
 }
 
 // ---------------------------------------------------------------------------

@@ -7,15 +7,15 @@
 //
 // Histograms per 64-token block, cnt[l][e][b] (uint16, expert-major), come
 // from the selection kernel or, for supplied ids, from layout_count below.
-// layout_scatter then runs one workgroup per 128 tokens (two histogram
-// blocks): each workgroup reads its layer's histograms row by row for its
-// experts (contiguous 16-byte loads), derives expert totals, their exclusive
-// scan (the offsets) and its own prefix over earlier blocks, and places its
-// assignments; in-block stable ranks come from per-64-slot LDS membership
-// bitmaps (popcount of the lower bits). One extra workgroup per layer sums
-// the per-block column sums of q into the entropy of the batch mean, and
-// another (when asked) derives the load statistics and the bias update from
-// the same histograms, so neither waits for the other.
+// layout_prefix then runs one wave per expert: a scan over the expert's
+// block counts gives tot[e] and, for every 128-token layout block lb,
+// pre[lb][e] = the expert's assignments in earlier tokens. layout_scatter
+// runs one workgroup per layout block: it reads its pre row and tot, scans
+// tot into the offsets and places its assignments; in-block stable ranks
+// come from per-64-slot LDS membership bitmaps (popcount of the lower bits).
+// Two extra workgroups per layer compute the entropy of the batch-mean
+// routing distribution from the per-block column sums of q and, when asked,
+// the load statistics and the bias update from tot.
 #include <math.h>
 
 #include "load_balance.hpp"
@@ -53,22 +53,72 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
   for (int e = threadIdx.x; e < a.Nb; e += kThreads) out[(size_t)e * a.nsb] = (uint16_t)hist[e];
 }
 
-// Exclusive scan of v[0..n) in LDS (n <= 2 * kThreads), deterministic.
+// Per expert (one wave each): tot[e] and, for every layout block lb,
+// pre[lb][e] = sum of cnt[e][b] over histogram blocks b < lb * 2.
+__global__ __launch_bounds__(kThreads) void layout_prefix_kernel(LayoutArgs a) {
+  constexpr int kPerLane = 4;                     // histogram blocks per lane per round
+  constexpr int kRound = kWave * kPerLane;        // 256 blocks per round
+  static_assert(kPerLane % kBlocksPerLayoutBlock == 0, "a lane covers whole layout blocks");
+  const int layer = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  if (e >= a.Nb) return;  // whole wave
+  const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
+  int32_t* pre = a.pre + (size_t)layer * a.nlb * a.Nb + e;
+  int carry = 0;
+  for (int b0 = 0; b0 < a.nsb; b0 += kRound) {
+    int c[kPerLane];
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+      const int b = b0 + lane * kPerLane + k;
+      c[k] = b < a.nsb ? row[b] : 0;
+    }
+    int x = 0;
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) x += c[k];
+    // inclusive scan over the wave
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      incl += lane >= o ? y : 0;
+    }
+    int run = carry + incl - x;  // assignments before this lane's first block
+#pragma unroll
+    for (int k = 0; k < kPerLane; k += kBlocksPerLayoutBlock) {
+      const int b = b0 + lane * kPerLane + k;
+      if (b < a.nsb) pre[(size_t)(b / kBlocksPerLayoutBlock) * a.Nb] = run;
+#pragma unroll
+      for (int j = 0; j < kBlocksPerLayoutBlock; ++j) run += c[k + j];
+    }
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  if (a.nsb == 0 && lane == 0) pre[0] = 0;  // empty batch: one (empty) layout block
+  if (lane == 0) a.tot[(size_t)layer * a.Nb + e] = carry;
+}
+
+// Exclusive scan of v[0..n) in LDS (n <= 2 * kThreads), deterministic:
+// each thread adds its pair, waves scan with lane shuffles, then the wave
+// totals are added in wave order.
 __device__ void block_exclusive_scan(int* v, int* tmp, int n) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int i0 = 2 * tid, i1 = 2 * tid + 1;
   const int a0 = i0 < n ? v[i0] : 0;
   const int a1 = i1 < n ? v[i1] : 0;
-  tmp[tid] = a0 + a1;
-  __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {
-    const int add = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  int x = a0 + a1;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    x += lane >= o ? y : 0;
   }
-  const int excl = tmp[tid] - (a0 + a1);
+  if (lane == kWave - 1) tmp[wave] = x;
   __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += tmp[w];
+  const int excl = base + x - (a0 + a1);
+  // each thread rewrites only the two entries it read
   if (i0 < n) v[i0] = excl;
   if (i1 < n) v[i1] = excl + a0;
   __syncthreads();
@@ -139,38 +189,12 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
   if (threadIdx.x == 0) a.agg_entropy[layer] = a.T > 0 ? red[0] : 0.f;
 }
 
-// Per expert e < Nb: total[e] = assignments over all histogram blocks of the
-// layer, pre[e] = those in blocks before b_first; total[e] = 0 for e >= Nb.
-__device__ void expert_totals(const LayoutArgs& a, int layer, int b_first, int* total, int* pre) {
-  const int Nb = a.Nb;
-  const uint16_t* cnt = a.cnt + (size_t)layer * Nb * a.nsb;
-  const bool vec = (a.nsb & 7) == 0;
+// total[e] = the layer's assignments of expert e (0 for e >= Nb) and, with
+// lb >= 0, pre[e] = those in tokens before layout block lb.
+__device__ void load_totals(const LayoutArgs& a, int layer, int lb, int* total, int* pre) {
   for (int e = threadIdx.x; e < 2 * kThreads; e += kThreads) {
-    int tot = 0, p = 0;
-    if (e < Nb) {
-      const uint16_t* row = cnt + (size_t)e * a.nsb;
-      if (vec) {
-#pragma unroll 8
-        for (int b = 0; b < a.nsb; b += 8) {
-          const uint4 w = *reinterpret_cast<const uint4*>(row + b);
-          const unsigned ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int lo = ww[k] & 0xFFFF, hi = ww[k] >> 16;
-            tot += lo + hi;
-            p += (b + 2 * k < b_first ? lo : 0) + (b + 2 * k + 1 < b_first ? hi : 0);
-          }
-        }
-      } else {
-        for (int b = 0; b < a.nsb; ++b) {
-          const int c = row[b];
-          tot += c;
-          p += b < b_first ? c : 0;
-        }
-      }
-      pre[e] = p;
-    }
-    total[e] = tot;
+    total[e] = e < a.Nb ? a.tot[(size_t)layer * a.Nb + e] : 0;
+    if (lb >= 0 && e < a.Nb) pre[e] = a.pre[((size_t)layer * a.nlb + lb) * a.Nb + e];
   }
 }
 
@@ -178,7 +202,7 @@ __device__ void expert_totals(const LayoutArgs& a, int layer, int b_first, int* 
 // (one workgroup per layer, beside the scatter workgroups).
 __device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* total, int* pre) {
   __shared__ BalanceScratch bal;
-  expert_totals(a, layer, 0, total, pre);
+  load_totals(a, layer, -1, total, pre);
   __syncthreads();
   block_load_balance(total, a.N, a.stats != nullptr ? a.stats + layer : nullptr,
                      a.bias_inout != nullptr ? a.bias_inout + (size_t)layer * a.N : nullptr,
@@ -187,7 +211,7 @@ __device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* tot
 
 // Workgroups [0, nlb) place 128 tokens each; then, if requested, one
 // workgroup for the batch-mean entropy and one for load balancing.
-__global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void layout_scatter_kernel(LayoutArgs a) {
   __shared__ int total[2 * kThreads];
   __shared__ int pre[kMaxBuckets];
   __shared__ int scan_tmp[kThreads];
@@ -211,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) 
   const size_t lbase = (size_t)layer * a.T * a.Kt;
   const int flat0 = t0 * a.Kt;
 
-  // per expert: total over all histogram blocks, and over the blocks before ours
-  expert_totals(a, layer, blk * kBlocksPerLayoutBlock, total, pre);
+  // per expert: all assignments, and those in tokens before this block
+  load_totals(a, layer, blk, total, pre);
   for (int c = 0; c < nchunk; ++c)
     for (int e = threadIdx.x; e < Nb; e += kThreads) bits[c][e] = 0ull;
   __syncthreads();
@@ -227,9 +251,18 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) 
   }
 
   // membership bitmaps: bit i of bits[c][e] <=> slot c*64+i of this block is e
-  for (int i = threadIdx.x; i < nslot; i += kThreads) {
-    const int e = a.idx[lbase + flat0 + i];
-    if (e >= 0 && e < Nb) atomicOr(&bits[i >> 6][e], 1ull << (i & 63));
+  constexpr int kIdsPerThread = kMaxSlotsPerBlock / kThreads;
+  int ids[kIdsPerThread];
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    ids[k] = i < nslot ? a.idx[lbase + flat0 + i] : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    const int e = ids[k];
+    if (i < nslot && e >= 0 && e < Nb) atomicOr(&bits[i >> 6][e], 1ull << (i & 63));
   }
   __syncthreads();
   for (int e = threadIdx.x; e < Nb; e += kThreads) {
@@ -240,8 +273,11 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) 
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nslot; i += kThreads) {
-    const int e = a.idx[lbase + flat0 + i];
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    if (i >= nslot) break;
+    const int e = ids[k];
     const int flat = flat0 + i;
     if (e >= 0 && e < Nb) {
       const int c = i >> 6;
@@ -260,9 +296,13 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(LayoutArgs a) 
 hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s) {
   if (a.need_count) {
     hipLaunchKernelGGL(layout_count_kernel, dim3(a.nsb, L), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const hipError_t ec = hipGetLastError();
+    if (ec != hipSuccess) return ec;
   }
+  hipLaunchKernelGGL(layout_prefix_kernel, dim3((a.Nb + kThreads / kWave - 1) / (kThreads / kWave), L),
+                     dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // a.nlb >= 1 (an empty batch still writes zero counts and offsets)
   const int extra = (a.agg_entropy != nullptr ? 1 : 0) +
                     (a.stats != nullptr || a.bias_inout != nullptr ? 1 : 0);

@@ -32,7 +32,7 @@ bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 // Workspace regions (byte offsets) for a validated descriptor.
 struct Plan {
   int Kt, Nb, nsb, nlb, ksplit;
-  size_t off_h, off_colpart, off_cnt, total;
+  size_t off_h, off_colpart, off_cnt, off_pre, off_tot, total;
 };
 
 Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
@@ -50,6 +50,10 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   if (want_agg) o += align_up(L * p.nsb * d.N * sizeof(float) + 16);
   p.off_cnt = o;  // expert histograms per 64-token block (uint16)
   o += align_up(L * p.Nb * p.nsb * sizeof(uint16_t) + 16);
+  p.off_pre = o;  // per layout block: each expert's assignments in earlier tokens
+  o += align_up(L * p.nlb * p.Nb * sizeof(int32_t));
+  p.off_tot = o;  // per expert: all assignments
+  o += align_up(L * p.Nb * sizeof(int32_t));
   p.total = o;
   return p;
 }
@@ -230,6 +234,8 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   moer::LayoutArgs la{};
   la.idx = indices ? io->idx_in : io->topk_idx;
   la.cnt = cnt;
+  la.pre = reinterpret_cast<int32_t*>(ws + p.off_pre);
+  la.tot = reinterpret_cast<int32_t*>(ws + p.off_tot);
   la.colpart = colpart;
   la.agg_entropy = want_agg ? io->agg_entropy : nullptr;
   la.counts = io->counts;

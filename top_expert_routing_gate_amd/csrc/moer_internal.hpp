@@ -33,6 +33,8 @@ struct ScoreArgs {
 struct LayoutArgs {
   const int32_t* idx;     // [L][T][Kt]
   uint16_t* cnt;          // [L][Nb][nsb] expert counts per 64-token block
+  int32_t* pre;           // [L][nlb][Nb] assignments of expert e before layout block lb
+  int32_t* tot;           // [L][Nb] assignments of expert e
   const float* colpart;   // [L][nsb][N] or nullptr
   float* agg_entropy;     // [L] or nullptr
   int32_t* counts;        // [L][Nb]

@@ -149,15 +149,47 @@ struct RowLds {
   float* slot_s;             // [kMaxSlots]
 };
 
+// The lane's per-expert constants of a layer, loaded once (and early, so
+// their latency hides under the affinity loads): selection bias and logit
+// offset of experts e0 .. e0+EPL-1 (0 past N or when absent).
+template <int EPL>
+struct LaneConsts {
+  float bias[EPL];
+  float offset[EPL];
+};
+template <int EPL>
+__device__ __forceinline__ void load_lane_consts(const ScoreArgs& a, int layer, bool with_offset,
+                                                 LaneConsts<EPL>& c) {
+  const int e0 = (threadIdx.x & 15) * EPL;
+  const float* b = a.bias != nullptr ? a.bias + (size_t)layer * a.N : nullptr;
+  const float* o = with_offset ? a.offset : nullptr;
+  auto fill = [&](const float* src, float (&dst)[EPL]) {
+    if (src != nullptr && EPL % 4 == 0 && e0 + EPL <= a.N && (a.N & 3) == 0) {
+#pragma unroll
+      for (int j = 0; j < EPL / 4; ++j) {
+        const float4 f = reinterpret_cast<const float4*>(src + e0)[j];
+        dst[4 * j] = f.x; dst[4 * j + 1] = f.y; dst[4 * j + 2] = f.z; dst[4 * j + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) dst[j] = (src != nullptr && e0 + j < a.N) ? src[e0 + j] : 0.f;
+    }
+  };
+  fill(b, c.bias);
+  fill(o, c.offset);
+}
+
 // Route token t of `layer` (live = t < T). v: the lane's EPL affinities (or
 // given scores), already summed over depth ranges, without the logit offset.
-// hist: the block histogram in LDS (cleared, and the clearing made visible by
-// a barrier, before the call). q: this lane's q = s / sum s (0 when dead).
-// All 16 lanes of the row must call together; rows are independent.
-template <int EPL, bool GROUPED, int MODE>
+// LPG: lanes per expert group when fixed at compile time, 0 = from a.G at
+// run time (GROUPED only). hist: the block histogram in LDS (cleared, and
+// the clearing made visible by a barrier, before the call). q: this lane's
+// q = s / sum s (0 when dead). All 16 lanes of the row must call together;
+// rows are independent.
+template <int EPL, bool GROUPED, int MODE, int LPG = 0>
 __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, bool live,
-                                          float (&v)[EPL], const RowLds& rs, int* hist,
-                                          float (&q)[EPL]) {
+                                          float (&v)[EPL], const LaneConsts<EPL>& lc,
+                                          const RowLds& rs, int* hist, float (&q)[EPL]) {
   const int N = a.N, K = a.K, T = a.T;
   const int Kt = K + a.n_shared;
   const int rl = threadIdx.x & 15;  // lane within the row
@@ -174,7 +206,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   if (MODE != kGiven) {
     if (a.offset != nullptr) {
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) v[j] += a.offset[min(e0 + j, N - 1)];
+      for (int j = 0; j < EPL; ++j) v[j] += lc.offset[j];
     }
     if (live && a.h_out != nullptr) {
 #pragma unroll
@@ -195,19 +227,17 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   }
   float s[EPL], key[EPL];
   if (full) {
-    const float* bias = a.bias != nullptr ? a.bias + (size_t)layer * N + e0 : nullptr;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       s[j] = score_of<MODE>(v[j], m, inv_z);
-      key[j] = (s[j] + (bias != nullptr ? bias[j] : 0.f)) + 0.f;
+      key[j] = (s[j] + lc.bias[j]) + 0.f;
     }
   } else {
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = e0 + j;
-      const float b = (a.bias != nullptr && e < N) ? a.bias[(size_t)layer * N + e] : 0.f;
       s[j] = e < N ? score_of<MODE>(v[j], m, inv_z) : 0.f;
-      key[j] = e < N ? (s[j] + b) + 0.f : NEG_INF;
+      key[j] = e < N ? (s[j] + lc.bias[j]) + 0.f : NEG_INF;
     }
   }
 
@@ -229,7 +259,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   // 3. group-limited eligibility
   bool eligible = true;
   if (GROUPED) {
-    const int lpg = (N / a.G) / EPL;  // lanes per group (power of two, <= 16)
+    const int lpg = LPG > 0 ? LPG : (N / a.G) / EPL;  // lanes per group (power of two, <= 16)
     const int g = rl / lpg;
     float m1 = key[0], m2 = NEG_INF;
 #pragma unroll

@@ -48,7 +48,7 @@ __device__ __forceinline__ void load_row(const ScoreArgs& a, size_t row_off, siz
   }
 }
 
-template <int EPL, bool GROUPED, int MODE>
+template <int EPL, bool GROUPED, int MODE, int LPG>
 __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   __shared__ unsigned long long cand[kRowTokens][kCandStride];
   __shared__ float cand_s[kRowTokens][kCandStride];
@@ -68,6 +68,8 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   const bool live = t < T;
 
   for (int i = threadIdx.x; i < Nb; i += kThreads) hist[i] = 0;
+  LaneConsts<EPL> lc;
+  load_lane_consts<EPL>(a, layer, MODE != kGiven, lc);
   const size_t row_off = ((size_t)layer * T + (live ? t : 0)) * N;
   const size_t split_stride = (size_t)gridDim.y * T * N;
   float v[EPL];
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
 
   const RowLds rs{cand[row], cand_s[row], slot_id[row], slot_s[row]};
   float q[EPL], col[EPL];
-  route_row<EPL, GROUPED, MODE>(a, layer, t, live, v, rs, hist, q);
+  route_row<EPL, GROUPED, MODE, LPG>(a, layer, t, live, v, lc, rs, hist, q);
   wave_column_sums<EPL>(q, col);
   if (a.colpart != nullptr) {
     // every lane stores (the 4 rows of a wavefront hold identical sums), so
@@ -102,17 +104,21 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   }
 }
 
-template <int EPL, bool GROUPED>
+template <int EPL, bool GROUPED, int LPG = 0>
 auto pick_kernel(const ScoreArgs& a) {
-  if (!a.apply_score) return route_rows_kernel<EPL, GROUPED, kGiven>;
-  if (a.score_fn == 1) return route_rows_kernel<EPL, GROUPED, kSigmoid>;
-  return route_rows_kernel<EPL, GROUPED, kSoftmax>;
+  if (!a.apply_score) return route_rows_kernel<EPL, GROUPED, kGiven, LPG>;
+  if (a.score_fn == 1) return route_rows_kernel<EPL, GROUPED, kSigmoid, LPG>;
+  return route_rows_kernel<EPL, GROUPED, kSoftmax, LPG>;
 }
 
 template <int EPL>
 hipError_t launch_epl(const ScoreArgs& a, int L, hipStream_t s) {
   const dim3 grid((a.T + kRowTokens - 1) / kRowTokens, L);
-  auto k = a.G > 1 ? pick_kernel<EPL, true>(a) : pick_kernel<EPL, false>(a);
+  // the DeepSeek-V3 geometry (groups of 32 experts, 2 row lanes per group)
+  // gets a kernel with the group width fixed at compile time
+  const bool two_lane_groups = EPL == 16 && a.G > 1 && a.N / a.G == 2 * EPL;
+  auto k = a.G > 1 ? (two_lane_groups ? pick_kernel<EPL, true, 2>(a) : pick_kernel<EPL, true>(a))
+                   : pick_kernel<EPL, false>(a);
   hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
