@@ -18,9 +18,12 @@ namespace {
 template <int BT, int BE, int WT, int WE, int NP, int NSTAGE>
 __global__ __launch_bounds__((WT * WE + NP) * kWave, 1) void gate_gemm_dma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
-    int L, int T, int d, int N, int ksplit, int n_tt, int n_te, int n_work, int per_xcd) {
+    int L, int T, int d, int N, int ksplit, int n_tt, int n_te, int n_work, int per_xcd,
+    int32_t* __restrict__ zero, int n_zero) {
   using P = GemmPipeline<BT, BE, WT, WE, NP, NSTAGE>;
   __shared__ u32x4 ring[NSTAGE][P::kStageSlots];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += P::kThreads) zero[i] = 0;
   GemmWork w;
   if (!decode_work(n_tt, n_te, ksplit, n_work, per_xcd, w)) return;
   const int t0 = w.tt * BT, e0 = w.te * BE;
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(256) void gate_gemm_f32_kernel(const float* __restr
 
 template <int BT, int BE, int WT, int WE, int NP, int NSTAGE>
 hipError_t launch_dma(const void* x, const void* w, float* part, int L, int T, int d, int N,
-                      int ksplit, hipStream_t s) {
+                      int ksplit, int32_t* zero, int n_zero, hipStream_t s) {
   const int n_tt = (T + BT - 1) / BT;
   const int n_te = (N + BE - 1) / BE;
   const int n_work = L * ksplit * n_te * n_tt;
@@ -194,7 +197,7 @@ hipError_t launch_dma(const void* x, const void* w, float* part, int L, int T, i
   hipLaunchKernelGGL((gate_gemm_dma_kernel<BT, BE, WT, WE, NP, NSTAGE>), dim3(8 * per_xcd),
                      dim3((WT * WE + NP) * kWave), 0, s, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(w), part, L, T, d, N, ksplit, n_tt, n_te,
-                     n_work, per_xcd);
+                     n_work, per_xcd, zero, n_zero);
   return hipGetLastError();
 }
 
@@ -223,11 +226,27 @@ int gate_gemm_ksplit(int dtype_bf16, int L, int T, int d, int N) {
   return ks;
 }
 
+bool gate_gemm_clears(int L, int T, int d, int N, int ksplit) {
+  return L > 0 && T > 0 && d % (kKStage * ksplit) == 0;
+}
+
+__global__ void zero_ints_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int L, int T, int d,
-                                 int N, int ksplit, hipStream_t s) {
+                                 int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s) {
   if (d % (kKStage * ksplit) == 0) {
-    if (small_n(N)) return launch_dma<64, 32, 4, 1, 4, 3>(x, w, part, L, T, d, N, ksplit, s);
-    return launch_dma<128, 256, 2, 2, 4, 3>(x, w, part, L, T, d, N, ksplit, s);
+    if (small_n(N))
+      return launch_dma<64, 32, 4, 1, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s);
+    return launch_dma<128, 256, 2, 2, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s);
   }
   if (ksplit != 1) return hipErrorInvalidValue;
   if (N <= 16) return launch_tile<16, 64, 1, 4>(x, w, part, L, T, d, N, s);

@@ -7,15 +7,17 @@
 //
 // Histograms per 64-token block, cnt[l][e][b] (uint16, expert-major), come
 // from the selection kernel or, for supplied ids, from layout_count below.
-// layout_prefix then runs one wave per expert: a scan over the expert's
-// block counts gives tot[e] and, for every 128-token layout block lb,
-// pre[lb][e] = the expert's assignments in earlier tokens. layout_scatter
-// runs one workgroup per layout block: it reads its pre row and tot, scans
-// tot into the offsets and places its assignments; in-block stable ranks
-// come from per-64-slot LDS membership bitmaps (popcount of the lower bits).
-// Two extra workgroups per layer compute the entropy of the batch-mean
-// routing distribution from the per-block column sums of q and, when asked,
-// the load statistics and the bias update from tot.
+// The same kernels add every block histogram into segsum[l][s][e], the
+// counts of segment s = 16 consecutive blocks (integer atomics: the sums do
+// not depend on the order). layout_scatter runs one workgroup per 128-token
+// layout block: an expert's total is the sum of its segments, and its
+// assignments before the block are the earlier segments plus the earlier
+// blocks of the block's own segment (at most 15 + 14 reads per expert). It
+// scans the totals into the offsets and places its assignments; in-block
+// stable ranks come from per-64-slot LDS membership bitmaps (popcount of the
+// lower bits). Two extra workgroups per layer compute the entropy of the
+// batch-mean routing distribution from the per-block column sums of q and,
+// when asked, the load statistics and the bias update from the totals.
 #include <math.h>
 
 #include "load_balance.hpp"
@@ -50,51 +52,11 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
   }
   __syncthreads();
   uint16_t* out = a.cnt + (size_t)layer * a.Nb * a.nsb + blk;
-  for (int e = threadIdx.x; e < a.Nb; e += kThreads) out[(size_t)e * a.nsb] = (uint16_t)hist[e];
-}
-
-// Per expert (one wave each): tot[e] and, for every layout block lb,
-// pre[lb][e] = sum of cnt[e][b] over histogram blocks b < lb * 2.
-__global__ __launch_bounds__(kThreads) void layout_prefix_kernel(LayoutArgs a) {
-  constexpr int kPerLane = 4;                     // histogram blocks per lane per round
-  constexpr int kRound = kWave * kPerLane;        // 256 blocks per round
-  static_assert(kPerLane % kBlocksPerLayoutBlock == 0, "a lane covers whole layout blocks");
-  const int layer = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
-  if (e >= a.Nb) return;  // whole wave
-  const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
-  int32_t* pre = a.pre + (size_t)layer * a.nlb * a.Nb + e;
-  int carry = 0;
-  for (int b0 = 0; b0 < a.nsb; b0 += kRound) {
-    int c[kPerLane];
-#pragma unroll
-    for (int k = 0; k < kPerLane; ++k) {
-      const int b = b0 + lane * kPerLane + k;
-      c[k] = b < a.nsb ? row[b] : 0;
-    }
-    int x = 0;
-#pragma unroll
-    for (int k = 0; k < kPerLane; ++k) x += c[k];
-    // inclusive scan over the wave
-    int incl = x;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      incl += lane >= o ? y : 0;
-    }
-    int run = carry + incl - x;  // assignments before this lane's first block
-#pragma unroll
-    for (int k = 0; k < kPerLane; k += kBlocksPerLayoutBlock) {
-      const int b = b0 + lane * kPerLane + k;
-      if (b < a.nsb) pre[(size_t)(b / kBlocksPerLayoutBlock) * a.Nb] = run;
-#pragma unroll
-      for (int j = 0; j < kBlocksPerLayoutBlock; ++j) run += c[k + j];
-    }
-    carry += __shfl(incl, kWave - 1, kWave);
+  int32_t* seg = a.segsum + ((size_t)layer * a.nseg + blk / kSegBlocks) * a.Nb;
+  for (int e = threadIdx.x; e < a.Nb; e += kThreads) {
+    out[(size_t)e * a.nsb] = (uint16_t)hist[e];
+    if (hist[e] != 0) atomicAdd(&seg[e], hist[e]);
   }
-  if (a.nsb == 0 && lane == 0) pre[0] = 0;  // empty batch: one (empty) layout block
-  if (lane == 0) a.tot[(size_t)layer * a.Nb + e] = carry;
 }
 
 // Exclusive scan of v[0..n) in LDS (n <= 2 * kThreads), deterministic:
@@ -190,11 +152,48 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
 }
 
 // total[e] = the layer's assignments of expert e (0 for e >= Nb) and, with
-// lb >= 0, pre[e] = those in tokens before layout block lb.
+// lb >= 0, pre[e] = those in tokens before layout block lb: the segments
+// wholly before it plus the blocks of its own segment before it.
 __device__ void load_totals(const LayoutArgs& a, int layer, int lb, int* total, int* pre) {
+  constexpr int kMaxSeg = 32;  // segments summed from registers; more take a loop
+  const int b_first = lb * kBlocksPerLayoutBlock;
+  const int s_own = lb >= 0 ? b_first / kSegBlocks : 0;
+  const int32_t* seg = a.segsum + (size_t)layer * a.nseg * a.Nb;
   for (int e = threadIdx.x; e < 2 * kThreads; e += kThreads) {
-    total[e] = e < a.Nb ? a.tot[(size_t)layer * a.Nb + e] : 0;
-    if (lb >= 0 && e < a.Nb) pre[e] = a.pre[((size_t)layer * a.nlb + lb) * a.Nb + e];
+    int tot = 0, p = 0;
+    if (e < a.Nb) {
+      for (int s0 = 0; s0 < a.nseg; s0 += kMaxSeg) {
+        int v[kMaxSeg];
+#pragma unroll
+        for (int k = 0; k < kMaxSeg; ++k)
+          v[k] = s0 + k < a.nseg ? seg[(size_t)(s0 + k) * a.Nb + e] : 0;
+#pragma unroll
+        for (int k = 0; k < kMaxSeg; ++k) {
+          tot += v[k];
+          p += s0 + k < s_own ? v[k] : 0;
+        }
+      }
+      if (lb >= 0) {
+        const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
+        const int b0 = s_own * kSegBlocks;
+        if ((a.nsb & 7) == 0 && b0 + kSegBlocks <= a.nsb) {
+          // the segment's block counts as two 16-byte loads, masked
+          static_assert(kSegBlocks == 16, "two uint4 per segment");
+          const uint4* r4 = reinterpret_cast<const uint4*>(row + b0);
+          const uint4 q0 = r4[0], q1 = r4[1];
+          const unsigned w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int b = b0 + 2 * k;
+            p += (b < b_first ? (int)(w[k] & 0xFFFF) : 0) + (b + 1 < b_first ? (int)(w[k] >> 16) : 0);
+          }
+        } else {
+          for (int b = b0; b < b_first; ++b) p += row[b];
+        }
+        pre[e] = p;
+      }
+    }
+    total[e] = tot;
   }
 }
 
@@ -299,10 +298,6 @@ hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s) {
     const hipError_t ec = hipGetLastError();
     if (ec != hipSuccess) return ec;
   }
-  hipLaunchKernelGGL(layout_prefix_kernel, dim3((a.Nb + kThreads / kWave - 1) / (kThreads / kWave), L),
-                     dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // a.nlb >= 1 (an empty batch still writes zero counts and offsets)
   const int extra = (a.agg_entropy != nullptr ? 1 : 0) +
                     (a.stats != nullptr || a.bias_inout != nullptr ? 1 : 0);

@@ -32,7 +32,8 @@ bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 // Workspace regions (byte offsets) for a validated descriptor.
 struct Plan {
   int Kt, Nb, nsb, nlb, ksplit;
-  size_t off_h, off_colpart, off_cnt, off_pre, off_tot, total;
+  int nseg;
+  size_t off_h, off_colpart, off_cnt, off_seg, total;
 };
 
 Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
@@ -50,10 +51,9 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   if (want_agg) o += align_up(L * p.nsb * d.N * sizeof(float) + 16);
   p.off_cnt = o;  // expert histograms per 64-token block (uint16)
   o += align_up(L * p.Nb * p.nsb * sizeof(uint16_t) + 16);
-  p.off_pre = o;  // per layout block: each expert's assignments in earlier tokens
-  o += align_up(L * p.nlb * p.Nb * sizeof(int32_t));
-  p.off_tot = o;  // per expert: all assignments
-  o += align_up(L * p.Nb * sizeof(int32_t));
+  p.nseg = (p.nsb + moer::kSegBlocks - 1) / moer::kSegBlocks;
+  p.off_seg = o;  // expert counts per segment of histogram blocks
+  o += align_up(L * p.nseg * p.Nb * sizeof(int32_t) + 16);
   p.total = o;
   return p;
 }
@@ -182,6 +182,14 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
       return fail(MOER_EHIP, "%s: %s", #expr, hipGetErrorString(he));           \
   } while (0)
 
+  // segment counters start at zero: cleared by the pipelined gate GEMM when
+  // it runs, else by a fill kernel
+  int32_t* segsum = reinterpret_cast<int32_t*>(ws + p.off_seg);
+  const int n_seg = L * p.nseg * p.Nb;
+  const bool gemm_clears = hidden && d.dtype == MOER_BF16 &&
+                           moer::gate_gemm_clears(L, d.T, d.d, d.N, p.ksplit);
+  if (!gemm_clears) MOER_CHECK(moer::launch_zero_ints(segsum, n_seg, s));
+
   // a1: gate affinities
   const float* h = nullptr;
   if (hidden && d.T > 0) {
@@ -189,7 +197,8 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     if (io->ev_gemm_begin) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_begin), s));
     if (d.dtype == MOER_BF16)
       MOER_CHECK(moer::launch_gate_gemm_bf16(io->x, io->w_gate, hbuf, L, d.T, d.d, d.N, p.ksplit,
-                                             s));
+                                             gemm_clears ? segsum : nullptr,
+                                             gemm_clears ? n_seg : 0, s));
     else
       MOER_CHECK(moer::launch_gate_gemm_f32(static_cast<const float*>(io->x),
                                             static_cast<const float*>(io->w_gate), hbuf, L, d.T,
@@ -223,6 +232,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     a.apply_score = hidden ? 1 : 0;
     if (path == 1) {
       a.cnt = cnt;
+      a.segsum = segsum;
       MOER_CHECK(moer::launch_route_rows(a, L, s));
     } else {
       a.cnt = nullptr;
@@ -234,8 +244,8 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   moer::LayoutArgs la{};
   la.idx = indices ? io->idx_in : io->topk_idx;
   la.cnt = cnt;
-  la.pre = reinterpret_cast<int32_t*>(ws + p.off_pre);
-  la.tot = reinterpret_cast<int32_t*>(ws + p.off_tot);
+  la.segsum = segsum;
+  la.nseg = p.nseg;
   la.colpart = colpart;
   la.agg_entropy = want_agg ? io->agg_entropy : nullptr;
   la.counts = io->counts;

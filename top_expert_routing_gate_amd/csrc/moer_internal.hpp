@@ -15,6 +15,7 @@ constexpr int kMaxSlots = 16;       // Kt
 constexpr int kMaxBuckets = kMaxExperts + kMaxSlots;
 constexpr int kRowTokens = 64;      // tokens per selection workgroup (= histogram block)
 constexpr int kLayoutTokens = 128;  // tokens per scatter workgroup (2 histogram blocks)
+constexpr int kSegBlocks = 16;       // histogram blocks per segment of the running totals
 
 // Everything a score/select launch needs (passed by value).
 struct ScoreArgs {
@@ -27,14 +28,14 @@ struct ScoreArgs {
   float* tok_entropy;     // [L][T] or nullptr
   float* colpart;         // [L][nsb][N] sums of q per 64-token block, or nullptr
   uint16_t* cnt;          // [L][Nb][nsb] expert counts per 64-token block, or nullptr
+  int32_t* segsum;        // [L][nseg][Nb] += the block counts (zero beforehand), or nullptr
   int T, N, K, G, Gk, n_shared, score_fn, apply_score, nsplit;
 };
 
 struct LayoutArgs {
   const int32_t* idx;     // [L][T][Kt]
   uint16_t* cnt;          // [L][Nb][nsb] expert counts per 64-token block
-  int32_t* pre;           // [L][nlb][Nb] assignments of expert e before layout block lb
-  int32_t* tot;           // [L][Nb] assignments of expert e
+  int32_t* segsum;        // [L][nseg][Nb] expert counts per segment of kSegBlocks blocks
   const float* colpart;   // [L][nsb][N] or nullptr
   float* agg_entropy;     // [L] or nullptr
   int32_t* counts;        // [L][Nb]
@@ -44,14 +45,20 @@ struct LayoutArgs {
   moer_load_stats_t* stats;  // [L] or nullptr
   float* bias_inout;      // [L][N] updated in place, or nullptr
   float bias_step;
-  int T, Kt, Nb, N, nlb, nsb, fill_invalid, need_count;
+  int T, Kt, Nb, N, nlb, nsb, nseg, fill_invalid, need_count;
 };
 
 // Depth ranges the bf16 gate GEMM splits d into (its partial sums are
 // part[0..ksplit) [L][T][N]); 1 for fp32 inputs.
 int gate_gemm_ksplit(int dtype_bf16, int L, int T, int d, int N);
+// zero[0..n_zero) is cleared by the launch before any of its tiles finish
+// (for counters the next kernels of the call accumulate into).
 hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int L, int T, int d,
-                                 int N, int ksplit, hipStream_t s);
+                                 int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s);
+// Whether launch_gate_gemm_bf16 takes the pipelined kernel (which clears
+// `zero` itself) for this shape; otherwise clear it with launch_zero_ints.
+bool gate_gemm_clears(int L, int T, int d, int N, int ksplit);
+hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s);
 hipError_t launch_gate_gemm_f32(const float* x, const float* w, float* h, int L, int T, int d,
                                 int N, hipStream_t s);
 hipError_t launch_score_topk(const ScoreArgs& a, int L, hipStream_t s);

@@ -93,6 +93,13 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
     uint16_t* out = a.cnt + (size_t)layer * Nb * gridDim.x + blockIdx.x;
     for (int e = threadIdx.x; e < Nb; e += kThreads) out[(size_t)e * gridDim.x] = (uint16_t)hist[e];
   }
+  if (a.segsum != nullptr) {
+    // running totals per segment of blocks (integer adds: any order, same sum)
+    const int nseg = (gridDim.x + kSegBlocks - 1) / kSegBlocks;
+    int32_t* seg = a.segsum + ((size_t)layer * nseg + blockIdx.x / kSegBlocks) * Nb;
+    for (int e = threadIdx.x; e < Nb; e += kThreads)
+      if (hist[e] != 0) atomicAdd(&seg[e], hist[e]);
+  }
   if (a.colpart != nullptr) {
     for (int e = threadIdx.x; e < N; e += kThreads) {
       const int idx = (e % EPL) * kRowLanes + e / EPL;
