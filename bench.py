@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="dsv3_group")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--overlap", action="store_true",
+                   help="alternate two streams so step i+1's gate GEMM overlaps step i's "
+                        "selection and layout (measured slower: the GEMM needs every CU)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration)")
     p.add_argument("--summarize-trace", metavar="DIR",
@@ -113,11 +116,24 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.pairs = []
+        self.extra = []
         for _ in range(n):
             a, b = ctypes.c_void_p(), ctypes.c_void_p()
             assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
             assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
             self.pairs.append((a, b))
+
+    def plain(self):
+        """An event without timing (cheap), for stream-to-stream ordering."""
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreateWithFlags(ctypes.byref(e), 0x2) == 0  # hipEventDisableTiming
+        self.extra.append(e)
+        return e
+
+    def record(self, e, stream):
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        assert self.hip.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream)) == 0
 
     def elapsed_ms(self, i):
         ms = ctypes.c_float()
@@ -129,6 +145,8 @@ class HipEvents:
         for a, b in self.pairs:
             self.hip.hipEventDestroy(a)
             self.hip.hipEventDestroy(b)
+        for e in self.extra:
+            self.hip.hipEventDestroy(e)
 
 
 def gemm_source_hash():
@@ -209,21 +227,40 @@ def main():
                 counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
                 perm=torch.empty(L, T * Kt, **i32), inv_perm=torch.empty(L, T * Kt, **i32))
     stats = torch.empty(L, 64, dtype=torch.uint8, device=dev)
-    ws = torch.empty(moer.moer_route_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     ev = HipEvents(args.steps)
 
-    # the router runs on a stream of its own (default priority), as a serving
-    # or training loop would; the legacy default stream adds per-launch waits
-    rs = torch.cuda.Stream()
+    # The router runs on a stream of its own (default priority), as a serving
+    # or training loop would (the legacy default stream adds per-launch
+    # waits). With --overlap, consecutive steps alternate between two such
+    # streams, each with its own workspace: step i+1's gate GEMM reads only x
+    # and W_g, so it may overlap step i's selection and layout, while step
+    # i+1's selection waits for an event recorded after step i (so it sees
+    # step i's bias update; the results are the one-stream sequence).
+    nstream = 2 if args.overlap else 1
+    streams = [torch.cuda.Stream() for _ in range(nstream)]
+    wss = [torch.empty(moer.moer_route_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+           for _ in range(nstream)]
+    done = [ev.plain() for _ in range(nstream)]
     torch.cuda.synchronize()
-    torch.cuda.set_stream(rs)
-    # arguments marshalled once per x batch; the loop only enqueues
-    calls = [moer.PreparedRoute(desc, workspace=ws, x=xb, w_gate=Wd, bias=bias,
-                                logit_offset=offd, load_stats=stats, bias_update=bias,
-                                bias_update_u=1e-3, **outs) for xb in xs]
+    # arguments marshalled once per (stream, x batch); the loop only enqueues
+    calls = []
+    for k in range(nstream):
+        with torch.cuda.stream(streams[k]):
+            calls.append([moer.PreparedRoute(desc, workspace=wss[k], x=xb, w_gate=Wd, bias=bias,
+                                             logit_offset=offd, load_stats=stats,
+                                             bias_update=bias, bias_update_u=1e-3, **outs)
+                          for xb in xs])
 
     def step(i, events=None):
-        calls[i % len(calls)](*(events or (None, None)))
+        k = i % nstream
+        wait = done[(i - 1) % nstream] if (nstream > 1 and i > 0) else None
+        calls[k][i % len(xs)](*(events or (None, None)), ev_select_wait=wait)
+        ev.record(done[k], streams[k])
+
+    def sync_streams():
+        # every stream has reached the end of what was enqueued so far
+        for st in streams:
+            st.synchronize()
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -233,30 +270,42 @@ def main():
         del a, bcopy
     for i in range(args.warmup):
         step(i)
+    sync_streams()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps",
           file=sys.stderr, flush=True)
-    # timed region 1 (value): K uninstrumented steps between two barriers
+    # timed region 1 (value): K uninstrumented steps between two barriers; the
+    # start event is on the first step's stream (the other stream's first
+    # work waits for step 0 through the chain of events anyway), the end event
+    # after every stream has finished
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    i0 = args.warmup
     t_wall = time.perf_counter()
-    e0.record()
+    e0.record(streams[i0 % nstream])
+    for st in streams:
+        if st is not streams[i0 % nstream]:
+            st.wait_event(e0)
     for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
+        step(i0 + i)
+    last = streams[(i0 + args.steps - 1) % nstream]
+    for st in streams:
+        if st is not last:
+            last.wait_stream(st)
+    e1.record(last)
+    sync_streams()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = e0.elapsed_time(e1) / args.steps
     # timed region 2 (roofline): the same K steps with hipEvents around every
     # gate GEMM launch on the route's stream (events cost a few us per step,
     # so they stay out of region 1)
-    torch.cuda.synchronize()
     for i in range(args.steps):
         step(args.warmup + args.steps + i, ev.pairs[i])
+    sync_streams()
     torch.cuda.synchronize()
     gemm_ms = sum(ev.elapsed_ms(i) for i in range(args.steps)) / args.steps
     ev.close()
-    torch.cuda.set_stream(torch.cuda.default_stream())
     st = moer.decode_load_stats(stats.cpu())[0]
     print(f"[bench] {ms_step * 1e3:.1f} us/step (wall {t_wall / args.steps * 1e6:.1f} us), "
           f"gate GEMM {gemm_ms * 1e3:.1f} us (event-timed pass); last imbalance "
@@ -282,7 +331,8 @@ def main():
         "config": {"workload": wl.name, "tokens": T, "hidden": wl.d, "experts": N,
                    "groups": wl.n_groups, "groups_kept": wl.topk_groups, "top_k": wl.K,
                    "score": "sigmoid" if wl.score_fn == 1 else "softmax",
-                   "step": "route+load_stats+bias_update (fused)", "x_batches_rotated": len(xs)},
+                   "step": "route+load_stats+bias_update (fused)", "x_batches_rotated": len(xs),
+                   "streams": nstream},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
     }

@@ -144,6 +144,13 @@ typedef struct {
                                 be the same buffer): the auxiliary-loss-free
                                 balancing step of one training iteration */
   float bias_update_u;       /* step u >= 0 for bias_update */
+  void* ev_select_wait;      /* opt hipEvent_t: the selection (and everything
+                                after it) waits for this event, the gate GEMM
+                                does not. Lets a loop overlap the next batch's
+                                GEMM with this batch's selection and layout:
+                                call i+1 on a second stream, with its own
+                                workspace, waiting for an event recorded after
+                                call i (whose bias update it then sees) */
 } moer_route_io;
 
 

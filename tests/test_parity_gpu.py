@@ -338,6 +338,56 @@ def test_fused_stats_and_bias_update():
             assert (_np(b_gpu[l]) == b_ref[l]).all(), (step, l)
 
 
+def test_overlapped_steps_match_one_stream():
+    """Consecutive training steps with the bias update, run on one stream and
+    then alternating two streams (own workspaces) where step i+1's gate GEMM
+    overlaps step i and its selection waits for an event after step i
+    (ev_select_wait): every step's counts, ids and updated bias must be
+    bitwise the same."""
+    import ctypes
+    wl = workloads.scaled(WL["collapse_balance"], T=2048, d=1024)
+    W, b0, off, gen = workloads.make_router(wl)
+    xs = [workloads.make_hidden(wl, seed=500 + i).to(DEV) for i in range(6)]
+    desc = moer.make_desc(T=wl.T, d=wl.d, N=wl.N, K=wl.K, n_groups=8, topk_groups=4)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def run(nstream):
+        streams = [torch.cuda.Stream() for _ in range(nstream)]
+        wss = [torch.empty(moer.moer_route_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+               for _ in range(nstream)]
+        done = []
+        for _ in range(nstream):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreateWithFlags(ctypes.byref(e), 0x2) == 0
+            done.append(e)
+        bias = b0.clone().to(DEV)
+        outs = _outputs(1, wl.T, wl.N, wl.Kt, wl.Nb)
+        snaps = []
+        torch.cuda.synchronize()
+        for i, x in enumerate(xs):
+            k = i % nstream
+            with torch.cuda.stream(streams[k]):
+                wait = done[(i - 1) % nstream] if (nstream > 1 and i > 0) else None
+                moer.moer_route(desc, workspace=wss[k], x=x, w_gate=W.to(DEV), bias=bias,
+                                logit_offset=off.to(DEV), bias_update=bias, bias_update_u=1e-3,
+                                ev_select_wait=wait, **outs)
+                snaps.append((outs["counts"].clone(), outs["topk_idx"].clone(), bias.clone()))
+                assert hip.hipEventRecord(done[k], ctypes.c_void_p(streams[k].cuda_stream)) == 0
+        torch.cuda.synchronize()
+        for e in done:
+            hip.hipEventDestroy(e)
+        return [[t.cpu() for t in sn] for sn in snaps]
+
+    one, two = run(1), run(2)
+    for i, (a, b) in enumerate(zip(one, two)):
+        for name, u, v in zip(("counts", "topk_idx", "bias"), a, b):
+            assert torch.equal(u, v), f"step {i}: {name}"
+    assert not torch.equal(one[0][2], one[-1][2])  # the bias did move
+
+
 def test_collapse_balancing_lockstep():
     """Celebrity experts (+3.0 logit offset) and 100 rounds of route -> count
     -> sign update, GPU and oracle in lockstep on identical fp32 scores: the

@@ -34,7 +34,7 @@ class MoerRouteIO(ctypes.Structure):
                 ("x", "w_gate", "scores", "idx_in", "bias", "logit_offset", "h_out", "topk_w",
                  "tok_entropy", "agg_entropy", "topk_idx", "counts", "offsets", "perm",
                  "inv_perm", "ev_gemm_begin", "ev_gemm_end", "load_stats", "bias_update")] + \
-        [("bias_update_u", ctypes.c_float)]
+        [("bias_update_u", ctypes.c_float), ("ev_select_wait", ctypes.c_void_p)]
 
 
 class MoerLoadStats(ctypes.Structure):
@@ -125,7 +125,7 @@ def _route_io(desc, *, x=None, w_gate=None, scores=None, idx_in=None, bias=None,
               logit_offset=None, h_out=None, topk_w=None, tok_entropy=None, agg_entropy=None,
               topk_idx=None, counts=None, offsets=None, perm=None, inv_perm=None,
               ev_gemm_begin=None, ev_gemm_end=None, load_stats=None, bias_update=None,
-              bias_update_u=0.0):
+              bias_update_u=0.0, ev_select_wait=None):
     for name, t, dt in (("x", x, None), ("w_gate", w_gate, None), ("scores", scores, torch.float32),
                         ("idx_in", idx_in, torch.int32), ("bias", bias, torch.float32),
                         ("logit_offset", logit_offset, torch.float32),
@@ -148,7 +148,7 @@ def _route_io(desc, *, x=None, w_gate=None, scores=None, idx_in=None, bias=None,
                        _ptr(logit_offset), _ptr(h_out), _ptr(topk_w), _ptr(tok_entropy),
                        _ptr(agg_entropy), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
                        _ptr(inv_perm), ev_gemm_begin, ev_gemm_end, _ptr(load_stats),
-                       _ptr(bias_update), float(bias_update_u))
+                       _ptr(bias_update), float(bias_update_u), ev_select_wait)
 
 
 def moer_route(desc, *, workspace, stream=None, **buffers):
@@ -174,9 +174,10 @@ class PreparedRoute:
         self._args = (ctypes.byref(self.desc), ctypes.byref(self.io), _ptr(workspace), nbytes,
                       _stream(stream))
 
-    def __call__(self, ev_gemm_begin=None, ev_gemm_end=None):
+    def __call__(self, ev_gemm_begin=None, ev_gemm_end=None, ev_select_wait=None):
         self.io.ev_gemm_begin = ev_gemm_begin
         self.io.ev_gemm_end = ev_gemm_end
+        self.io.ev_select_wait = ev_select_wait
         st = _lib.moer_route(*self._args)
         if st != MOER_OK:
             _check(st)

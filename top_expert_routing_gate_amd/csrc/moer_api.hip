@@ -206,6 +206,8 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     if (io->ev_gemm_end) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_end), s));
     h = hbuf;
   }
+  if (io->ev_select_wait != nullptr)
+    MOER_CHECK(hipStreamWaitEvent(s, static_cast<hipEvent_t>(io->ev_select_wait), 0));
 
   // a2-a6: scores, selection, weights, entropy, per-block expert histograms
   float* colpart = want_agg ? reinterpret_cast<float*>(ws + p.off_colpart) : nullptr;

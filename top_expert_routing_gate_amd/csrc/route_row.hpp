@@ -78,6 +78,12 @@ __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp_f<kHalfMirror>(v));
   return fmaxf(v, dpp_f<kMirror>(v));
 }
+__device__ __forceinline__ float row_min(float v) {
+  v = fminf(v, dpp_f<kXor1>(v));
+  v = fminf(v, dpp_f<kXor2>(v));
+  v = fminf(v, dpp_f<kHalfMirror>(v));
+  return fminf(v, dpp_f<kMirror>(v));
+}
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp_f<kXor1>(v);
   v += dpp_f<kXor2>(v);
@@ -117,8 +123,11 @@ __device__ __forceinline__ unsigned long long row_max_u64(unsigned long long v) 
 }
 
 // Orderable encoding: larger word <=> larger key, then smaller expert id.
+// -0 and +0 are the same key: -0 is mapped to +0 here, where the order bits
+// are formed (plain float compares already treat them as equal).
 __device__ __forceinline__ unsigned long long pack_key(float key, int e) {
-  const unsigned f = __builtin_bit_cast(unsigned, key);
+  unsigned f = __builtin_bit_cast(unsigned, key);
+  f = f == 0x80000000u ? 0u : f;
   const unsigned u = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
   return ((unsigned long long)u << 32) | (unsigned)(0xFFFF - e);
 }
@@ -141,13 +150,23 @@ __device__ __forceinline__ float score_of(float v, float m, float inv_z) {
   return exp2_hw((v - m) * kLog2e) * inv_z;
 }
 
-// LDS scratch of one token row.
+// LDS scratch of one token row. A candidate is one 64-bit word written as two
+// 32-bit halves: low = 0xFFFF - expert id, high = the key's order bits, so
+// that one unsigned 64-bit compare orders (key desc, id asc).
 struct RowLds {
   unsigned long long* cand;  // [kCandStride]
   float* cand_s;             // [kCandStride] score of each candidate
   int* slot_id;              // [kMaxSlots]
   float* slot_s;             // [kMaxSlots]
 };
+// Order bits of a key: for keys all > 0 the raw bits already order them;
+// otherwise flip negatives (and set the sign of non-negatives).
+__device__ __forceinline__ unsigned order_bits(float key, bool all_positive) {
+  unsigned f = __builtin_bit_cast(unsigned, key);
+  if (all_positive) return f;
+  f = f == 0x80000000u ? 0u : f;  // -0 is +0
+  return (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+}
 
 // The lane's per-expert constants of a layer, loaded once (and early, so
 // their latency hides under the affinity loads): selection bias and logit
@@ -225,48 +244,58 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     for (int j = 0; j < EPL; ++j) z += (full || e0 + j < N) ? exp2_hw((v[j] - m) * kLog2e) : 0.f;
     inv_z = rcp_hw(row_sum(z));
   }
-  float s[EPL], key[EPL];
-  if (full) {
+  // scores, keys, and each expert's entropy term s*log2(s) (from quantities
+  // the score already has where possible)
+  float s[EPL], key[EPL], ent[EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      s[j] = score_of<MODE>(v[j], m, inv_z);
-      key[j] = (s[j] + lc.bias[j]) + 0.f;
+  for (int j = 0; j < EPL; ++j) {
+    const bool in = full || e0 + j < N;
+    if (MODE == kSigmoid) {
+      const float tj = 1.f + exp2_hw(-v[j] * kLog2e);  // s = 1/t, log2 s = -log2 t
+      s[j] = in ? rcp_hw(tj) : 0.f;
+      ent[j] = -s[j] * log2_hw(fminf(tj, __FLT_MAX__));  // s = 0 when t overflows
+    } else if (MODE == kSoftmax) {
+      const float aj = (v[j] - m) * kLog2e;  // log2 p = aj + log2(inv_z)
+      s[j] = in ? exp2_hw(aj) * inv_z : 0.f;
+      ent[j] = s[j] * aj;  // the log2(inv_z) * sum(p) part is added after the sum
+    } else {
+      s[j] = in ? v[j] : 0.f;
+      ent[j] = s[j] > 0.f ? s[j] * log2_hw(s[j]) : 0.f;
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = e0 + j;
-      s[j] = e < N ? score_of<MODE>(v[j], m, inv_z) : 0.f;
-      key[j] = e < N ? (s[j] + lc.bias[j]) + 0.f : NEG_INF;
-    }
+    key[j] = in ? s[j] + lc.bias[j] : NEG_INF;
   }
 
-  // 6. entropy of q = s / sum s
+  // 6. entropy of q = s / sum s: H = log2(S) - (sum s log2 s) / S
   float ssum = 0.f, slog = 0.f;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     ssum += s[j];
-    slog += s[j] > 0.f ? s[j] * log2_hw(s[j]) : 0.f;
+    slog += ent[j];
   }
   ssum = row_sum(ssum);
   slog = row_sum(slog);
+  if (MODE == kSoftmax) slog += log2_hw(inv_z) * ssum;
   if (live && rl == 0 && a.tok_entropy != nullptr)
     a.tok_entropy[(size_t)layer * T + t] = ssum > 0.f ? log2f(ssum) - slog / ssum : 0.f;
   const float inv_s = (live && ssum > 0.f) ? 1.f / ssum : 0.f;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) q[j] = s[j] * inv_s;
 
+  // the lane's two largest keys (used by both the group stage and the bound)
+  float lt1 = key[0], lt2 = NEG_INF;
+#pragma unroll
+  for (int j = 1; j < EPL; ++j) {
+    lt2 = fmaxf(lt2, fminf(lt1, key[j]));
+    lt1 = fmaxf(lt1, key[j]);
+  }
+
   // 3. group-limited eligibility
   bool eligible = true;
+  float group_m2 = NEG_INF;  // second largest key of this lane's group
   if (GROUPED) {
     const int lpg = LPG > 0 ? LPG : (N / a.G) / EPL;  // lanes per group (power of two, <= 16)
     const int g = rl / lpg;
-    float m1 = key[0], m2 = NEG_INF;
-#pragma unroll
-    for (int j = 1; j < EPL; ++j) {
-      m2 = fmaxf(m2, fminf(m1, key[j]));
-      m1 = fmaxf(m1, key[j]);
-    }
+    float m1 = lt1, m2 = lt2;
     // merge the group's lanes (lanes of a group are aligned, lpg a power of 2)
     auto merge = [&](float b1, float b2) {
       const float n2 = fmaxf(fminf(m1, b1), fmaxf(m2, b2));
@@ -292,37 +321,41 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     MOER_ROT(15)
 #undef MOER_ROT
     eligible = g < a.G && rank < a.Gk;
+    group_m2 = m2;
   }
 
-  // lo: K-th largest of the eligible lanes' two largest keys (keys of up to 32
-  // distinct eligible experts, so lo is at most the K-th largest eligible key)
-  float l1 = NEG_INF, l2 = NEG_INF;
-  if (eligible) {
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      l2 = fmaxf(l2, fminf(l1, key[j]));
-      l1 = fmaxf(l1, key[j]);
-    }
-  }
-  int c1 = 1 + (l2 >= l1 ? 1 : 0), c2 = 2;  // values >= l1 / >= l2, own pair included
+  // lo: a key that at least K distinct eligible experts reach, so every chosen
+  // expert has key >= lo.
+  float lo;
+  if (GROUPED && 2 * a.Gk == K) {
+    // the kept groups' two largest keys are exactly K such experts: lo is
+    // the smallest of them (the groups' second keys)
+    lo = row_min(eligible ? group_m2 : __builtin_inff());
+  } else {
+    // the K-th largest of the eligible lanes' two largest keys (up to 32)
+    const float l1 = eligible ? lt1 : NEG_INF, l2 = eligible ? lt2 : NEG_INF;
+    int c1 = 1 + (l2 >= l1 ? 1 : 0), c2 = 2;  // values >= l1 / >= l2, own pair included
 #define MOER_CGE(n)                                          \
-  {                                                          \
-    const float o1 = dpp_f<0x120 + (n)>(l1);                 \
-    const float o2 = dpp_f<0x120 + (n)>(l2);                 \
-    c1 += (o1 >= l1 ? 1 : 0) + (o2 >= l1 ? 1 : 0);           \
-    c2 += (o1 >= l2 ? 1 : 0) + (o2 >= l2 ? 1 : 0);           \
-  }
-  MOER_CGE(1) MOER_CGE(2) MOER_CGE(3) MOER_CGE(4) MOER_CGE(5) MOER_CGE(6) MOER_CGE(7)
-  MOER_CGE(8) MOER_CGE(9) MOER_CGE(10) MOER_CGE(11) MOER_CGE(12) MOER_CGE(13) MOER_CGE(14)
-  MOER_CGE(15)
+    {                                                        \
+      const float o1 = dpp_f<0x120 + (n)>(l1);               \
+      const float o2 = dpp_f<0x120 + (n)>(l2);               \
+      c1 += (o1 >= l1 ? 1 : 0) + (o2 >= l1 ? 1 : 0);         \
+      c2 += (o1 >= l2 ? 1 : 0) + (o2 >= l2 ? 1 : 0);         \
+    }
+    MOER_CGE(1) MOER_CGE(2) MOER_CGE(3) MOER_CGE(4) MOER_CGE(5) MOER_CGE(6) MOER_CGE(7)
+    MOER_CGE(8) MOER_CGE(9) MOER_CGE(10) MOER_CGE(11) MOER_CGE(12) MOER_CGE(13) MOER_CGE(14)
+    MOER_CGE(15)
 #undef MOER_CGE
-  const float lo = row_max(fmaxf(c1 >= K ? l1 : NEG_INF, c2 >= K ? l2 : NEG_INF));
+    lo = row_max(fmaxf(c1 >= K ? l1 : NEG_INF, c2 >= K ? l2 : NEG_INF));
+  }
 
-  // candidates: eligible keys >= lo
+  // candidates: eligible keys >= lo (lo is finite: at least K finite keys
+  // reach it; the clamp keeps absent experts' -inf keys out regardless)
+  const float lo_f = fmaxf(lo, -__FLT_MAX__);
   unsigned bits = 0;
   if (eligible) {
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) bits |= (key[j] >= lo && key[j] > NEG_INF) ? 1u << j : 0u;
+    for (int j = 0; j < EPL; ++j) bits |= key[j] >= lo_f ? 1u << j : 0u;
   }
   const int mine = __builtin_popcount(bits);
   const int incl = row_scan(mine);
@@ -331,14 +364,28 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   // wavefront's LDS operations complete in order: no barrier is needed.
   if (count <= kCandCap) {
     // 4. compact, then slot = number of candidates that beat this one
+    const bool all_positive = lo > 0.f;  // every candidate key >= lo
+    unsigned* cw = reinterpret_cast<unsigned*>(rs.cand);
     int pos = incl - mine;
+    if (all_positive) {
 #pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (bits & (1u << j)) {
-        rs.cand[pos] = pack_key(key[j], e0 + j);
-        rs.cand_s[pos] = s[j];
-        ++pos;
-      }
+      for (int j = 0; j < EPL; ++j)
+        if (bits & (1u << j)) {
+          cw[2 * pos] = (unsigned)(0xFFFF - (e0 + j));
+          cw[2 * pos + 1] = __builtin_bit_cast(unsigned, key[j]);
+          rs.cand_s[pos] = s[j];
+          ++pos;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (bits & (1u << j)) {
+          cw[2 * pos] = (unsigned)(0xFFFF - (e0 + j));
+          cw[2 * pos + 1] = order_bits(key[j], false);
+          rs.cand_s[pos] = s[j];
+          ++pos;
+        }
+    }
     for (int c = rl; c < count; c += kRowLanes) {
       const unsigned long long my = rs.cand[c];
       int r = 0;

@@ -12,7 +12,6 @@ namespace moer {
 namespace {
 
 constexpr int kThreads = kRowTokens * kRowLanes;  // 1024: one row per token
-constexpr int kWaves = kThreads / kWave;
 
 template <int EPL>
 __device__ __forceinline__ void load_row(const ScoreArgs& a, size_t row_off, size_t split_stride,
@@ -55,7 +54,9 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   __shared__ int slot_id[kRowTokens][kMaxSlots];
   __shared__ float slot_s[kRowTokens][kMaxSlots];
   __shared__ int hist[kMaxBuckets];
-  __shared__ float colw[kWaves][kRowLanes * EPL];
+  __shared__ __attribute__((aligned(16))) float colq[kRowTokens][kRowLanes * EPL];
+  constexpr int kParts = kThreads / (kRowLanes * EPL) < 4 ? kThreads / (kRowLanes * EPL) : 4;
+  __shared__ float colp[kParts > 0 ? kParts : 1][kRowLanes * EPL];
 
   const int N = a.N, T = a.T;
   const int Nb = N + a.n_shared;
@@ -63,7 +64,6 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int rl = lane & 15;
   const int row = threadIdx.x >> 4;  // row within the workgroup = token slot
-  const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * kRowTokens + row;
   const bool live = t < T;
 
@@ -79,14 +79,12 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   __syncthreads();  // histogram cleared
 
   const RowLds rs{cand[row], cand_s[row], slot_id[row], slot_s[row]};
-  float q[EPL], col[EPL];
+  float q[EPL];
   route_row<EPL, GROUPED, MODE, LPG>(a, layer, t, live, v, lc, rs, hist, q);
-  wave_column_sums<EPL>(q, col);
   if (a.colpart != nullptr) {
-    // every lane stores (the 4 rows of a wavefront hold identical sums), so
-    // the lane exchanges above are never moved under a lane-dependent branch
+    // this token's q (zero for tokens past T) for the block's column sums
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) colw[wave][j * kRowLanes + rl] = col[j];
+    for (int j = 0; j < EPL; ++j) colq[row][rl * EPL + j] = q[j];
   }
   __syncthreads();
   if (a.cnt != nullptr) {
@@ -101,11 +99,22 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
       if (hist[e] != 0) atomicAdd(&seg[e], hist[e]);
   }
   if (a.colpart != nullptr) {
+    // column sums of q over the 64 rows, in a fixed order: kParts partial
+    // sums over consecutive rows, then the partials in order
+    constexpr int kW = kRowLanes * EPL;
+    constexpr int kRowsPerPart = kRowTokens / kParts;
+    if (threadIdx.x < kParts * kW) {
+      const int e = threadIdx.x % kW, part = threadIdx.x / kW;
+      float acc = colq[part * kRowsPerPart][e];
+#pragma unroll 8
+      for (int r = 1; r < kRowsPerPart; ++r) acc += colq[part * kRowsPerPart + r][e];
+      colp[part][e] = acc;
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < N; e += kThreads) {
-      const int idx = (e % EPL) * kRowLanes + e / EPL;
-      float acc = colw[0][idx];
+      float acc = colp[0][e];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) acc += colw[w][idx];
+      for (int p = 1; p < kParts; ++p) acc += colp[p][e];
       a.colpart[((size_t)layer * gridDim.x + blockIdx.x) * N + e] = acc;
     }
   }
