@@ -13,6 +13,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moero.c")
 _LIB = os.path.join(_HERE, "libmoero.so")
+# a prebuilt oracle library to load instead (the pin tests' mutation check
+# points this at deliberately broken builds)
+_LIB_OVERRIDE = os.environ.get("MOERO_LIB")
 
 SOFTMAX, SIGMOID = 0, 1
 
@@ -43,9 +46,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build_oracle()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build_oracle()
+            lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32 = ctypes.c_int32
         lib.moero_affinities.argtypes = [P, P, P, i32, i32, i32, P]
