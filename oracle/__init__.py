@@ -12,6 +12,8 @@ from .api import (  # noqa: F401
     agg_entropy,
     bias_update,
     build_oracle,
+    combine,
+    dispatch,
     layout,
     load_stats,
     num_threads,

@@ -63,6 +63,8 @@ def _load():
         lib.moero_layout.argtypes = [P, i32, i32, i32, P, P, P, P]
         lib.moero_load_stats.argtypes = [P, i32, ctypes.POINTER(_Stats)]
         lib.moero_bias_update.argtypes = [P, P, i32, ctypes.c_float]
+        lib.moero_dispatch.argtypes = [P, ctypes.c_int64, i32, i32, P, P]
+        lib.moero_combine.argtypes = [P, P, P, i32, i32, i32, P]
         lib.moero_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -133,6 +135,38 @@ def layout(idx, Nb):
     inv = np.empty(T * Kt, np.int32)
     _load().moero_layout(_p(idx), T, Kt, Nb, _p(counts), _p(offsets), _p(perm), _p(inv))
     return counts, offsets, perm, inv
+
+
+def dispatch(x, perm, Kt, out=None):
+    """Rows of x [T, d] (any dtype, copied as bytes) gathered into layout
+    order: returns [T*Kt, d]; rows whose perm entry is -1 keep ``out``'s
+    contents (zeros when ``out`` is None)."""
+    x = np.ascontiguousarray(x)
+    perm = _c(perm, np.int32)
+    T = x.shape[0]
+    assert perm.shape == (T * Kt,)
+    if out is None:
+        out = np.zeros((T * Kt,) + x.shape[1:], x.dtype)
+    else:
+        out = np.array(out, dtype=x.dtype, copy=True, order="C")
+        assert out.shape == (T * Kt,) + x.shape[1:]
+    row_bytes = x.dtype.itemsize * int(np.prod(x.shape[1:], dtype=np.int64))
+    _load().moero_dispatch(_p(x), row_bytes, T, Kt, _p(perm), _p(out))
+    return out
+
+
+def combine(out_rows, w, perm):
+    """y [T, d] fp64 = per token, the w-weighted sum of its slots' rows of
+    out_rows [T*Kt, d] (given as exact values; converted to fp64 here)."""
+    w = _c(w, np.float32)
+    T, Kt = w.shape
+    out_rows = _c(out_rows, np.float64)
+    d = out_rows.shape[1]
+    assert out_rows.shape == (T * Kt, d)
+    perm = _c(perm, np.int32)
+    y = np.empty((T, d), np.float64)
+    _load().moero_combine(_p(out_rows), _p(w), _p(perm), T, Kt, d, _p(y))
+    return y
 
 
 def load_stats(counts):

@@ -14,7 +14,9 @@
  * Pinning (what checks this file against something other than itself) is
  * done by the CPU tests: the [P4] worked example, entropy closed forms,
  * brute-force enumeration of group-limited top-k, library special cases
- * (fp64 matmul/softmax/sigmoid/stable sort) and the bias closed form.
+ * (fp64 matmul/softmax/sigmoid/stable sort), the bias closed form, and for
+ * dispatch/combine the bucket-membership properties and the closed form of a
+ * combine over experts that only scale their rows.
  */
 #include "moero.h"
 
@@ -259,6 +261,34 @@ void moero_layout(const int32_t* idx, int32_t T, int32_t Kt, int32_t Nb,
         ++pos;
       }
     }
+  }
+}
+
+/* [P2] DeepEP section: dispatch. Walk the layout in its own (expert-major)
+ * order and fetch each position's token row. */
+void moero_dispatch(const void* x, int64_t row_bytes, int32_t T, int32_t Kt,
+                    const int32_t* perm, void* x_out) {
+  const int64_t A = (int64_t)T * Kt;
+  for (int64_t pos = 0; pos < A; ++pos) {
+    if (perm[pos] < 0) continue;
+    const int64_t t = perm[pos] / Kt;
+    memcpy((char*)x_out + pos * row_bytes, (const char*)x + t * row_bytes, (size_t)row_bytes);
+  }
+}
+
+/* [P2] token routing and DeepEP section: weighted combine. Each layout
+ * position adds its expert-output row, times the weight of the slot it
+ * serves, to that slot's token. */
+void moero_combine(const double* out, const float* w, const int32_t* perm,
+                   int32_t T, int32_t Kt, int32_t d, double* y) {
+  const int64_t A = (int64_t)T * Kt;
+  for (int64_t i = 0; i < (int64_t)T * d; ++i) y[i] = 0.0;
+  for (int64_t pos = 0; pos < A; ++pos) {
+    const int32_t slot = perm[pos];
+    if (slot < 0) continue;
+    const int64_t t = slot / Kt;
+    const double wk = (double)w[slot];
+    for (int32_t j = 0; j < d; ++j) y[t * d + j] += wk * out[pos * d + j];
   }
 }
 

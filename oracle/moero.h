@@ -98,6 +98,25 @@ void moero_load_stats(const int32_t* counts, int32_t N, moero_stats* out);
  * b[e] += u * sign(mean_load - load[e]), sign(0) = 0, in fp32. */
 void moero_bias_update(float* bias, const int32_t* counts, int32_t N, float u);
 
+/* Local dispatch ([P2] DeepEP section: tokens go to the experts they were
+ * routed to, grouped by destination; on one device that is a gather into
+ * expert-contiguous order). For every position pos of the layout with
+ * perm[pos] >= 0, row pos of x_out is the row of token perm[pos] / Kt of x.
+ * Rows are row_bytes bytes (copied, not converted); rows whose perm entry is
+ * -1 are not written. */
+void moero_dispatch(const void* x, int64_t row_bytes, int32_t T, int32_t Kt,
+                    const int32_t* perm, void* x_out);
+
+/* Weighted combine ([P2] token routing: the layer output is the sum of the
+ * chosen experts' outputs weighted by the routing weights; [P2] DeepEP
+ * section: combine returns them to token order). out [T*Kt][d] holds one
+ * expert-output row per layout position (fp64 copies of the exact values),
+ * w [T][Kt] the fp32 weights: y[t] = sum over the slots k of token t that
+ * have a position (perm[pos] == t*Kt + k) of w[t][k] * out[pos], in fp64.
+ * A slot with no position contributes nothing. */
+void moero_combine(const double* out, const float* w, const int32_t* perm,
+                   int32_t T, int32_t Kt, int32_t d, double* y);
+
 int moero_num_threads(void);
 
 #ifdef __cplusplus

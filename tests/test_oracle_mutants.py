@@ -58,6 +58,16 @@ MUTANTS = [
     ("gap misses the top-K boundary",
      "double dk = (double)cand[K - 1].v - (double)cand[K].v;\n          if (dk < margin) margin = dk;",
      "double dk = (double)cand[K - 1].v - (double)cand[K].v;\n          (void)dk;"),
+    ("dispatch token from the slot index", "const int64_t t = perm[pos] / Kt;",
+     "const int64_t t = perm[pos] % Kt;"),
+    ("dispatch drops the first slot", "if (perm[pos] < 0) continue;", "if (perm[pos] <= 0) continue;"),
+    ("combine weight of the token's first slot", "const double wk = (double)w[slot];",
+     "const double wk = (double)w[t * Kt];"),
+    ("combine keeps only the last slot", "y[t * d + j] += wk * out[pos * d + j];",
+     "y[t * d + j] = wk * out[pos * d + j];"),
+    ("combine skips position 0",
+     "for (int64_t pos = 0; pos < A; ++pos) {\n    const int32_t slot = perm[pos];",
+     "for (int64_t pos = 1; pos < A; ++pos) {\n    const int32_t slot = perm[pos];"),
 ]
 
 

@@ -288,6 +288,96 @@ def test_layout_keeps_slot_order_for_repeated_ids_and_skips_invalid():
     assert inv.tolist() == [1, 2, 0, -1, 3, -1]
 
 
+# -------------------------------------------- [P2] dispatch and combine
+def _idx_with_repeats_and_invalid(T, Kt, Nb, seed):
+    g = np.random.default_rng(seed)
+    idx = g.integers(0, Nb, (T, Kt)).astype(np.int32)   # repeats allowed
+    idx[g.random((T, Kt)) < 0.1] = -1                     # some unplaced slots
+    idx[g.random((T, Kt)) < 0.05] = Nb + 3
+    return idx
+
+
+def _token_coded_rows(T, d):
+    # row t carries t in its first two bf16 words and a t-dependent pattern
+    x = np.empty((T, d), np.uint16)
+    x[:, 0] = np.arange(T) & 0xFFFF
+    x[:, 1] = np.arange(T) >> 16
+    x[:, 2:] = (np.arange(T)[:, None] * 131 + np.arange(2, d)[None, :] * 7) & 0xFFFF
+    return x
+
+
+@pytest.mark.parametrize("T,Kt,Nb,d", [(1, 1, 1, 8), (37, 3, 5, 16), (64, 9, 17, 24)])
+def test_dispatch_buckets_hold_the_routed_tokens_in_token_order(T, Kt, Nb, d):
+    # Checked from idx alone (not from perm): bucket e of the output holds, in
+    # ascending token order, one copy of token t's row per slot of t routed to
+    # e; positions past the placed rows are untouched.
+    idx = _idx_with_repeats_and_invalid(T, Kt, Nb, seed=T * 7 + Nb)
+    x = _token_coded_rows(T, d)
+    counts, offsets, perm, _ = oracle.layout(idx, Nb)
+    sentinel = np.full((T * Kt, d), 0xDEAD, np.uint16)
+    xd = oracle.dispatch(x, perm, Kt, out=sentinel)
+    placed = int(((idx >= 0) & (idx < Nb)).sum())
+    pos = 0
+    for e in range(Nb):
+        want = [t for t in range(T) for k in range(Kt) if idx[t, k] == e]
+        got = xd[pos:pos + len(want)]
+        tok = got[:, 0].astype(np.int64) | (got[:, 1].astype(np.int64) << 16)
+        assert tok.tolist() == want
+        assert (got == x[want]).all()
+        pos += len(want)
+    assert pos == placed
+    assert (xd[placed:] == 0xDEAD).all()
+
+
+def test_dispatch_copies_bytes_of_any_row_type():
+    idx = np.array([[1, 0], [1, 1]], np.int32)
+    _, _, perm, _ = oracle.layout(idx, 2)
+    x = np.array([[1.5, -0.0, np.inf], [np.nan, 2.25, -3.0]], np.float32)
+    xd = oracle.dispatch(x, perm, 2)
+    want = np.array([x[0], x[0], x[1], x[1]])
+    assert xd.view(np.uint32).tolist() == want.view(np.uint32).tolist()
+
+
+@pytest.mark.parametrize("T,Kt,Nb,d", [(5, 1, 3, 4), (40, 4, 6, 12), (33, 9, 10, 8)])
+def test_combine_of_scaling_experts_closed_form(T, Kt, Nb, d):
+    # Experts that multiply their rows by c_e: the combined row of token t is
+    # x[t] * sum over its placed slots k of w[t,k] * c[idx[t,k]] — computed
+    # from idx directly. Dyadic values keep every sum exact in fp64.
+    g = np.random.default_rng(T + Kt)
+    idx = _idx_with_repeats_and_invalid(T, Kt, Nb, seed=Kt * 11 + d)
+    x = g.integers(-8, 9, (T, d)).astype(np.float64)
+    c = g.integers(1, 9, Nb) / 4.0
+    w = (g.integers(0, 9, (T, Kt)) / 8.0).astype(np.float32)
+    counts, offsets, perm, _ = oracle.layout(idx, Nb)
+    xd = oracle.dispatch(x, perm, Kt)
+    expert_of_pos = np.searchsorted(offsets, np.arange(T * Kt), side="right") - 1
+    out = xd * np.where(expert_of_pos < Nb, c[np.minimum(expert_of_pos, Nb - 1)], 0.0)[:, None]
+    y = oracle.combine(out, w, perm)
+    valid = (idx >= 0) & (idx < Nb)
+    factor = (w.astype(np.float64) * np.where(valid, c[np.clip(idx, 0, Nb - 1)], 0.0)).sum(1)
+    assert (y == x * factor[:, None]).all()
+
+
+def test_combine_of_identity_experts_returns_the_input():
+    # w = 1/Kt on every slot (Kt a power of two): dispatch then combine through
+    # identity experts gives x back exactly; one-hot weights pick one slot.
+    g = np.random.default_rng(9)
+    T, Kt, Nb, d = 50, 4, 7, 16
+    idx = g.integers(0, Nb, (T, Kt)).astype(np.int32)
+    x = g.standard_normal((T, d))
+    _, _, perm, _ = oracle.layout(idx, Nb)
+    xd = oracle.dispatch(x, perm, Kt)
+    y = oracle.combine(xd, np.full((T, Kt), 0.25, np.float32), perm)
+    assert (y == x).all()
+    onehot = np.zeros((T, Kt), np.float32)
+    onehot[np.arange(T), np.arange(T) % Kt] = 1.0
+    marked = xd * (1.0 + np.arange(T * Kt))[:, None]   # row pos scaled by pos + 1
+    y1 = oracle.combine(marked, onehot, perm)
+    _, _, _, inv = oracle.layout(idx, Nb)
+    chosen = inv.reshape(T, Kt)[np.arange(T), np.arange(T) % Kt]
+    assert (y1 == x * (1.0 + chosen)[:, None]).all()
+
+
 # ------------------------------------------------------------ bias update
 def test_bias_update_closed_form():
     g = torch.Generator().manual_seed(4)
