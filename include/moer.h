@@ -189,6 +189,44 @@ moer_status moer_load_stats(const int32_t* counts, int32_t n_layers, int32_t N,
 moer_status moer_bias_update(float* bias, const int32_t* counts, int32_t n_layers,
                              int32_t N, int32_t stride, float u, void* stream);
 
+/* Local dispatch (hotdry "DeepSeek V4 MoE load balancing", DeepEP section:
+ * dispatch carries each token to the experts it was routed to; on one device
+ * that is a gather into the layout's expert-contiguous order). For every
+ * layer l, token t and slot k whose position p = inv_perm[l][t*Kt + k] lies
+ * in [0, T*Kt):
+ *   x_out[l][p] = x[l][t]        (a row of row_bytes bytes, copied as is)
+ * so the rows of expert e end up at offsets[e] .. offsets[e+1]-1, tokens
+ * ascending. Rows of x_out that no slot names are not written.
+ *   x        [L][T] rows of row_bytes, device, 16-byte aligned
+ *   inv_perm [L][T*Kt] int32, device (moer_route's inv_perm); entries that
+ *            are negative or >= T*Kt are skipped
+ *   x_out    [L][T*Kt] rows of row_bytes, device, 16-byte aligned; must not
+ *            overlap x
+ * row_bytes > 0 and a multiple of 16; 1 <= Kt <= 16; T*Kt < 2^31. Reads each
+ * x row once and writes Kt rows. MOER_EINVAL on a bad argument. */
+moer_status moer_dispatch(const void* x, int64_t row_bytes, int32_t n_layers, int32_t T,
+                          int32_t Kt, const int32_t* inv_perm, void* x_out, void* stream);
+
+/* Weighted combine (hotdry, token routing section: the layer output is the
+ * sum of the chosen experts' outputs weighted by the routing weights; DeepEP
+ * section: combine returns them to token order):
+ *   y[l][t] = sum over slots k of token t with a position p (as in
+ *             moer_dispatch) of w[l][t][k] * expert_out[l][p]
+ * accumulated in fp32 in slot order (one fused multiply-add per term),
+ * rounded once to y's dtype (bf16: round to nearest even). A token with no
+ * placed slot gets a zero row.
+ *   expert_out [L][T*Kt][d] in out_dtype (MOER_BF16 or MOER_F32), device,
+ *              16-byte aligned: one expert-output row per layout position
+ *   w          [L][T][Kt] fp32 (moer_route's topk_w; shared slots weigh 1)
+ *   inv_perm   [L][T*Kt] int32, as in moer_dispatch
+ *   y          [L][T][d] in y_dtype (MOER_BF16 or MOER_F32), device,
+ *              16-byte aligned; must not overlap the inputs
+ * d > 0 and a multiple of 8; 1 <= Kt <= 16; T*Kt < 2^31. Reads Kt rows and
+ * writes one row per token. MOER_EINVAL on a bad argument. */
+moer_status moer_combine(const void* expert_out, moer_dtype out_dtype, const float* w,
+                         const int32_t* inv_perm, int32_t n_layers, int32_t T, int32_t Kt,
+                         int32_t d, void* y, moer_dtype y_dtype, void* stream);
+
 const char* moer_status_str(moer_status status);
 const char* moer_last_error(void);
 int moer_abi_version(void);

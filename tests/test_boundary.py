@@ -149,3 +149,59 @@ def test_stats_and_bias_validation():
         moer.MOER_EINVAL
     assert lib.moer_bias_update(fake, fake, 1, 4, 4, ctypes.c_float(-1.0), None) == \
         moer.MOER_EINVAL
+
+
+def _dispatch_raw(x=0x1000, row_bytes=14336, L=1, T=4, Kt=8, inv=0x2000, out=0x3000):
+    st = _moer._lib.moer_dispatch(x, row_bytes, L, T, Kt, inv, out, None)
+    return st, _moer._lib.moer_last_error().decode()
+
+
+def _combine_raw(eo=0x1000, eo_dt=moer.MOER_BF16, w=0x2000, inv=0x3000, L=1, T=4, Kt=8, d=7168,
+                 y=0x4000, y_dt=moer.MOER_BF16):
+    st = _moer._lib.moer_combine(eo, eo_dt, w, inv, L, T, Kt, d, y, y_dt, None)
+    return st, _moer._lib.moer_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(L=0), "n_layers"),
+    (dict(T=-1), "T >= 0"),
+    (dict(Kt=0), "Kt must"),
+    (dict(Kt=17), "Kt must"),
+    (dict(T=2**28, Kt=8), "2^31"),
+    (dict(row_bytes=0), "row_bytes"),
+    (dict(row_bytes=14344), "row_bytes"),
+    (dict(x=None), "required"),
+    (dict(inv=None), "required"),
+    (dict(out=None), "required"),
+    (dict(x=0x1008), "aligned"),
+    (dict(out=0x3004), "aligned"),
+])
+def test_dispatch_rejects_bad_arguments(kw, frag):
+    st, msg = _dispatch_raw(**kw)
+    assert st == moer.MOER_EINVAL and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(L=0), "n_layers"),
+    (dict(Kt=0), "Kt must"),
+    (dict(Kt=17), "Kt must"),
+    (dict(d=0), "multiple of 8"),
+    (dict(d=7164), "multiple of 8"),
+    (dict(eo_dt=7), "MOER_BF16 or MOER_F32"),
+    (dict(y_dt=-1), "MOER_BF16 or MOER_F32"),
+    (dict(eo=None), "required"),
+    (dict(w=None), "required"),
+    (dict(inv=None), "required"),
+    (dict(y=None), "required"),
+    (dict(eo=0x1002), "aligned"),
+    (dict(y=0x4008), "aligned"),
+])
+def test_combine_rejects_bad_arguments(kw, frag):
+    st, msg = _combine_raw(**kw)
+    assert st == moer.MOER_EINVAL and frag in msg, msg
+
+
+def test_dispatch_and_combine_of_no_tokens_launch_nothing():
+    # T = 0 returns before any device call, so it runs without a GPU
+    assert _dispatch_raw(T=0, x=None, inv=None, out=None)[0] == moer.MOER_OK
+    assert _combine_raw(T=0, eo=None, w=None, inv=None, y=None)[0] == moer.MOER_OK

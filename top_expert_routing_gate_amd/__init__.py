@@ -1,10 +1,10 @@
 """MI355X-native Mixture-of-Experts router (gfx950 HIP kernels behind a C ABI).
 
 The C-ABI entry points (include/moer.h) are re-exported under their own names
-(``moer_route``, ``moer_load_stats``, ``moer_bias_update``, ...). ``route``,
-``load_stats`` and ``bias_update`` are conveniences that allocate the output
-tensors with torch and pass the current stream; all routing work runs in the
-library's kernels.
+(``moer_route``, ``moer_load_stats``, ``moer_bias_update``, ``moer_dispatch``,
+``moer_combine``, ...). ``route``, ``load_stats``, ``bias_update``, ``dispatch``
+and ``combine`` are conveniences that allocate the output tensors with torch
+and pass the current stream; all routing work runs in the library's kernels.
 """
 import torch
 
@@ -33,6 +33,8 @@ from ._moer import (  # noqa: F401
     make_desc,
     moer_abi_version,
     moer_bias_update,
+    moer_combine,
+    moer_dispatch,
     moer_load_stats,
     moer_route,
     moer_route_workspace_bytes,
@@ -118,3 +120,37 @@ def bias_update(bias, counts, u=1e-3, stream=None):
     bias2, counts2 = _layers(bias, 2), _layers(counts, 2)
     moer_bias_update(bias2, counts2, bias2.shape[0], bias2.shape[1], counts2.shape[1], u, stream)
     return bias
+
+
+def _rows(t, rank):
+    return t if t.dim() == rank else t.unsqueeze(0)
+
+
+def dispatch(x, inv_perm, Kt, out=None, stream=None):
+    """Gather token rows into the layout's expert-contiguous order.
+
+    x [L,T,d] (any dtype; rows are copied as bytes), inv_perm [L,T*Kt] as
+    returned by ``route``; returns out [L,T*Kt,d] (allocated when None; rows
+    no slot names are left as they are, i.e. uninitialised in a new tensor).
+    """
+    x, inv_perm = _rows(x, 3), _rows(inv_perm, 2)
+    L, T, d = x.shape
+    if out is None:
+        out = torch.empty(L, T * Kt, d, dtype=x.dtype, device=x.device)
+    moer_dispatch(x, d * x.element_size(), L, T, Kt, inv_perm, out, stream)
+    return out
+
+
+def combine(expert_out, w, inv_perm, out_dtype=torch.bfloat16, out=None, stream=None):
+    """Weighted combine back to token order: y[l,t] = sum_k w[l,t,k] *
+    expert_out[l, inv_perm[l, t*Kt+k]] (fp32 accumulation, one rounding).
+
+    expert_out [L,T*Kt,d] bf16/fp32, w [L,T,Kt] fp32; returns y [L,T,d].
+    """
+    expert_out, w, inv_perm = _rows(expert_out, 3), _rows(w, 3), _rows(inv_perm, 2)
+    L, T, Kt = w.shape
+    d = expert_out.shape[2]
+    if out is None:
+        out = torch.empty(L, T, d, dtype=out_dtype, device=expert_out.device)
+    moer_combine(expert_out, w, inv_perm, L, T, Kt, d, out, stream)
+    return out

@@ -20,7 +20,8 @@ MOER_IN_HIDDEN, MOER_IN_SCORES, MOER_IN_INDICES = 0, 1, 2
 MOER_MAX_EXPERTS, MOER_MAX_SLOTS = 256, 16
 
 EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats", "moer_bias_update",
-            "moer_status_str", "moer_last_error", "moer_abi_version")
+            "moer_dispatch", "moer_combine", "moer_status_str", "moer_last_error",
+            "moer_abi_version")
 
 
 class MoerRouteDesc(ctypes.Structure):
@@ -71,6 +72,10 @@ def _load():
     lib.moer_load_stats.restype = ctypes.c_int
     lib.moer_bias_update.argtypes = [P, P, i32, i32, i32, ctypes.c_float, P]
     lib.moer_bias_update.restype = ctypes.c_int
+    lib.moer_dispatch.argtypes = [P, ctypes.c_int64, i32, i32, i32, P, P, P]
+    lib.moer_dispatch.restype = ctypes.c_int
+    lib.moer_combine.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, ctypes.c_int, P]
+    lib.moer_combine.restype = ctypes.c_int
     lib.moer_status_str.argtypes = [ctypes.c_int]
     lib.moer_status_str.restype = ctypes.c_char_p
     lib.moer_last_error.restype = ctypes.c_char_p
@@ -197,6 +202,32 @@ def moer_bias_update(bias, counts, n_layers, N, stride, u, stream=None):
         raise TypeError("bias must be float32 and counts int32")
     _check(_lib.moer_bias_update(_ptr(bias), _ptr(counts), n_layers, N, stride, u,
                                  _stream(stream)))
+
+
+_DTYPE_CODE = {torch.bfloat16: MOER_BF16, torch.float32: MOER_F32}
+
+
+def moer_dispatch(x, row_bytes, n_layers, T, Kt, inv_perm, x_out, stream=None):
+    """x [L,T,...] rows of row_bytes bytes -> x_out [L,T*Kt,...] in layout
+    order (rows no slot names are left as they are)."""
+    if inv_perm.dtype != torch.int32:
+        raise TypeError("inv_perm must be int32")
+    if x.dtype != x_out.dtype:
+        raise TypeError("x and x_out must have the same dtype")
+    _check(_lib.moer_dispatch(_ptr(x), int(row_bytes), n_layers, T, Kt, _ptr(inv_perm),
+                              _ptr(x_out), _stream(stream)))
+
+
+def moer_combine(expert_out, w, inv_perm, n_layers, T, Kt, d, y, stream=None):
+    """y [L,T,d] = per token the w-weighted sum of its slots' rows of
+    expert_out [L,T*Kt,d]; expert_out and y are bf16 or fp32."""
+    if w.dtype != torch.float32 or inv_perm.dtype != torch.int32:
+        raise TypeError("w must be float32 and inv_perm int32")
+    if expert_out.dtype not in _DTYPE_CODE or y.dtype not in _DTYPE_CODE:
+        raise TypeError("expert_out and y must be bfloat16 or float32")
+    _check(_lib.moer_combine(_ptr(expert_out), _DTYPE_CODE[expert_out.dtype], _ptr(w),
+                             _ptr(inv_perm), n_layers, T, Kt, d, _ptr(y), _DTYPE_CODE[y.dtype],
+                             _stream(stream)))
 
 
 def decode_load_stats(raw):

@@ -29,6 +29,16 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+moer_status check_rows(int32_t n_layers, int32_t T, int32_t Kt) {
+  if (n_layers < 1 || T < 0) return fail(MOER_EINVAL, "need n_layers >= 1 and T >= 0");
+  if (Kt < 1 || Kt > MOER_MAX_SLOTS)
+    return fail(MOER_EINVAL, "Kt must be in [1, %d] (got %d)", MOER_MAX_SLOTS, Kt);
+  if ((int64_t)T * Kt >= ((int64_t)1 << 31)) return fail(MOER_EINVAL, "T * Kt must be < 2^31");
+  return MOER_OK;
+}
+
 // Workspace regions (byte offsets) for a validated descriptor.
 struct Plan {
   int Kt, Nb, nsb, nlb, ksplit;
@@ -293,6 +303,44 @@ moer_status moer_bias_update(float* bias, const int32_t* counts, int32_t n_layer
   hipError_t he = moer::launch_bias_update(bias, counts, n_layers, N, stride, u,
                                            static_cast<hipStream_t>(stream));
   if (he != hipSuccess) return fail(MOER_EHIP, "bias_update launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+moer_status moer_dispatch(const void* x, int64_t row_bytes, int32_t n_layers, int32_t T,
+                          int32_t Kt, const int32_t* inv_perm, void* x_out, void* stream) {
+  const moer_status st = check_rows(n_layers, T, Kt);
+  if (st != MOER_OK) return st;
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(MOER_EINVAL, "row_bytes must be a positive multiple of 16 (got %lld)",
+                (long long)row_bytes);
+  if (T == 0) return ok();
+  if (x == nullptr || inv_perm == nullptr || x_out == nullptr)
+    return fail(MOER_EINVAL, "x, inv_perm and x_out are required");
+  if (!aligned16(x) || !aligned16(x_out))
+    return fail(MOER_EINVAL, "x and x_out must be 16-byte aligned");
+  hipError_t he = moer::launch_dispatch(x, row_bytes, n_layers, T, Kt, inv_perm, x_out,
+                                        static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(MOER_EHIP, "dispatch launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+moer_status moer_combine(const void* expert_out, moer_dtype out_dtype, const float* w,
+                         const int32_t* inv_perm, int32_t n_layers, int32_t T, int32_t Kt,
+                         int32_t d, void* y, moer_dtype y_dtype, void* stream) {
+  const moer_status st = check_rows(n_layers, T, Kt);
+  if (st != MOER_OK) return st;
+  if (d < 1 || d % 8 != 0) return fail(MOER_EINVAL, "d must be a positive multiple of 8 (got %d)", d);
+  if ((out_dtype != MOER_BF16 && out_dtype != MOER_F32) || (y_dtype != MOER_BF16 && y_dtype != MOER_F32))
+    return fail(MOER_EINVAL, "out_dtype and y_dtype must be MOER_BF16 or MOER_F32");
+  if (T == 0) return ok();
+  if (expert_out == nullptr || w == nullptr || inv_perm == nullptr || y == nullptr)
+    return fail(MOER_EINVAL, "expert_out, w, inv_perm and y are required");
+  if (!aligned16(expert_out) || !aligned16(y))
+    return fail(MOER_EINVAL, "expert_out and y must be 16-byte aligned");
+  hipError_t he = moer::launch_combine(expert_out, out_dtype == MOER_BF16, w, inv_perm, n_layers,
+                                       T, Kt, d, y, y_dtype == MOER_BF16,
+                                       static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(MOER_EHIP, "combine launch: %s", hipGetErrorString(he));
   return ok();
 }
 

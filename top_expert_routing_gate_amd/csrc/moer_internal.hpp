@@ -72,6 +72,12 @@ hipError_t launch_load_stats(const int32_t* counts, int L, int N, int stride, mo
 hipError_t launch_bias_update(float* bias, const int32_t* counts, int L, int N, int stride,
                               float u, hipStream_t s);
 
+// Local dispatch / weighted combine (token-major, one wavefront per token).
+hipError_t launch_dispatch(const void* x, int64_t row_bytes, int L, int T, int Kt,
+                           const int32_t* inv_perm, void* out, hipStream_t s);
+hipError_t launch_combine(const void* eo, int eo_bf16, const float* w, const int32_t* inv_perm,
+                          int L, int T, int Kt, int d, void* y, int y_bf16, hipStream_t s);
+
 // Experts held per lane by the one-wave-per-token selection.
 inline int experts_per_lane(int N) { return N > 128 ? 4 : (N > 64 ? 2 : 1); }
 

@@ -120,3 +120,16 @@ def make_indices(T, Kt, Nb, seed, n_layers=1):
     g = torch.Generator().manual_seed(seed)
     r = torch.rand(n_layers, T, Nb, generator=g)
     return torch.argsort(r, dim=-1)[..., :Kt].to(torch.int32).contiguous()
+
+
+def make_expert_rows(n_rows, d, seed, dtype=BF16, n_layers=1):
+    """Stand-in expert outputs [L,n_rows,d] ~ N(0,1), one row per layout
+    position (the experts themselves are outside the router)."""
+    g = torch.Generator().manual_seed(seed)
+    return _round(torch.randn(n_layers, n_rows, d, generator=g), dtype)
+
+
+def make_weights(T, Kt, seed, n_layers=1):
+    """Positive fp32 weights [L,T,Kt] in (0, 1) for combine-only tests."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.rand(n_layers, T, Kt, generator=g).float().contiguous()
