@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--overlap", action="store_true",
                    help="alternate two streams so step i+1's gate GEMM overlaps step i's "
                         "selection and layout (measured slower: the GEMM needs every CU)")
+    p.add_argument("--no-dispatch-combine", action="store_true",
+                   help="skip timing the local dispatch and weighted combine that follow the "
+                        "route (reported beside the route, not part of its step)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration)")
     p.add_argument("--summarize-trace", metavar="DIR",
@@ -63,7 +66,9 @@ def summarize_trace(d, out, command):
 
     stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     rows = list(csv.DictReader(open(stats[0])))
-    lines = ["# Kernel trace: router step, DeepSeek-V3-style 16k-token batch", "",
+    lines = ["# Kernel trace: bench.py on the DeepSeek-V3-style 16k-token batch", "",
+             "Route steps (gate GEMM, selection, layout; warmup, value pass and event-timed "
+             "pass), then the local dispatch and weighted combine of the same batch.", "",
              "Command (from /tmp, TMPDIR=/tmp):", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -189,6 +194,42 @@ def cpu_baseline(wl, inp):
                       f"scores, selection, entropy, layout, load stats, bias update; {dt:.1f} s"}
 
 
+def time_dispatch_combine(moer, torch, wl, x, outs, stream, steps):
+    """Local dispatch of the batch to its experts and the weighted combine
+    back, on the route's last layout (bf16 rows; the dispatched rows stand in
+    for the expert outputs). Each is timed over `steps` launches between two
+    events on the route's stream. Algorithmic bytes per launch: every token
+    row read once and written Kt times (dispatch), Kt rows read and one
+    written (combine): L*T*(1+Kt)*d*2."""
+    L, T, Kt, d = wl.n_layers, wl.T, wl.Kt, wl.d
+    dev = x.device
+    xd = torch.empty(L, T * Kt, d, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(L, T, d, dtype=torch.bfloat16, device=dev)
+    inv, w = outs["inv_perm"], outs["topk_w"]
+    res = {}
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            moer.dispatch(x, inv, Kt, out=xd)
+            moer.combine(xd, w, inv, out=y)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            moer.dispatch(x, inv, Kt, out=xd)
+        ev[1].record(stream)
+        for _ in range(steps):
+            moer.combine(xd, w, inv, out=y)
+        ev[2].record(stream)
+    torch.cuda.synchronize()
+    nbytes = L * T * (1 + Kt) * d * 2
+    for k, (a, b) in (("dispatch", (0, 1)), ("combine", (1, 2))):
+        us = ev[a].elapsed_time(ev[b]) * 1e3 / steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[k] = {"us": us, "bytes": nbytes, "achieved": gbs, "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+    del xd, y
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -311,6 +352,12 @@ def main():
           f"gate GEMM {gemm_ms * 1e3:.1f} us (event-timed pass); last imbalance "
           f"{st['imbalance']:.3f}", file=sys.stderr, flush=True)
 
+    dc = None
+    if not args.no_dispatch_combine:
+        dc = time_dispatch_combine(moer, torch, wl, xs[0], outs, streams[0], args.steps)
+        print(f"[bench] dispatch {dc['dispatch']['us']:.1f} us, combine "
+              f"{dc['combine']['us']:.1f} us", file=sys.stderr, flush=True)
+
     esize = 2 if wl.dtype == workloads.BF16 else 4
     alg_bytes = L * (T + N) * wl.d * esize  # x + W_g of every layer per launch
     achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
@@ -336,6 +383,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
     }
+    if dc is not None:
+        line["dispatch_combine"] = dc
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one batch", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, {"x": xs_cpu[0], "W": W, "bias": b0})
