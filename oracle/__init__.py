@@ -10,10 +10,12 @@ from .api import (  # noqa: F401
     SOFTMAX,
     affinities,
     agg_entropy,
+    balanced_indices,
     bias_update,
     build_oracle,
     combine,
     dispatch,
+    hotspot_accumulate,
     layout,
     load_stats,
     num_threads,

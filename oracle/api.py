@@ -65,6 +65,8 @@ def _load():
         lib.moero_bias_update.argtypes = [P, P, i32, ctypes.c_float]
         lib.moero_dispatch.argtypes = [P, ctypes.c_int64, i32, i32, P, P]
         lib.moero_combine.argtypes = [P, P, P, i32, i32, i32, P]
+        lib.moero_balanced_indices.argtypes = [i32, i32, i32, i32, i32, P]
+        lib.moero_hotspot_accumulate.argtypes = [P, P, i32, i32, i32]
         lib.moero_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -167,6 +169,23 @@ def combine(out_rows, w, perm):
     y = np.empty((T, d), np.float64)
     _load().moero_combine(_p(out_rows), _p(w), _p(perm), T, Kt, d, _p(y))
     return y
+
+
+def balanced_indices(T, K, N, n_shared=0, first=0):
+    """Forcible-balance expert ids [T, K + n_shared] int32."""
+    idx = np.empty((T, K + n_shared), np.int32)
+    _load().moero_balanced_indices(T, K, N, n_shared, int(first), _p(idx))
+    return idx
+
+
+def hotspot_accumulate(hot, counts, N):
+    """Returns hot [L, N] int64 plus counts[:, :N] (inputs are not modified)."""
+    hot = np.array(hot, dtype=np.int64, copy=True, order="C")
+    counts = _c(np.atleast_2d(counts), np.int32)
+    L, stride = counts.shape
+    assert hot.shape == (L, N)
+    _load().moero_hotspot_accumulate(_p(hot), _p(counts), L, N, stride)
+    return hot
 
 
 def load_stats(counts):

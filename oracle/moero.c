@@ -292,6 +292,28 @@ void moero_combine(const double* out, const float* w, const int32_t* perm,
   }
 }
 
+/* [P5] forcible load balancing: consecutive assignments of the batch walk
+ * the experts round-robin, so every expert receives the same number (within
+ * one) and a token's K routed slots are K different experts when K <= N. */
+void moero_balanced_indices(int32_t T, int32_t K, int32_t N, int32_t n_shared, int32_t first,
+                            int32_t* idx) {
+  const int32_t Kt = K + n_shared;
+  int64_t start = first % N;
+  if (start < 0) start += N;
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t k = 0; k < K; ++k)
+      idx[(int64_t)t * Kt + k] = (int32_t)(((int64_t)t * K + k + start) % N);
+    for (int32_t j = 0; j < n_shared; ++j) idx[(int64_t)t * Kt + K + j] = N + j;
+  }
+}
+
+/* [P5] hotspot collection: add this batch's per-expert token counts. */
+void moero_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t n_layers, int32_t N,
+                              int32_t stride) {
+  for (int32_t l = 0; l < n_layers; ++l)
+    for (int32_t e = 0; e < N; ++e) hot[(int64_t)l * N + e] += counts[(int64_t)l * stride + e];
+}
+
 /* [P4] Run the example: total, mean = total / N, imbalance = max / mean
  * (0 when the mean is 0), capacity = max · N. Added: argmax (lowest expert on
  * ties); load entropy in bits of counts/total ([P1] Mathematics applied to

@@ -117,6 +117,19 @@ void moero_dispatch(const void* x, int64_t row_bytes, int32_t T, int32_t Kt,
 void moero_combine(const double* out, const float* w, const int32_t* perm,
                    int32_t T, int32_t Kt, int32_t d, double* y);
 
+/* Forcible load balancing ([P5]: the top-k output is replaced by indices
+ * that load every expert equally, as an upper bound for balancing): slot k
+ * < K of token t gets expert (t*K + k + first) mod N, the n_shared shared
+ * slots get N..N+n_shared-1. idx is [T][K + n_shared]. */
+void moero_balanced_indices(int32_t T, int32_t K, int32_t N, int32_t n_shared, int32_t first,
+                            int32_t* idx);
+
+/* Expert hotspot collection ([P5]: per layer and expert, the number of
+ * tokens the expert processed): hot[l][e] += counts[l*stride + e] for
+ * e < N, over n_layers layers. */
+void moero_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t n_layers, int32_t N,
+                              int32_t stride);
+
 int moero_num_threads(void);
 
 #ifdef __cplusplus

@@ -68,6 +68,12 @@ MUTANTS = [
     ("combine skips position 0",
      "for (int64_t pos = 0; pos < A; ++pos) {\n    const int32_t slot = perm[pos];",
      "for (int64_t pos = 1; pos < A; ++pos) {\n    const int32_t slot = perm[pos];"),
+    ("balanced ids restart per token", "idx[(int64_t)t * Kt + k] = (int32_t)(((int64_t)t * K + k + start) % N);",
+     "idx[(int64_t)t * Kt + k] = (int32_t)(((int64_t)k + start) % N);"),
+    ("balanced ids ignore the start", "int64_t start = first % N;", "int64_t start = 0 * first;"),
+    ("hotspot reads the wrong stride",
+     "hot[(int64_t)l * N + e] += counts[(int64_t)l * stride + e];",
+     "hot[(int64_t)l * N + e] += counts[(int64_t)l * N + e];"),
 ]
 
 

@@ -378,6 +378,44 @@ def test_combine_of_identity_experts_returns_the_input():
     assert (y1 == x * (1.0 + chosen)[:, None]).all()
 
 
+# ------------------------------------- [P5] forcible balance and hotspots
+@pytest.mark.parametrize("T,K,N,ns", [(64, 1, 4, 0), (16384, 8, 256, 0), (128, 8, 256, 1),
+                                      (100, 3, 7, 0), (5, 4, 4, 2)])
+def test_balanced_indices_load_every_expert_equally(T, K, N, ns):
+    # [P5] "absolute balance": when N divides T*K every expert gets T*K/N
+    # assignments, so imbalance is exactly 1.0 and capacity T*K ([P4]'s
+    # definitions); otherwise counts differ by at most one. A token's routed
+    # experts are distinct (K <= N); shared slots come last.
+    for first in (0, 5, -3):
+        idx = oracle.balanced_indices(T, K, N, ns, first)
+        routed = idx[:, :K]
+        assert all(len(set(r)) == K for r in routed.tolist())
+        assert (idx[:, K:] == N + np.arange(ns)).all()
+        counts = np.bincount(routed.ravel(), minlength=N)
+        assert counts.max() - counts.min() <= (0 if (T * K) % N == 0 else 1)
+        if (T * K) % N == 0:
+            st = oracle.load_stats(counts.astype(np.int32))
+            assert st["imbalance"] == 1.0 and st["capacity"] == T * K and st["cv"] == 0.0
+    assert oracle.balanced_indices(2, 2, 4, 0, 1).tolist() == [[1, 2], [3, 0]]
+
+
+def test_hotspot_matrix_sums_batches_of_counts():
+    # The hotspot matrix after three batches equals the per-layer bincount of
+    # all their expert ids together (shared buckets left out).
+    g = np.random.default_rng(3)
+    L, T, Kt, N = 3, 50, 3, 10
+    hot = np.zeros((L, N), np.int64)
+    ids = []
+    for _ in range(3):
+        idx = g.integers(0, N + 1, (L, T, Kt)).astype(np.int32)   # N = a shared bucket
+        counts = np.stack([oracle.layout(idx[l], N + 1)[0] for l in range(L)])
+        hot = oracle.hotspot_accumulate(hot, counts, N)
+        ids.append(idx)
+    allids = np.concatenate(ids, axis=1)
+    want = np.stack([np.bincount(allids[l].ravel(), minlength=N + 1)[:N] for l in range(L)])
+    assert (hot == want).all()
+
+
 # ------------------------------------------------------------ bias update
 def test_bias_update_closed_form():
     g = torch.Generator().manual_seed(4)
