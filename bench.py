@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-dispatch-combine", action="store_true",
                    help="skip timing the local dispatch and weighted combine that follow the "
                         "route (reported beside the route, not part of its step)")
+    p.add_argument("--no-forcible", action="store_true",
+                   help="skip timing the layout on forcibly balanced ids against the routed ids")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration)")
     p.add_argument("--summarize-trace", metavar="DIR",
@@ -230,6 +232,39 @@ def time_dispatch_combine(moer, torch, wl, x, outs, stream, steps):
     return res
 
 
+def time_forcible_layout(moer, torch, wl, outs, stream, steps):
+    """The layout path (moer_route in INDICES mode: counts, offsets, perm,
+    inv_perm) on the batch's routed ids and on forcibly balanced ids (every
+    expert T*K/N assignments), each over `steps` calls between two events on
+    the route's stream: the balanced case is the upper bound the pages'
+    forcible balancing measures."""
+    L, T, K, N, ns = wl.n_layers, wl.T, wl.K, wl.N, wl.n_shared
+    dev = outs["topk_idx"].device
+    desc = moer.make_desc(n_layers=L, T=T, N=N, K=K, n_shared=ns, input=moer.MOER_IN_INDICES)
+    i32 = dict(dtype=torch.int32, device=dev)
+    Kt, Nb = K + ns, N + ns
+    lay = dict(counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
+               perm=torch.empty(L, T * Kt, **i32), inv_perm=torch.empty(L, T * Kt, **i32))
+    ws = torch.empty(max(1, moer.moer_route_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        balanced = moer.balanced_indices(T, K, N, n_layers=L, n_shared=ns, device=dev)
+        routed = outs["topk_idx"].clone()
+        res = {}
+        for name, ids in (("routed_ids", routed), ("balanced_ids", balanced)):
+            call = moer.PreparedRoute(desc, workspace=ws, idx_in=ids, **lay)
+            for _ in range(3):
+                call()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(steps):
+                call()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            res[name] = {"us": ev[0].elapsed_time(ev[1]) * 1e3 / steps,
+                         "max_count": int(lay["counts"][:, :N].max())}
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -358,6 +393,12 @@ def main():
         print(f"[bench] dispatch {dc['dispatch']['us']:.1f} us, combine "
               f"{dc['combine']['us']:.1f} us", file=sys.stderr, flush=True)
 
+    fl = None
+    if not args.no_forcible:
+        fl = time_forcible_layout(moer, torch, wl, outs, streams[0], args.steps)
+        print(f"[bench] layout (INDICES mode): routed ids {fl['routed_ids']['us']:.1f} us, "
+              f"balanced ids {fl['balanced_ids']['us']:.1f} us", file=sys.stderr, flush=True)
+
     esize = 2 if wl.dtype == workloads.BF16 else 4
     alg_bytes = L * (T + N) * wl.d * esize  # x + W_g of every layer per launch
     achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
@@ -385,6 +426,8 @@ def main():
     }
     if dc is not None:
         line["dispatch_combine"] = dc
+    if fl is not None:
+        line["forcible_layout"] = fl
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one batch", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, {"x": xs_cpu[0], "W": W, "bias": b0})

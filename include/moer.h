@@ -227,6 +227,26 @@ moer_status moer_combine(const void* expert_out, moer_dtype out_dtype, const flo
                          const int32_t* inv_perm, int32_t n_layers, int32_t T, int32_t Kt,
                          int32_t d, void* y, moer_dtype y_dtype, void* stream);
 
+/* Forcible load balancing (MindIE "expert parallelism load balancer":
+ * the top-k output replaced by indices that balance the experts exactly, an
+ * upper bound for load balancing; not a routing decision). Writes
+ *   idx[l][t][k] = (t*K + k + first) mod N      for k < K
+ *   idx[l][t][K + j] = N + j                     for the n_shared shared slots
+ * into idx [L][T][K + n_shared] int32 (device), ready for moer_route's
+ * INDICES mode. Every expert gets T*K/N assignments per layer (within one);
+ * a token's K routed ids are distinct. 1 <= K <= N <= 256, K + n_shared <=
+ * 16, T*(K + n_shared) < 2^31; `first` is any integer (taken mod N). */
+moer_status moer_balanced_indices(int32_t* idx, int32_t n_layers, int32_t T, int32_t K, int32_t N,
+                                  int32_t n_shared, int32_t first, void* stream);
+
+/* Expert hotspot collection (MindIE balancer: per layer and expert, the
+ * number of tokens the expert processed): hot[l][e] += counts[l*stride + e]
+ * for e < N. hot [L][N] int64 and counts (e.g. moer_route's [L][Nb]) are
+ * device memory; stride >= N. Call once per batch; copy `hot` to the host
+ * whenever a hotspot table is written. */
+moer_status moer_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t n_layers,
+                                    int32_t N, int32_t stride, void* stream);
+
 const char* moer_status_str(moer_status status);
 const char* moer_last_error(void);
 int moer_abi_version(void);

@@ -205,3 +205,38 @@ def test_dispatch_and_combine_of_no_tokens_launch_nothing():
     # T = 0 returns before any device call, so it runs without a GPU
     assert _dispatch_raw(T=0, x=None, inv=None, out=None)[0] == moer.MOER_OK
     assert _combine_raw(T=0, eo=None, w=None, inv=None, y=None)[0] == moer.MOER_OK
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(N=0), "N must"),
+    (dict(N=257), "N must"),
+    (dict(K=0), "K must"),
+    (dict(K=9, N=8), "K must"),
+    (dict(ns=-1), "n_shared"),
+    (dict(K=8, ns=9), "Kt must"),
+    (dict(L=0), "n_layers"),
+    (dict(T=2**28), "2^31"),
+    (dict(idx=None), "required"),
+])
+def test_balanced_indices_reject_bad_arguments(kw, frag):
+    a = dict(idx=0x1000, L=1, T=16, K=8, N=256, ns=0, first=0)
+    a.update(kw)
+    st = _moer._lib.moer_balanced_indices(a["idx"], a["L"], a["T"], a["K"], a["N"], a["ns"],
+                                          a["first"], None)
+    msg = _moer._lib.moer_last_error().decode()
+    assert st == moer.MOER_EINVAL and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(hot=None), "required"),
+    (dict(counts=None), "required"),
+    (dict(L=0), "n_layers"),
+    (dict(stride=3, N=4), "stride >= N"),
+])
+def test_hotspot_accumulate_rejects_bad_arguments(kw, frag):
+    a = dict(hot=0x1000, counts=0x2000, L=1, N=4, stride=4)
+    a.update(kw)
+    st = _moer._lib.moer_hotspot_accumulate(a["hot"], a["counts"], a["L"], a["N"], a["stride"],
+                                            None)
+    msg = _moer._lib.moer_last_error().decode()
+    assert st == moer.MOER_EINVAL and frag in msg, msg

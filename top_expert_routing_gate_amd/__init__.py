@@ -32,9 +32,11 @@ from ._moer import (  # noqa: F401
     decode_load_stats,
     make_desc,
     moer_abi_version,
+    moer_balanced_indices,
     moer_bias_update,
     moer_combine,
     moer_dispatch,
+    moer_hotspot_accumulate,
     moer_load_stats,
     moer_route,
     moer_route_workspace_bytes,
@@ -154,3 +156,35 @@ def combine(expert_out, w, inv_perm, out_dtype=torch.bfloat16, out=None, stream=
         out = torch.empty(L, T, d, dtype=out_dtype, device=expert_out.device)
     moer_combine(expert_out, w, inv_perm, L, T, Kt, d, out, stream)
     return out
+
+
+def balanced_indices(T, K, N, *, n_layers=1, n_shared=0, first=0, device="cuda", stream=None):
+    """Forcible-balance expert ids [L, T, K + n_shared] int32 on the device
+    (slot k of token t -> expert (t*K + k + first) mod N), for moer_route's
+    INDICES mode."""
+    idx = torch.empty(n_layers, T, K + n_shared, dtype=torch.int32, device=device)
+    moer_balanced_indices(idx, n_layers, T, K, N, n_shared, first, stream)
+    return idx
+
+
+class HotspotRecorder:
+    """Per-layer, per-expert token counts summed over batches (the hotspot
+    matrix), kept on the device; ``write_csv`` appends the matrix (one row
+    per layer, one column per expert) to a CSV file on the host."""
+
+    def __init__(self, n_layers, N, device="cuda"):
+        self.N = N
+        self.hot = torch.zeros(n_layers, N, dtype=torch.int64, device=device)
+        self.batches = 0
+
+    def add(self, counts, stream=None):
+        counts = _layers(counts, 2)
+        moer_hotspot_accumulate(self.hot, counts, counts.shape[0], self.N, counts.shape[1], stream)
+        self.batches += 1
+
+    def write_csv(self, path):
+        m = self.hot.cpu().tolist()
+        with open(path, "a") as f:
+            for row in m:
+                f.write(",".join(str(v) for v in row) + "\n")
+        return m

@@ -20,8 +20,8 @@ MOER_IN_HIDDEN, MOER_IN_SCORES, MOER_IN_INDICES = 0, 1, 2
 MOER_MAX_EXPERTS, MOER_MAX_SLOTS = 256, 16
 
 EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats", "moer_bias_update",
-            "moer_dispatch", "moer_combine", "moer_status_str", "moer_last_error",
-            "moer_abi_version")
+            "moer_dispatch", "moer_combine", "moer_balanced_indices", "moer_hotspot_accumulate",
+            "moer_status_str", "moer_last_error", "moer_abi_version")
 
 
 class MoerRouteDesc(ctypes.Structure):
@@ -76,6 +76,10 @@ def _load():
     lib.moer_dispatch.restype = ctypes.c_int
     lib.moer_combine.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, ctypes.c_int, P]
     lib.moer_combine.restype = ctypes.c_int
+    lib.moer_balanced_indices.argtypes = [P, i32, i32, i32, i32, i32, i32, P]
+    lib.moer_balanced_indices.restype = ctypes.c_int
+    lib.moer_hotspot_accumulate.argtypes = [P, P, i32, i32, i32, P]
+    lib.moer_hotspot_accumulate.restype = ctypes.c_int
     lib.moer_status_str.argtypes = [ctypes.c_int]
     lib.moer_status_str.restype = ctypes.c_char_p
     lib.moer_last_error.restype = ctypes.c_char_p
@@ -228,6 +232,20 @@ def moer_combine(expert_out, w, inv_perm, n_layers, T, Kt, d, y, stream=None):
     _check(_lib.moer_combine(_ptr(expert_out), _DTYPE_CODE[expert_out.dtype], _ptr(w),
                              _ptr(inv_perm), n_layers, T, Kt, d, _ptr(y), _DTYPE_CODE[y.dtype],
                              _stream(stream)))
+
+
+def moer_balanced_indices(idx, n_layers, T, K, N, n_shared=0, first=0, stream=None):
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    _check(_lib.moer_balanced_indices(_ptr(idx), n_layers, T, K, N, n_shared, int(first),
+                                      _stream(stream)))
+
+
+def moer_hotspot_accumulate(hot, counts, n_layers, N, stride, stream=None):
+    if hot.dtype != torch.int64 or counts.dtype != torch.int32:
+        raise TypeError("hot must be int64 and counts int32")
+    _check(_lib.moer_hotspot_accumulate(_ptr(hot), _ptr(counts), n_layers, N, stride,
+                                        _stream(stream)))
 
 
 def decode_load_stats(raw):

@@ -344,4 +344,33 @@ moer_status moer_combine(const void* expert_out, moer_dtype out_dtype, const flo
   return ok();
 }
 
+moer_status moer_balanced_indices(int32_t* idx, int32_t n_layers, int32_t T, int32_t K, int32_t N,
+                                  int32_t n_shared, int32_t first, void* stream) {
+  if (N < 1 || N > MOER_MAX_EXPERTS)
+    return fail(MOER_EINVAL, "N must be in [1, %d] (got %d)", MOER_MAX_EXPERTS, N);
+  if (K < 1 || K > N) return fail(MOER_EINVAL, "K must be in [1, N] (got %d)", K);
+  if (n_shared < 0) return fail(MOER_EINVAL, "n_shared must be >= 0");
+  const moer_status st = check_rows(n_layers, T, K + n_shared);
+  if (st != MOER_OK) return st;
+  if (T == 0) return ok();
+  if (idx == nullptr) return fail(MOER_EINVAL, "idx is required");
+  int start = first % N;
+  if (start < 0) start += N;
+  hipError_t he = moer::launch_balanced_indices(idx, n_layers, T, K, N, n_shared, start,
+                                                static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(MOER_EHIP, "balanced_indices launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+moer_status moer_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t n_layers,
+                                    int32_t N, int32_t stride, void* stream) {
+  if (hot == nullptr || counts == nullptr) return fail(MOER_EINVAL, "hot and counts are required");
+  if (n_layers < 1 || N < 1 || stride < N)
+    return fail(MOER_EINVAL, "need n_layers >= 1, N >= 1, stride >= N");
+  hipError_t he = moer::launch_hotspot_accumulate(hot, counts, n_layers, N, stride,
+                                                  static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(MOER_EHIP, "hotspot launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
 }  // extern "C"

@@ -78,6 +78,12 @@ hipError_t launch_dispatch(const void* x, int64_t row_bytes, int L, int T, int K
 hipError_t launch_combine(const void* eo, int eo_bf16, const float* w, const int32_t* inv_perm,
                           int L, int T, int Kt, int d, void* y, int y_bf16, hipStream_t s);
 
+// Forcible-balance expert ids and hotspot accumulation (elementwise).
+hipError_t launch_balanced_indices(int32_t* idx, int L, int T, int K, int N, int n_shared,
+                                   int start, hipStream_t s);
+hipError_t launch_hotspot_accumulate(int64_t* hot, const int32_t* counts, int L, int N, int stride,
+                                     hipStream_t s);
+
 // Experts held per lane by the one-wave-per-token selection.
 inline int experts_per_lane(int N) { return N > 128 ? 4 : (N > 64 ? 2 : 1); }
 
