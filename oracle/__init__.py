@@ -6,10 +6,13 @@ code with the HIP library. The arithmetic lives in ``moero.c`` (plain C,
 fp64); this package only builds it and marshals numpy arrays.
 """
 from .api import (  # noqa: F401
+    PROPORTIONAL,
+    SIGN,
     SIGMOID,
     SOFTMAX,
     affinities,
     agg_entropy,
+    balance_step,
     balanced_indices,
     bias_update,
     build_oracle,
@@ -18,6 +21,7 @@ from .api import (  # noqa: F401
     hotspot_accumulate,
     layout,
     load_stats,
+    logit_bias,
     num_threads,
     route,
     scores,

@@ -2,7 +2,7 @@
 
 No arithmetic of the method is done here: every step calls into moero.c,
 except ``route``, which only chains those calls in the order the pages give
-(affinities -> scores -> selection -> layout -> entropy).
+(affinities -> [logit bias] -> scores -> selection -> layout -> entropy).
 """
 import ctypes
 import os
@@ -67,6 +67,9 @@ def _load():
         lib.moero_combine.argtypes = [P, P, P, i32, i32, i32, P]
         lib.moero_balanced_indices.argtypes = [i32, i32, i32, i32, i32, P]
         lib.moero_hotspot_accumulate.argtypes = [P, P, i32, i32, i32]
+        lib.moero_logit_bias.argtypes = [P, P, i32, i32]
+        lib.moero_balance_step.argtypes = [P, P, i32, i32, ctypes.c_float, ctypes.c_float, i32,
+                                           P, P]
         lib.moero_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -188,6 +191,31 @@ def hotspot_accumulate(hot, counts, N):
     return hot
 
 
+def logit_bias(h, b):
+    """Returns h [T,N] fp64 with the fp32 bias b [N] added to every row."""
+    h = np.array(h, dtype=np.float64, copy=True, order="C")
+    b = _c(b, np.float32)
+    T, N = h.shape
+    _load().moero_logit_bias(_p(h), _p(b), T, N)
+    return h
+
+
+SIGN, PROPORTIONAL = 0, 1
+
+
+def balance_step(bias, counts, *, rule=SIGN, step=1e-3, alpha=1.0, every=1, loads=None,
+                 calls=None):
+    """One balancing step; returns (bias, loads, calls) updated copies."""
+    b = np.array(bias, dtype=np.float32, copy=True)
+    counts = _c(counts, np.int32)
+    N = counts.shape[0]
+    ld = None if loads is None else np.array(loads, dtype=np.float32, copy=True)
+    cl = None if calls is None else np.array([calls], dtype=np.int32)
+    _load().moero_balance_step(_p(b), _p(counts), N, int(rule), ctypes.c_float(step),
+                               ctypes.c_float(alpha), int(every), _p(ld), _p(cl))
+    return b, ld, None if cl is None else int(cl[0])
+
+
 def load_stats(counts):
     counts = _c(counts, np.int32)
     st = _Stats()
@@ -204,16 +232,23 @@ def bias_update(bias, counts, u=1e-3):
 
 
 def route(*, K, score_fn, x=None, W=None, offset=None, s32=None, idx_in=None, bias=None,
-          n_groups=1, topk_groups=1, n_shared=0, N=None):
+          n_groups=1, topk_groups=1, n_shared=0, N=None, bias_mode="score"):
     """One router layer through the oracle, in the order of the pages.
 
     Input is one of: hidden states (x [T,d], W [N,d], fp32 holding the exact
     input values), fp32 scores s32 [T,N], or supplied indices idx_in [T,Kt].
+    bias_mode "score" adds the bias to the scores for the selection only;
+    "logit" (hidden states only) adds it to the logits.
     """
+    if bias_mode == "logit" and (x is None or idx_in is not None or s32 is not None):
+        raise ValueError("logit-space bias needs hidden-state input")
     out = {}
     if idx_in is None:
         if s32 is None:
             h = affinities(x, W, offset)
+            if bias_mode == "logit":
+                h = logit_bias(h, bias)
+                bias = None
             s64 = scores(h, score_fn)
             s32 = s64.astype(np.float32)
             out["h"] = h

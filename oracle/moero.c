@@ -314,6 +314,56 @@ void moero_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t n_lay
     for (int32_t e = 0; e < N; ++e) hot[(int64_t)l * N + e] += counts[(int64_t)l * stride + e];
 }
 
+/* [P1] listing: the dynamic bias is added to the raw gate logits before
+ * the softmax, so every later step sees the compensated logits. */
+void moero_logit_bias(double* h, const float* b, int32_t T, int32_t N) {
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t e = 0; e < N; ++e) h[(int64_t)t * N + e] += (double)b[e];
+}
+
+/* [P1] listing (proportional rule: lower an overloaded expert's bias by the
+ * decay times its relative load error) and [P2] auxiliary-loss-free section
+ * (direction-only rule; a moving average smooths the load statistics; the
+ * bias is updated every so many steps). */
+void moero_balance_step(float* bias, const int32_t* counts, int32_t N, int32_t rule, float step,
+                        float alpha, int32_t every, float* loads, int32_t* calls) {
+  const int32_t ncall = calls ? *calls : 0;
+  float* l = (float*)malloc((size_t)N * sizeof(float));
+  const float keep = 1.0f - alpha;
+  for (int32_t e = 0; e < N; ++e) {
+    volatile float ce = (float)counts[e];
+    if (loads == NULL || ncall == 0) {
+      l[e] = ce;
+    } else {
+      volatile float fresh = alpha * ce;
+      volatile float old = keep * loads[e];
+      volatile float sum = fresh + old;
+      l[e] = sum;
+    }
+    if (loads) loads[e] = l[e];
+  }
+  if ((ncall + 1) % every == 0) {
+    double total = 0.0;
+    for (int32_t e = 0; e < N; ++e) total += (double)l[e];
+    const double mean = total / (double)N;
+    for (int32_t e = 0; e < N; ++e) {
+      if (rule == 0) {
+        const double diff = mean - (double)l[e];
+        const float s = diff > 0 ? step : (diff < 0 ? -step : 0.0f);
+        volatile float nb = bias[e] + s;
+        bias[e] = nb;
+      } else if (mean > 0.0) {
+        const double rel = ((double)l[e] - mean) / mean;
+        const float delta = (float)((double)step * rel);
+        volatile float nb = bias[e] - delta;
+        bias[e] = nb;
+      }
+    }
+  }
+  if (calls) *calls = ncall + 1;
+  free(l);
+}
+
 /* [P4] Run the example: total, mean = total / N, imbalance = max / mean
  * (0 when the mean is 0), capacity = max · N. Added: argmax (lowest expert on
  * ties); load entropy in bits of counts/total ([P1] Mathematics applied to

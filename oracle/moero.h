@@ -130,6 +130,29 @@ void moero_balanced_indices(int32_t T, int32_t K, int32_t N, int32_t n_shared, i
 void moero_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t n_layers, int32_t N,
                               int32_t stride);
 
+/* Logit-space selection bias ([P1] listing "Dynamic Expert Bias Routing
+ * Controller": the bias is added to the raw logits, and the scores, the
+ * top-k, the weights and the entropy all come from the compensated logits):
+ * h[t][e] += b[e] in fp64. */
+void moero_logit_bias(double* h, const float* b, int32_t T, int32_t N);
+
+/* One balancing step with a selectable rule, smoothing and period
+ * ([P1] listing: proportional update; [P2] auxiliary-loss-free section:
+ * sign-style direction, moving-average load statistics, update period).
+ *   loads: l_e = counts_e on the first call (calls == 0 or loads NULL),
+ *          else l_e = alpha*counts_e + (1-alpha)*l_e (fp32, no fused ops);
+ *   rule, on every `every`-th call (calls+1 divisible by every):
+ *     mean = (sum over e of l_e, in fp64, ascending e) / N
+ *     SIGN (0):         b_e += step * sign(mean - l_e)          (fp32 add)
+ *     PROPORTIONAL (1): b_e -= (float)(step * ((l_e - mean) / mean)) when
+ *                       mean > 0 (fp64 divide and multiply, one rounding to
+ *                       fp32, then the fp32 subtraction)
+ *   *calls += 1 (when calls is not NULL).
+ * counts [N] int32; loads [N] fp32 state or NULL (then alpha must be 1);
+ * calls: one counter or NULL (then every must be 1). */
+void moero_balance_step(float* bias, const int32_t* counts, int32_t N, int32_t rule, float step,
+                        float alpha, int32_t every, float* loads, int32_t* calls);
+
 int moero_num_threads(void);
 
 #ifdef __cplusplus

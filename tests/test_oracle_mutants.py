@@ -74,6 +74,17 @@ MUTANTS = [
     ("hotspot reads the wrong stride",
      "hot[(int64_t)l * N + e] += counts[(int64_t)l * stride + e];",
      "hot[(int64_t)l * N + e] += counts[(int64_t)l * N + e];"),
+    ("logit bias subtracted", "h[(int64_t)t * N + e] += (double)b[e];",
+     "h[(int64_t)t * N + e] -= (double)b[e];"),
+    ("moving average weights swapped", "volatile float fresh = alpha * ce;",
+     "volatile float fresh = keep * ce;"),
+    ("proportional rule sign", "volatile float nb = bias[e] - delta;",
+     "volatile float nb = bias[e] + delta;"),
+    ("proportional error over N", "const double rel = ((double)l[e] - mean) / mean;",
+     "const double rel = ((double)l[e] - mean) / (double)N;"),
+    ("period off by one", "if ((ncall + 1) % every == 0) {", "if (ncall % every == 0) {"),
+    ("sign rule against the total", "const double diff = mean - (double)l[e];",
+     "const double diff = total - (double)l[e];"),
 ]
 
 

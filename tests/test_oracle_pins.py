@@ -437,6 +437,125 @@ def test_bias_update_closed_form():
     assert (nb[counts < mean] > b[counts < mean]).all()
 
 
+# ----------------------------------------- [P1]/[P2] balancing-rule variants
+def test_balance_step_sign_rule_closed_form_and_equals_bias_update():
+    g = np.random.default_rng(21)
+    b = (g.uniform(-0.01, 0.01, 256)).astype(np.float32)
+    counts = g.integers(400, 620, 256).astype(np.int32)
+    counts[:5] = counts[5]  # some ties with each other
+    nb, _, _ = oracle.balance_step(b, counts, rule=oracle.SIGN, step=1e-3)
+    mean = counts.sum() / 256.0
+    want = (b + np.float32(1e-3) * np.sign(mean - counts).astype(np.float32)).astype(np.float32)
+    assert (nb == want).all()
+    assert (nb == oracle.bias_update(b, counts, 1e-3)).all()
+
+
+def test_balance_step_proportional_is_the_listing_rule():
+    # [P1] listing: bias -= decay * sign(err) * |err| / target, err = load -
+    # target, target = T*K/N. Dyadic case: every quantity exact.
+    counts = np.array([128, 64, 64, 32, 96, 0, 64, 64], np.int32)  # total 512, target 64
+    b = (np.arange(8) / 64.0 - 0.0625).astype(np.float32)
+    nb, _, _ = oracle.balance_step(b, counts, rule=oracle.PROPORTIONAL, step=0.25)
+    target = 512 / 8
+    err = counts - target
+    want = b.astype(np.float64) - 0.25 * np.sign(err) * (np.abs(err) / target)
+    assert (nb.astype(np.float64) == want).all()
+    # random loads with gamma = 0.05: the listing's expression in fp64, rounded
+    # to fp32 the same way, agrees to one fp32 ulp
+    g = np.random.default_rng(8)
+    counts = g.integers(300, 700, 256).astype(np.int32)
+    b = g.uniform(-0.01, 0.01, 256).astype(np.float32)
+    nb, _, _ = oracle.balance_step(b, counts, rule=oracle.PROPORTIONAL, step=0.05)
+    target = counts.sum() / 256.0
+    err = counts - target
+    delta = (np.float64(np.float32(0.05)) * np.sign(err) * (np.abs(err) / target)).astype(np.float32)
+    want = (b - delta).astype(np.float32)
+    ulps = np.abs(nb.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1 and (ulps == 0).mean() > 0.95
+    # an overloaded expert's bias goes down, an underloaded one's up
+    assert (nb[counts > target] < b[counts > target]).all()
+    assert (nb[counts < target] > b[counts < target]).all()
+    # no load at all: no change
+    z, _, _ = oracle.balance_step(b, np.zeros(256, np.int32), rule=oracle.PROPORTIONAL, step=0.05)
+    assert (z == b).all()
+
+
+def test_balance_step_moving_average_closed_form():
+    # alpha = 1/4: l_1 = c_1, l_n = c_n/4 + 3 l_(n-1)/4, i.e.
+    # l_n = sum_(k=2..n) alpha (1-alpha)^(n-k) c_k + (1-alpha)^(n-1) c_1
+    # (dyadic values: exact in fp32 for these few steps).
+    a = 0.25
+    seq = [np.array(v, np.int32) for v in ([8, 0, 4, 4], [0, 8, 4, 4], [16, 0, 0, 0],
+                                           [4, 4, 4, 4], [0, 0, 12, 4])]
+    b = np.zeros(4, np.float32)
+    loads, calls = np.zeros(4, np.float32), 0
+    for n in range(1, len(seq) + 1):
+        b, loads, calls = oracle.balance_step(b, seq[n - 1], rule=oracle.SIGN, step=0.125,
+                                              alpha=a, loads=loads, calls=calls)
+        want = (1 - a) ** (n - 1) * seq[0] + sum(a * (1 - a) ** (n - k) * seq[k - 1]
+                                                 for k in range(2, n + 1))
+        assert (loads.astype(np.float64) == want).all(), n
+    assert calls == 5
+
+
+def test_balance_step_every_n_calls():
+    # the rule runs on calls 3 and 6 only (every = 3), always on the current
+    # loads; the call counter counts every call
+    counts = np.array([10, 2, 6, 6], np.int32)   # mean 6: expert 0 down, expert 1 up
+    b = np.zeros(4, np.float32)
+    calls = 0
+    history = []
+    for _ in range(6):
+        b, _, calls = oracle.balance_step(b, counts, rule=oracle.SIGN, step=0.5, every=3,
+                                          calls=calls)
+        history.append(b.tolist())
+    assert history[0] == history[1] == [0, 0, 0, 0]
+    assert history[2] == history[3] == history[4] == [-0.5, 0.5, 0, 0]
+    assert history[5] == [-1.0, 1.0, 0, 0] and calls == 6
+
+
+def test_logit_space_bias_matches_library_softmax_topk():
+    # [P1] listing: softmax of (logits + bias), top-k of those probabilities,
+    # weights renormalised from them, entropy of the batch mean of them.
+    g = torch.Generator().manual_seed(12)
+    T, d, N, K = 64, 32, 16, 2
+    x = torch.randn(T, d, generator=g).numpy()
+    W = (torch.randn(N, d, generator=g) / 4).numpy()
+    b = (torch.randn(N, generator=g) * 0.5).numpy().astype(np.float32)
+    out = oracle.route(x=x, W=W, bias=b, K=K, score_fn=oracle.SOFTMAX, bias_mode="logit")
+    h = x.astype(np.float64) @ W.astype(np.float64).T + b.astype(np.float64)
+    p = scipy.special.softmax(h, axis=1)
+    top = np.argsort(-p, axis=1, kind="stable")[:, :K]
+    assert (out["idx"] == top).all()
+    pt = np.take_along_axis(p, top, 1)
+    assert np.allclose(out["w"], pt / pt.sum(1, keepdims=True), rtol=1e-6)
+    mean = p.mean(0)
+    assert abs(out["agg_H"] - float(-(mean * np.log2(mean)).sum())) < 1e-12
+    # a constant logit bias leaves softmax routing unchanged
+    c = oracle.route(x=x, W=W, bias=np.full(N, 0.75, np.float32), K=K, score_fn=oracle.SOFTMAX,
+                     bias_mode="logit")
+    z = oracle.route(x=x, W=W, bias=None, K=K, score_fn=oracle.SOFTMAX)
+    assert (c["idx"] == z["idx"]).all() and np.allclose(c["w"], z["w"], rtol=1e-6)
+
+
+def test_logit_space_bias_sigmoid_groups_brute_force():
+    # sigmoid of the compensated logits, then the group-limited choice made on
+    # those scores with no further bias, checked by enumeration
+    g = np.random.default_rng(77)
+    T, d, N, G, Gk, K = 40, 8, 16, 4, 2, 4
+    x = g.standard_normal((T, d)).astype(np.float32)
+    W = g.standard_normal((N, d)).astype(np.float32)
+    b = g.uniform(-1, 1, N).astype(np.float32)
+    out = oracle.route(x=x, W=W, bias=b, K=K, score_fn=oracle.SIGMOID, n_groups=G,
+                       topk_groups=Gk, bias_mode="logit")
+    s = scipy.special.expit(x.astype(np.float64) @ W.astype(np.float64).T + b)
+    for t in range(T):
+        chosen, _, _ = _brute_force(s[t].astype(np.float32).astype(np.float64), G, Gk, K)
+        assert out["idx"][t].tolist() == chosen
+        st = s[t][chosen]
+        assert np.allclose(out["w"][t], st / st.sum(), rtol=1e-6)
+
+
 # ---------------------------------------------------------- route composite
 def test_route_chains_steps_in_order():
     g = torch.Generator().manual_seed(2)
