@@ -265,6 +265,30 @@ def time_forcible_layout(moer, torch, wl, outs, stream, steps):
     return res
 
 
+def time_balance_step(moer, torch, wl, outs, stream, steps):
+    """The balancing-rule variants on the batch's counts, each over `steps`
+    calls between two events on the route's stream (a copy of the bias, so
+    the route's own bias is untouched)."""
+    dev = outs["counts"].device
+    res = {}
+    with torch.cuda.stream(stream):
+        for name, kw in (("sign", dict(rule="sign", step=1e-3)),
+                         ("proportional_ema_every4", dict(rule="proportional", step=0.05,
+                                                          alpha=0.1, every=4))):
+            bias = torch.zeros(wl.n_layers, wl.N, device=dev)
+            state = moer.BalanceState(wl.n_layers, wl.N, device=dev)
+            for _ in range(3):
+                moer.balance_step(bias, outs["counts"], state=state, **kw)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(steps):
+                moer.balance_step(bias, outs["counts"], state=state, **kw)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            res[name] = {"us": ev[0].elapsed_time(ev[1]) * 1e3 / steps}
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -399,6 +423,10 @@ def main():
         print(f"[bench] layout (INDICES mode): routed ids {fl['routed_ids']['us']:.1f} us, "
               f"balanced ids {fl['balanced_ids']['us']:.1f} us", file=sys.stderr, flush=True)
 
+    bs = time_balance_step(moer, torch, wl, outs, streams[0], args.steps)
+    print(f"[bench] balance step: sign {bs['sign']['us']:.1f} us, proportional+EMA "
+          f"{bs['proportional_ema_every4']['us']:.1f} us", file=sys.stderr, flush=True)
+
     esize = 2 if wl.dtype == workloads.BF16 else 4
     alg_bytes = L * (T + N) * wl.d * esize  # x + W_g of every layer per launch
     achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
@@ -428,6 +456,7 @@ def main():
         line["dispatch_combine"] = dc
     if fl is not None:
         line["forcible_layout"] = fl
+    line["balance_step"] = bs
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one batch", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, {"x": xs_cpu[0], "W": W, "bias": b0})

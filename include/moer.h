@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOER_ABI_VERSION 1
+#define MOER_ABI_VERSION 2
 #define MOER_MAX_EXPERTS 256 /* N */
 #define MOER_MAX_SLOTS 16    /* Kt = K + n_shared */
 
@@ -74,6 +74,21 @@ typedef enum {
 } moer_score_fn;
 
 typedef enum { MOER_BF16 = 0, MOER_F32 = 1 } moer_dtype;
+
+typedef enum {
+  MOER_BIAS_SCORE = 0, /* key = s + b for the selection only; weights and
+                          entropy from the unbiased scores (hotdry,
+                          auxiliary-loss-free balancing) */
+  MOER_BIAS_LOGIT = 1  /* b added to the logits: scores, selection, weights
+                          and entropy all from h + b (dailyaiworld listing
+                          "Dynamic Expert Bias Routing Controller"); HIDDEN
+                          input only */
+} moer_bias_mode;
+
+typedef enum {
+  MOER_RULE_SIGN = 0,        /* b_e += step * sign(mean - load_e)          */
+  MOER_RULE_PROPORTIONAL = 1 /* b_e -= step * (load_e - mean) / mean       */
+} moer_bias_rule;
 
 typedef enum {
   MOER_IN_HIDDEN = 0,  /* x and W_g given: full path from the gate GEMM      */
@@ -96,6 +111,7 @@ typedef struct {
   int32_t score_fn;    /* moer_score_fn */
   int32_t dtype;       /* moer_dtype of x and W_g (HIDDEN mode) */
   int32_t input;       /* moer_input */
+  int32_t bias_mode;   /* moer_bias_mode (0 = MOER_BIAS_SCORE) */
 } moer_route_desc;
 
 /* Per-layer record written by moer_load_stats (device memory, 64 bytes). */
@@ -246,6 +262,38 @@ moer_status moer_balanced_indices(int32_t* idx, int32_t n_layers, int32_t T, int
  * whenever a hotspot table is written. */
 moer_status moer_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t n_layers,
                                     int32_t N, int32_t stride, void* stream);
+
+/* Balancing rule with smoothing and a period (dailyaiworld listing:
+ * proportional update with a decay factor; hotdry auxiliary-loss-free
+ * section: direction-only update, loads smoothed by a moving average, the
+ * bias updated every so many steps). */
+typedef struct {
+  int32_t rule;  /* moer_bias_rule */
+  float step;    /* u (SIGN) or the decay factor gamma (PROPORTIONAL), >= 0 */
+  float alpha;   /* moving-average weight of the new counts, in (0, 1];
+                    1 = the loads are this call's counts */
+  int32_t every; /* apply the rule on every `every`-th call, >= 1 */
+} moer_balance_cfg;
+
+/* One balancing step per layer l (one call per training step):
+ *   loads[l][e] = counts[l][e]                             on the first call
+ *                 (calls[l] == 0) or when loads is NULL,
+ *               = alpha*counts + (1-alpha)*loads[l][e]     otherwise (fp32,
+ *                 two products and a sum, no fused multiply-add)
+ *   if (calls[l] + 1) % every == 0:
+ *     mean = (sum over e < N of loads[l][e], in fp64, ascending e) / N
+ *     SIGN:         bias[l][e] += step * sign(mean - loads[l][e])
+ *     PROPORTIONAL: bias[l][e] -= (float)(step * ((loads[l][e] - mean)
+ *                   / mean)) (fp64, one rounding), no change when mean == 0
+ *   calls[l] += 1
+ * bias [L][N] fp32, in place; counts [L][stride] int32 (stride >= N, e.g.
+ * moer_route's counts); loads [L][N] fp32 caller state (required when
+ * alpha < 1); calls [L] int32 caller state (required when every > 1). Zero
+ * both before the first call. With alpha = 1, every = 1 and SIGN this is
+ * moer_bias_update (the comparison agrees with the integer one). */
+moer_status moer_balance_step(float* bias, const int32_t* counts, int32_t n_layers, int32_t N,
+                              int32_t stride, const moer_balance_cfg* cfg, float* loads,
+                              int32_t* calls, void* stream);
 
 const char* moer_status_str(moer_status status);
 const char* moer_last_error(void);

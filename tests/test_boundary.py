@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert moer.moer_abi_version() == 1
+    assert moer.moer_abi_version() == 2
     assert _moer._status_name(moer.MOER_EINVAL) == "MOER_EINVAL"
     assert _moer._status_name(moer.MOER_EWORKSPACE) == "MOER_EWORKSPACE"
 
@@ -240,3 +240,63 @@ def test_hotspot_accumulate_rejects_bad_arguments(kw, frag):
                                             None)
     msg = _moer._lib.moer_last_error().decode()
     assert st == moer.MOER_EINVAL and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(bias_mode=5), "bias_mode"),
+    (dict(bias_mode=moer.MOER_BIAS_LOGIT, input=moer.MOER_IN_SCORES), "HIDDEN"),
+    (dict(bias_mode=moer.MOER_BIAS_LOGIT, input=moer.MOER_IN_INDICES), "HIDDEN"),
+])
+def test_bias_mode_validation(kw, frag):
+    d = _desc(**kw)
+    st, msg = _route_raw(d)
+    assert st == moer.MOER_EINVAL and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(bias=None), "required"),
+    (dict(counts=None), "required"),
+    (dict(cfg=None), "required"),
+    (dict(N=300), "N <= 256"),
+    (dict(stride=100), "stride >= N"),
+    (dict(rule=3), "unknown rule"),
+    (dict(step=-1.0), "step must"),
+    (dict(step=float("inf")), "step must"),
+    (dict(step=float("nan")), "step must"),
+    (dict(alpha=0.0), "alpha must"),
+    (dict(alpha=1.5), "alpha must"),
+    (dict(every=0), "every must"),
+    (dict(alpha=0.5, loads=None), "loads state"),
+    (dict(every=4, calls=None), "calls state"),
+])
+def test_balance_step_rejects_bad_arguments(kw, frag):
+    a = dict(bias=0x1000, counts=0x2000, L=2, N=256, stride=256, rule=0, step=1e-3, alpha=1.0,
+             every=1, loads=0x3000, calls=0x4000, cfg=True)
+    a.update(kw)
+    cfg = _moer.MoerBalanceCfg(a["rule"], a["step"], a["alpha"], a["every"])
+    st = _moer._lib.moer_balance_step(a["bias"], a["counts"], a["L"], a["N"], a["stride"],
+                                      ctypes.byref(cfg) if a["cfg"] else None, a["loads"],
+                                      a["calls"], None)
+    msg = _moer._lib.moer_last_error().decode()
+    assert st == moer.MOER_EINVAL and frag in msg, msg
+
+
+def test_balance_monitor_alarms_against_oracle_stats():
+    import numpy as np
+
+    import oracle
+
+    mon = moer.BalanceMonitor(8, cv_limit=0.2, hot_margin=0.5, persist=2)
+    balanced = np.full(8, 64, np.int32)
+    hot = np.array([200, 40, 40, 40, 40, 56, 48, 48], np.int32)   # expert 0 at 3.1x the mean
+    assert mon.observe(balanced) == []
+    a1 = mon.observe(hot)
+    cv = oracle.load_stats(hot)["cv"]
+    assert a1 == [("spread", pytest.approx(cv, rel=1e-12))]
+    a2 = mon.observe(hot)
+    assert ("hot", 0, 2) in a2 and all(a[0] != "hot" or a[1] == 0 for a in a2)
+    assert mon.observe(balanced) == [] and mon.streak[0] == 0
+    # the spread limit sits exactly at the pages' 20 %
+    c = np.array([120, 80, 100, 100], np.int32)   # std/mean = sqrt(200)/100 = 0.141
+    assert moer.BalanceMonitor(4).observe(c) == []
+    assert oracle.load_stats(c)["cv"] < 0.2

@@ -97,12 +97,15 @@ def test_scores_mode_bit_exact_ragged(wl):
     _scores_case(wl, seed=7)
 
 
-def _hidden_case(wl, seed_note, sample=None, check_h=True):
+def _hidden_case(wl, seed_note, sample=None, check_h=True, bias_mode="score", bias=None):
     inp = workloads.make_inputs(wl)
     x, W, b, off = inp["x"], inp["W"], inp["bias"], inp["offset"]
+    if bias is not None:
+        b = bias
     out = moer.route(x.to(DEV), W.to(DEV), K=wl.K, score_fn=wl.score_fn, n_groups=wl.n_groups,
                      topk_groups=wl.topk_groups, n_shared=wl.n_shared, bias=b.to(DEV),
-                     logit_offset=None if off is None else off.to(DEV), want_h=True)
+                     logit_offset=None if off is None else off.to(DEV), want_h=True,
+                     bias_mode=bias_mode)
     torch.cuda.synchronize()
     worst_dh, n_diff = 0.0, 0
     for l in range(wl.n_layers):
@@ -110,7 +113,7 @@ def _hidden_case(wl, seed_note, sample=None, check_h=True):
         xs = x[l][torch.from_numpy(rows)].float().numpy()
         ref = oracle.route(x=xs, W=W[l].float().numpy(), offset=None if off is None else off.numpy(),
                            bias=b[l].numpy(), K=wl.K, score_fn=wl.score_fn, n_groups=wl.n_groups,
-                           topk_groups=wl.topk_groups, n_shared=wl.n_shared)
+                           topk_groups=wl.topk_groups, n_shared=wl.n_shared, bias_mode=bias_mode)
         gh = _np(out["h"][l]).astype(np.float64)
         dh = np.abs(gh[rows] - ref["h"]).max()
         worst_dh = max(worst_dh, dh)
@@ -411,3 +414,97 @@ def test_collapse_balancing_lockstep():
         imb.append(oracle.load_stats(ref["counts"][:wl.N])["imbalance"])
     say(f"  imbalance round 0 {imb[0]:.2f} -> round 99 {imb[-1]:.2f}")
     assert imb[-1] < imb[0]
+
+
+# ------------------------------------------- balancing-rule variants
+@pytest.mark.parametrize("wl", [
+    workloads.scaled(WL["mixtral_top2"], T=600),
+    workloads.scaled(WL["dsv3_group"], T=500),
+    workloads.scaled(WL["collapse_balance"], T=300),
+    workloads.scaled(WL["decode_layers"], n_layers=3, T=70),
+], ids=lambda w: f"{w.name}-T{w.T}-L{w.n_layers}")
+def test_logit_space_bias_hidden_mode(wl):
+    # The dailyaiworld controller's reading: the bias joins the logits, and
+    # scores, selection, weights and entropy all come from h + b. A bias of
+    # +-0.5 (larger than the score-space one) makes the shift visible.
+    say(f"[logit bias] {wl}")
+    g = torch.Generator().manual_seed(31)
+    b = ((torch.rand(wl.n_layers, wl.N, generator=g) * 2 - 1) * 0.5).float()
+    _hidden_case(wl, wl.name + "/logit", bias_mode="logit", bias=b)
+
+
+BALANCE_CFGS = [
+    dict(rule="sign", step=1e-3, alpha=1.0, every=1),
+    dict(rule="proportional", step=0.05, alpha=1.0, every=1),
+    dict(rule="sign", step=2e-3, alpha=0.25, every=3),
+    dict(rule="proportional", step=0.05, alpha=0.1, every=2),
+]
+
+
+@pytest.mark.parametrize("cfg", BALANCE_CFGS, ids=lambda c: "-".join(str(v) for v in c.values()))
+@pytest.mark.parametrize("L,N,stride", [(3, 256, 256), (2, 8, 8), (4, 256, 257)])
+def test_balance_step_bit_exact_over_calls(cfg, L, N, stride):
+    say(f"[balance step] {cfg} L={L} N={N}")
+    g = np.random.default_rng(N + L)
+    b0 = g.uniform(-0.01, 0.01, (L, N)).astype(np.float32)
+    bias = torch.from_numpy(b0).to(DEV)
+    state = moer.BalanceState(L, N)
+    ref = [dict(b=b0[l].copy(), loads=np.zeros(N, np.float32), calls=0) for l in range(L)]
+    for call in range(7):
+        counts = g.integers(0, 900, (L, stride)).astype(np.int32)
+        if call == 4:
+            counts[:, :N] = 512   # a balanced call: the rules leave the bias alone
+        moer.balance_step(bias, torch.from_numpy(counts).to(DEV), state=state, **cfg)
+        torch.cuda.synchronize()
+        for l in range(L):
+            r = ref[l]
+            r["b"], r["loads"], r["calls"] = oracle.balance_step(
+                r["b"], counts[l, :N], rule=oracle.SIGN if cfg["rule"] == "sign" else
+                oracle.PROPORTIONAL, step=cfg["step"], alpha=cfg["alpha"], every=cfg["every"],
+                loads=r["loads"], calls=r["calls"])
+            assert (_np(bias[l]) == r["b"]).all(), f"call {call} layer {l}: bias"
+            assert (_np(state.loads[l]) == r["loads"]).all(), f"call {call} layer {l}: loads"
+            assert int(state.calls[l]) == r["calls"]
+
+
+def test_balance_step_sign_equals_bias_update():
+    g = np.random.default_rng(5)
+    counts = torch.from_numpy(g.integers(300, 700, (2, 257)).astype(np.int32)).to(DEV)
+    b = torch.from_numpy(g.uniform(-0.01, 0.01, (2, 256)).astype(np.float32)).to(DEV)
+    a, c = b.clone(), b.clone()
+    moer.balance_step(a, counts, rule="sign", step=1e-3)
+    moer.bias_update(c, counts, 1e-3)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c)
+
+
+def test_dailyaiworld_controller_loop():
+    # The listing's controller run for 12 batches on the collapse workload
+    # (celebrity experts): logit-space bias, proportional update with decay
+    # 0.05. Each step is checked against the oracle on the GPU's own counts
+    # (selections within the near-tie rule); the celebrities' bias must fall.
+    wl = workloads.scaled(WL["collapse_balance"], T=1024, d=1024)
+    say(f"[controller] {wl}")
+    W, b0, off, _ = workloads.make_router(wl)
+    bias = torch.zeros(1, wl.N, device=DEV)
+    b_ref = np.zeros(wl.N, np.float32)
+    for it in range(12):
+        x = workloads.make_hidden(wl, seed=2000 + it)
+        out = moer.route(x.to(DEV), W.to(DEV), K=wl.K, n_groups=wl.n_groups,
+                         topk_groups=wl.topk_groups, bias=bias, logit_offset=off.to(DEV),
+                         bias_mode="logit", want_h=True)
+        torch.cuda.synchronize()
+        ref = oracle.route(x=x[0].float().numpy(), W=W[0].float().numpy(), offset=off.numpy(),
+                           bias=b_ref, K=wl.K, score_fn=wl.score_fn, n_groups=wl.n_groups,
+                           topk_groups=wl.topk_groups, bias_mode="logit")
+        gi = _np(out["topk_idx"][0])
+        same = (gi == ref["idx"]).all(axis=1)
+        assert np.all(same | (ref["gap"] < 1e-3)), f"batch {it}"
+        counts = out["counts"]
+        moer.balance_step(bias, counts, rule="proportional", step=0.05)
+        torch.cuda.synchronize()
+        b_ref, _, _ = oracle.balance_step(b_ref, _np(counts[0])[:wl.N], rule=oracle.PROPORTIONAL,
+                                          step=0.05)
+        assert (_np(bias[0]) == b_ref).all(), f"batch {it}: bias"
+    celeb = list(wl.celebrities)
+    assert (b_ref[celeb] < 0).all()

@@ -13,6 +13,8 @@ from ._moer import (  # noqa: F401
     LIB_PATH,
     LOAD_STATS_FIELDS,
     MOER_BF16,
+    MOER_BIAS_LOGIT,
+    MOER_BIAS_SCORE,
     MOER_EHIP,
     MOER_EINVAL,
     MOER_EUNSUPPORTED,
@@ -24,14 +26,18 @@ from ._moer import (  # noqa: F401
     MOER_MAX_EXPERTS,
     MOER_MAX_SLOTS,
     MOER_OK,
+    MOER_RULE_PROPORTIONAL,
+    MOER_RULE_SIGN,
     MOER_SIGMOID,
     MOER_SOFTMAX,
+    MoerBalanceCfg,
     MoerError,
     MoerRouteDesc,
     PreparedRoute,
     decode_load_stats,
     make_desc,
     moer_abi_version,
+    moer_balance_step,
     moer_balanced_indices,
     moer_bias_update,
     moer_combine,
@@ -43,6 +49,8 @@ from ._moer import (  # noqa: F401
 )
 
 _SCORE_FN = {"softmax": MOER_SOFTMAX, "sigmoid": MOER_SIGMOID}
+_BIAS_MODE = {"score": MOER_BIAS_SCORE, "logit": MOER_BIAS_LOGIT}
+_RULE = {"sign": MOER_RULE_SIGN, "proportional": MOER_RULE_PROPORTIONAL}
 
 
 def _layers(t, rank):
@@ -53,7 +61,7 @@ def _layers(t, rank):
 def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups=1, n_shared=0,
           bias=None, logit_offset=None, scores=None, idx_in=None, N=None, want_h=False,
           want_inv_perm=True, want_entropy=True, want_load_stats=False, bias_update=None,
-          bias_update_u=1e-3, workspace=None, stream=None):
+          bias_update_u=1e-3, bias_mode="score", workspace=None, stream=None):
     """Route a batch; returns a dict of device tensors, each with a leading
     layer dimension L.
 
@@ -62,6 +70,9 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
     want_load_stats adds the raw load-statistics records ("load_stats", uint8
     [L,64]); bias_update [L,N] fp32 (may be `bias` itself) gets the sign-step
     update with step bias_update_u from this call's counts, in place.
+    bias_mode "score" adds the bias to the scores for the selection only;
+    "logit" (hidden-state input) adds it to the logits, so the weights and
+    entropies come from the compensated scores too.
     """
     x, w_gate = _layers(x, 3), _layers(w_gate, 3)
     scores, idx_in, bias = _layers(scores, 3), _layers(idx_in, 3), _layers(bias, 2)
@@ -78,7 +89,7 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
     Kt, Nb = K + n_shared, N + n_shared
     desc = make_desc(n_layers=L, T=T, d=d, N=N, K=K, n_groups=n_groups, topk_groups=topk_groups,
                      n_shared=n_shared, score_fn=_SCORE_FN.get(score_fn, score_fn), dtype=dtype,
-                     input=mode)
+                     input=mode, bias_mode=_BIAS_MODE.get(bias_mode, bias_mode))
     i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
     out = {"counts": torch.empty(L, Nb, **i32), "offsets": torch.empty(L, Nb + 1, **i32),
            "perm": torch.empty(L, T * Kt, **i32)}
@@ -188,3 +199,61 @@ class HotspotRecorder:
             for row in m:
                 f.write(",".join(str(v) for v in row) + "\n")
         return m
+
+
+class BalanceState:
+    """Caller-owned state of moer_balance_step for L layers of N experts:
+    the moving-average loads and the per-layer call counters (zeroed)."""
+
+    def __init__(self, n_layers, N, device="cuda"):
+        self.loads = torch.zeros(n_layers, N, dtype=torch.float32, device=device)
+        self.calls = torch.zeros(n_layers, dtype=torch.int32, device=device)
+
+
+def balance_step(bias, counts, *, rule="sign", step=1e-3, alpha=1.0, every=1, state=None,
+                 stream=None):
+    """One balancing step on bias [L, N] (in place) from counts [L, stride]:
+    rule "sign" (b += step*sign(mean - load)) or "proportional"
+    (b -= step*(load - mean)/mean), loads smoothed by a moving average of
+    weight alpha, the rule applied every `every` calls (state: a
+    BalanceState, needed when alpha < 1 or every > 1)."""
+    bias2, counts2 = _layers(bias, 2), _layers(counts, 2)
+    cfg = MoerBalanceCfg(_RULE.get(rule, rule), float(step), float(alpha), int(every))
+    moer_balance_step(bias2, counts2, bias2.shape[0], bias2.shape[1], counts2.shape[1], cfg,
+                      None if state is None else state.loads,
+                      None if state is None else state.calls, stream)
+    return bias
+
+
+class BalanceMonitor:
+    """Host-side balance alarms from per-batch expert counts (hotdry,
+    deployment section: keep the spread of expert activation frequency
+    within 20 % of the mean; an expert whose load stays more than 50 % above
+    the mean calls for a replica or a different bias step).
+
+    ``observe(counts)`` takes one batch's counts [N] (host integers) and
+    returns the alarms raised: ("spread", cv) when the coefficient of
+    variation exceeds ``cv_limit``, and ("hot", expert, batches) for each
+    expert above (1 + hot_margin) x mean for ``persist`` consecutive
+    batches."""
+
+    def __init__(self, N, cv_limit=0.20, hot_margin=0.50, persist=3):
+        self.N, self.cv_limit, self.hot_margin, self.persist = N, cv_limit, hot_margin, persist
+        self.streak = [0] * N
+
+    def observe(self, counts):
+        c = [int(v) for v in list(counts)[:self.N]]
+        total = sum(c)
+        alarms = []
+        if total == 0:
+            self.streak = [0] * self.N
+            return alarms
+        mean = total / self.N
+        cv = (sum((v - mean) ** 2 for v in c) / self.N) ** 0.5 / mean
+        if cv > self.cv_limit:
+            alarms.append(("spread", cv))
+        for e, v in enumerate(c):
+            self.streak[e] = self.streak[e] + 1 if v > (1.0 + self.hot_margin) * mean else 0
+            if self.streak[e] >= self.persist:
+                alarms.append(("hot", e, self.streak[e]))
+        return alarms

@@ -17,17 +17,25 @@ MOER_OK, MOER_EINVAL, MOER_EUNSUPPORTED, MOER_EWORKSPACE, MOER_EHIP = range(5)
 MOER_SOFTMAX, MOER_SIGMOID = 0, 1
 MOER_BF16, MOER_F32 = 0, 1
 MOER_IN_HIDDEN, MOER_IN_SCORES, MOER_IN_INDICES = 0, 1, 2
+MOER_BIAS_SCORE, MOER_BIAS_LOGIT = 0, 1
+MOER_RULE_SIGN, MOER_RULE_PROPORTIONAL = 0, 1
 MOER_MAX_EXPERTS, MOER_MAX_SLOTS = 256, 16
 
 EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats", "moer_bias_update",
-            "moer_dispatch", "moer_combine", "moer_balanced_indices", "moer_hotspot_accumulate",
+            "moer_balance_step", "moer_dispatch", "moer_combine", "moer_balanced_indices",
+            "moer_hotspot_accumulate",
             "moer_status_str", "moer_last_error", "moer_abi_version")
 
 
 class MoerRouteDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layers", "T", "d", "N", "K", "n_groups", "topk_groups", "n_shared",
-                 "score_fn", "dtype", "input")]
+                 "score_fn", "dtype", "input", "bias_mode")]
+
+
+class MoerBalanceCfg(ctypes.Structure):
+    _fields_ = [("rule", ctypes.c_int32), ("step", ctypes.c_float), ("alpha", ctypes.c_float),
+                ("every", ctypes.c_int32)]
 
 
 class MoerRouteIO(ctypes.Structure):
@@ -76,6 +84,8 @@ def _load():
     lib.moer_dispatch.restype = ctypes.c_int
     lib.moer_combine.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, ctypes.c_int, P]
     lib.moer_combine.restype = ctypes.c_int
+    lib.moer_balance_step.argtypes = [P, P, i32, i32, i32, ctypes.POINTER(MoerBalanceCfg), P, P, P]
+    lib.moer_balance_step.restype = ctypes.c_int
     lib.moer_balanced_indices.argtypes = [P, i32, i32, i32, i32, i32, i32, P]
     lib.moer_balanced_indices.restype = ctypes.c_int
     lib.moer_hotspot_accumulate.argtypes = [P, P, i32, i32, i32, P]
@@ -121,9 +131,10 @@ def moer_abi_version():
 
 
 def make_desc(*, T, N, K, n_layers=1, d=0, n_groups=1, topk_groups=1, n_shared=0,
-              score_fn=MOER_SIGMOID, dtype=MOER_BF16, input=MOER_IN_HIDDEN):
+              score_fn=MOER_SIGMOID, dtype=MOER_BF16, input=MOER_IN_HIDDEN,
+              bias_mode=MOER_BIAS_SCORE):
     return MoerRouteDesc(n_layers, T, d, N, K, n_groups, topk_groups, n_shared, score_fn, dtype,
-                         input)
+                         input, bias_mode)
 
 
 def moer_route_workspace_bytes(desc):
@@ -232,6 +243,20 @@ def moer_combine(expert_out, w, inv_perm, n_layers, T, Kt, d, y, stream=None):
     _check(_lib.moer_combine(_ptr(expert_out), _DTYPE_CODE[expert_out.dtype], _ptr(w),
                              _ptr(inv_perm), n_layers, T, Kt, d, _ptr(y), _DTYPE_CODE[y.dtype],
                              _stream(stream)))
+
+
+def moer_balance_step(bias, counts, n_layers, N, stride, cfg, loads=None, calls=None,
+                      stream=None):
+    """cfg: MoerBalanceCfg; loads [L,N] fp32 and calls [L] int32 are the
+    caller's state (device tensors or None)."""
+    if bias.dtype != torch.float32 or counts.dtype != torch.int32:
+        raise TypeError("bias must be float32 and counts int32")
+    if loads is not None and loads.dtype != torch.float32:
+        raise TypeError("loads must be float32")
+    if calls is not None and calls.dtype != torch.int32:
+        raise TypeError("calls must be int32")
+    _check(_lib.moer_balance_step(_ptr(bias), _ptr(counts), n_layers, N, stride,
+                                  ctypes.byref(cfg), _ptr(loads), _ptr(calls), _stream(stream)))
 
 
 def moer_balanced_indices(idx, n_layers, T, K, N, n_shared=0, first=0, stream=None):

@@ -112,6 +112,10 @@ moer_status validate_desc(const moer_route_desc* d) {
     if ((long long)d->T * d->d >= (1LL << 40) || (long long)d->N * d->d >= (1LL << 40))
       return fail(MOER_EINVAL, "hidden size too large");
   }
+  if (d->bias_mode != MOER_BIAS_SCORE && d->bias_mode != MOER_BIAS_LOGIT)
+    return fail(MOER_EINVAL, "unknown bias_mode %d", d->bias_mode);
+  if (d->bias_mode == MOER_BIAS_LOGIT && d->input != MOER_IN_HIDDEN)
+    return fail(MOER_EINVAL, "a logit-space bias needs HIDDEN input (the logits)");
   if (d->input != MOER_IN_INDICES && selection_path(*d) == 0)
     return fail(MOER_EUNSUPPORTED,
                 "group size %d with N=%d: these kernels need N/n_groups to be a power of two "
@@ -242,6 +246,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     a.n_shared = d.n_shared;
     a.score_fn = d.score_fn;
     a.apply_score = hidden ? 1 : 0;
+    a.bias_logit = d.bias_mode == MOER_BIAS_LOGIT ? 1 : 0;
     if (path == 1) {
       a.cnt = cnt;
       a.segsum = segsum;
@@ -370,6 +375,29 @@ moer_status moer_hotspot_accumulate(int64_t* hot, const int32_t* counts, int32_t
   hipError_t he = moer::launch_hotspot_accumulate(hot, counts, n_layers, N, stride,
                                                   static_cast<hipStream_t>(stream));
   if (he != hipSuccess) return fail(MOER_EHIP, "hotspot launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+moer_status moer_balance_step(float* bias, const int32_t* counts, int32_t n_layers, int32_t N,
+                              int32_t stride, const moer_balance_cfg* cfg, float* loads,
+                              int32_t* calls, void* stream) {
+  if (bias == nullptr || counts == nullptr || cfg == nullptr)
+    return fail(MOER_EINVAL, "bias, counts and cfg are required");
+  if (n_layers < 1 || N < 1 || N > MOER_MAX_EXPERTS || stride < N)
+    return fail(MOER_EINVAL, "need n_layers >= 1, 1 <= N <= %d, stride >= N", MOER_MAX_EXPERTS);
+  if (cfg->rule != MOER_RULE_SIGN && cfg->rule != MOER_RULE_PROPORTIONAL)
+    return fail(MOER_EINVAL, "unknown rule %d", cfg->rule);
+  if (!(cfg->step >= 0.f) || cfg->step == __builtin_inff())
+    return fail(MOER_EINVAL, "step must be finite and >= 0");
+  if (!(cfg->alpha > 0.f && cfg->alpha <= 1.f)) return fail(MOER_EINVAL, "alpha must be in (0, 1]");
+  if (cfg->every < 1) return fail(MOER_EINVAL, "every must be >= 1");
+  if (cfg->alpha < 1.f && loads == nullptr)
+    return fail(MOER_EINVAL, "alpha < 1 needs the loads state");
+  if (cfg->every > 1 && calls == nullptr) return fail(MOER_EINVAL, "every > 1 needs the calls state");
+  hipError_t he = moer::launch_balance_step(bias, counts, n_layers, N, stride, cfg->rule, cfg->step,
+                                            cfg->alpha, cfg->every, loads, calls,
+                                            static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(MOER_EHIP, "balance_step launch: %s", hipGetErrorString(he));
   return ok();
 }
 

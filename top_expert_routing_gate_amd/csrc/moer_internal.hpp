@@ -30,6 +30,7 @@ struct ScoreArgs {
   uint16_t* cnt;          // [L][Nb][nsb] expert counts per 64-token block, or nullptr
   int32_t* segsum;        // [L][nseg][Nb] += the block counts (zero beforehand), or nullptr
   int T, N, K, G, Gk, n_shared, score_fn, apply_score, nsplit;
+  int bias_logit;         // 1: the bias is added to the logits (with the offset)
 };
 
 struct LayoutArgs {
@@ -77,6 +78,12 @@ hipError_t launch_dispatch(const void* x, int64_t row_bytes, int L, int T, int K
                            const int32_t* inv_perm, void* out, hipStream_t s);
 hipError_t launch_combine(const void* eo, int eo_bf16, const float* w, const int32_t* inv_perm,
                           int L, int T, int Kt, int d, void* y, int y_bf16, hipStream_t s);
+
+// Balancing step with rule, moving-average loads and period (one
+// workgroup per layer).
+hipError_t launch_balance_step(float* bias, const int32_t* counts, int L, int N, int stride,
+                               int rule, float step, float alpha, int every, float* loads,
+                               int32_t* calls, hipStream_t s);
 
 // Forcible-balance expert ids and hotspot accumulation (elementwise).
 hipError_t launch_balanced_indices(int32_t* idx, int L, int T, int K, int N, int n_shared,

@@ -170,7 +170,9 @@ __device__ __forceinline__ unsigned order_bits(float key, bool all_positive) {
 
 // The lane's per-expert constants of a layer, loaded once (and early, so
 // their latency hides under the affinity loads): selection bias and logit
-// offset of experts e0 .. e0+EPL-1 (0 past N or when absent).
+// offset of experts e0 .. e0+EPL-1 (0 past N or when absent). With a
+// logit-space bias the bias is folded into the offset (offset + b, one fp32
+// rounding) and the selection bias is zero.
 template <int EPL>
 struct LaneConsts {
   float bias[EPL];
@@ -196,6 +198,13 @@ __device__ __forceinline__ void load_lane_consts(const ScoreArgs& a, int layer, 
   };
   fill(b, c.bias);
   fill(o, c.offset);
+  if (a.bias_logit) {  // the bias joins the logit offset; the keys are the scores
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      c.offset[j] += c.bias[j];
+      c.bias[j] = 0.f;
+    }
+  }
 }
 
 // Route token t of `layer` (live = t < T). v: the lane's EPL affinities (or
@@ -223,7 +232,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   }
   // 1. affinities (+ offset) and scores
   if (MODE != kGiven) {
-    if (a.offset != nullptr) {
+    if (a.offset != nullptr || (a.bias_logit && a.bias != nullptr)) {
 #pragma unroll
       for (int j = 0; j < EPL; ++j) v[j] += lc.offset[j];
     }

@@ -60,11 +60,19 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
   const float NEG_INF = -__builtin_inff();
 
   float bias_r[E];
+  float off_r[E];
   float col[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const int e = lane * E + j;
     bias_r[j] = (a.bias != nullptr && e < N) ? a.bias[(size_t)layer * N + e] : 0.f;
+    // logit-space bias: added to the logits with the offset (offset + b, one
+    // fp32 rounding, as in the row kernel); the keys are then the scores
+    off_r[j] = (a.offset != nullptr && e < N) ? a.offset[e] : 0.f;
+    if (a.bias_logit) {
+      off_r[j] += bias_r[j];
+      bias_r[j] = 0.f;
+    }
     col[j] = 0.f;
   }
 
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
       if (e < N) {
         acc = a.in[row_off + e];
         for (int sp = 1; sp < a.nsplit; ++sp) acc += a.in[sp * split_stride + row_off + e];
-        if (a.offset != nullptr) acc += a.offset[e];
+        if (a.offset != nullptr || (a.bias_logit && a.bias != nullptr)) acc += off_r[j];
         if (a.h_out != nullptr) a.h_out[row_off + e] = acc;
       }
       v[j] = acc;
