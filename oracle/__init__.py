@@ -16,8 +16,10 @@ from .api import (  # noqa: F401
     balanced_indices,
     bias_update,
     build_oracle,
+    capacity_route,
     combine,
     dispatch,
+    expert_capacity,
     hotspot_accumulate,
     layout,
     load_stats,

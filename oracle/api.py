@@ -58,6 +58,8 @@ def _load():
         lib.moero_scores.argtypes = [P, i32, i32, i32, P]
         lib.moero_select.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, P]
         lib.moero_select.restype = ctypes.c_int
+        lib.moero_capacity_route.argtypes = [ctypes.POINTER(_Cfg), P, P, P, i32, P, P, P, P]
+        lib.moero_capacity_route.restype = ctypes.c_int
         lib.moero_agg_entropy.argtypes = [P, i32, i32]
         lib.moero_agg_entropy.restype = ctypes.c_double
         lib.moero_layout.argtypes = [P, i32, i32, i32, P, P, P, P]
@@ -122,6 +124,30 @@ def select(s32, s64, bias, K, n_groups=1, topk_groups=1, n_shared=0):
     if rc != 0:
         raise ValueError("oracle: invalid routing configuration")
     return idx, w, H, gap
+
+
+def expert_capacity(T, K, N, factor="1.25"):
+    """ceil(factor * T * K / N) in exact rational arithmetic."""
+    from fractions import Fraction
+    q = Fraction(factor) * T * K / N
+    return -((-q.numerator) // q.denominator)
+
+
+def capacity_route(s32, s64, bias, K, cap, n_groups=1, topk_groups=1, n_shared=0):
+    """Capacity-limited routing. Returns idx [T,Kt] int32 (-1 = dropped),
+    w [T,Kt] f32, and the numbers of rerouted and dropped slots."""
+    s32 = _c(s32, np.float32); s64 = _c(s64, np.float64); bias = _c(bias, np.float32)
+    T, N = s32.shape
+    Kt = K + n_shared
+    cfg = _Cfg(T, N, K, n_groups, topk_groups, n_shared)
+    idx = np.empty((T, Kt), np.int32)
+    w = np.empty((T, Kt), np.float32)
+    rr, dr = ctypes.c_int64(), ctypes.c_int64()
+    rc = _load().moero_capacity_route(ctypes.byref(cfg), _p(s32), _p(s64), _p(bias), int(cap),
+                                      _p(idx), _p(w), ctypes.byref(rr), ctypes.byref(dr))
+    if rc != 0:
+        raise ValueError("oracle: invalid routing configuration")
+    return idx, w, rr.value, dr.value
 
 
 def agg_entropy(s64):

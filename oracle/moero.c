@@ -110,6 +110,50 @@ static int cfg_valid(const moero_cfg* c) {
   return 1;
 }
 
+/* Steps 1-3 of the per-token decision (see moero_select): the biased
+ * keys, the group-limited eligibility, and the eligible experts ranked by
+ * (key descending, id ascending) into cand[0..n). Returns n; lowers
+ * *margin to the gap between the Gk-th and the next group score. */
+static int32_t rank_token(const float* st, const float* bias, int32_t N, int32_t G, int32_t Gk,
+                          ranked* cand, ranked* grp, ranked* mem, float* key, char* kept,
+                          double* margin) {
+  const int32_t gsz = N / G;
+  /* 1. biased keys */
+  for (int32_t e = 0; e < N; ++e) {
+    volatile float k = st[e] + (bias ? bias[e] : 0.0f);
+    key[e] = k + 0.0f;
+  }
+  /* 2. group-limited eligibility */
+  if (G > 1) {
+    for (int32_t g = 0; g < G; ++g) {
+      for (int32_t j = 0; j < gsz; ++j) {
+        mem[j].v = key[g * gsz + j];
+        mem[j].id = g * gsz + j;
+      }
+      qsort(mem, (size_t)gsz, sizeof(ranked), by_value_desc_id_asc);
+      volatile float gs = mem[0].v + mem[1].v;
+      grp[g].v = gs + 0.0f;
+      grp[g].id = g;
+    }
+    qsort(grp, (size_t)G, sizeof(ranked), by_value_desc_id_asc);
+    memset(kept, 0, (size_t)G);
+    for (int32_t r = 0; r < Gk; ++r) kept[grp[r].id] = 1;
+    if (Gk < G) {
+      double dg = (double)grp[Gk - 1].v - (double)grp[Gk].v;
+      if (dg < *margin) *margin = dg;
+    }
+  } else {
+    kept[0] = 1;
+  }
+  /* 3. eligible experts, ranked */
+  int32_t n_el = 0;
+  for (int32_t e = 0; e < N; ++e) {
+    if (kept[e / gsz]) { cand[n_el].v = key[e]; cand[n_el].id = e; ++n_el; }
+  }
+  qsort(cand, (size_t)n_el, sizeof(ranked), by_value_desc_id_asc);
+  return n_el;
+}
+
 /* Per-token routing decision.
  *  1. key_e = s_e + b_e in fp32 ([P2] auxiliary-loss-free balancing: the
  *     bias is added to the affinity score for the routing decision only);
@@ -154,39 +198,7 @@ int moero_select(const moero_cfg* cfg, const float* s32, const double* s64,
         const float* st = s32 + (size_t)t * N;
         const double* sd = s64 + (size_t)t * N;
         double margin = INFINITY;
-        /* 1. biased keys */
-        for (int32_t e = 0; e < N; ++e) {
-          volatile float k = st[e] + (bias ? bias[e] : 0.0f);
-          key[e] = k + 0.0f;
-        }
-        /* 2. group-limited eligibility */
-        if (G > 1) {
-          for (int32_t g = 0; g < G; ++g) {
-            for (int32_t j = 0; j < gsz; ++j) {
-              mem[j].v = key[g * gsz + j];
-              mem[j].id = g * gsz + j;
-            }
-            qsort(mem, (size_t)gsz, sizeof(ranked), by_value_desc_id_asc);
-            volatile float gs = mem[0].v + mem[1].v;
-            grp[g].v = gs + 0.0f;
-            grp[g].id = g;
-          }
-          qsort(grp, (size_t)G, sizeof(ranked), by_value_desc_id_asc);
-          memset(kept, 0, (size_t)G);
-          for (int32_t r = 0; r < Gk; ++r) kept[grp[r].id] = 1;
-          if (Gk < G) {
-            double dg = (double)grp[Gk - 1].v - (double)grp[Gk].v;
-            if (dg < margin) margin = dg;
-          }
-        } else {
-          kept[0] = 1;
-        }
-        /* 3. top-K among eligible experts */
-        int32_t n_el = 0;
-        for (int32_t e = 0; e < N; ++e) {
-          if (kept[e / gsz]) { cand[n_el].v = key[e]; cand[n_el].id = e; ++n_el; }
-        }
-        qsort(cand, (size_t)n_el, sizeof(ranked), by_value_desc_id_asc);
+        const int32_t n_el = rank_token(st, bias, N, G, Gk, cand, grp, mem, key, kept, &margin);
         for (int32_t k = 0; k + 1 < K; ++k) {
           double dk = (double)cand[k].v - (double)cand[k + 1].v;
           if (dk < margin) margin = dk;
@@ -215,6 +227,115 @@ int moero_select(const moero_cfg* cfg, const float* s32, const double* s64,
     free(cand); free(grp); free(mem); free(key); free(kept);
   }
   return failed ? -1 : 0;
+}
+
+/* Capacity-limited routing ([P1] production testing: a hard per-expert
+ * token capacity, 1.25 x T*K/N in the page's setting; tokens beyond it go
+ * to their next candidate experts). Read here as rounds of proposals:
+ *  - every token's candidates are its eligible experts in decision order
+ *    (steps 1-3 of moero_select); round 0 proposes its top-K (slot k ->
+ *    candidate k);
+ *  - in each round an expert accepts that round's proposals in (token,
+ *    slot) order while it holds fewer than `cap` assignments, and rejects
+ *    the rest; accepted assignments are never revisited;
+ *  - a rejected slot proposes the token's next unused candidate (a token's
+ *    rejected slots take them in slot order) in the next round, or is
+ *    dropped (id -1, weight 0) when none is left;
+ *  - rounds repeat until nothing is pending.
+ * Slot k keeps its position; shared slots are not limited (ids N+j,
+ * weight 1). Weights are the placed routed slots' unbiased scores
+ * renormalised (fp64, stored as fp32; 1/n_placed when they sum to 0).
+ * Writes idx [T][Kt], w [T][Kt] (either may be NULL), and the numbers of
+ * slots placed on another expert than their first proposal and of slots
+ * dropped. Returns -1 on an invalid configuration. */
+int moero_capacity_route(const moero_cfg* cfg, const float* s32, const double* s64,
+                         const float* bias, int32_t cap, int32_t* idx, float* w,
+                         int64_t* n_rerouted, int64_t* n_dropped) {
+  if (!cfg_valid(cfg)) return -1;
+  const int32_t T = cfg->T, N = cfg->N, K = cfg->K, G = cfg->n_groups;
+  const int32_t Gk = cfg->topk_groups, Kt = K + cfg->n_shared;
+  const int32_t gsz = N / G;
+  const int64_t A = (int64_t)T * K;
+  enum { PENDING = 0, ACCEPTED = 1, REJECTED = 2, DROPPED = 3 };
+  int32_t* list = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * (size_t)N);
+  int32_t* n_el = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t* prop = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A > 0 ? A : 1));
+  char* state = (char*)malloc((size_t)(A > 0 ? A : 1));
+  int32_t* held = (int32_t*)calloc((size_t)N, sizeof(int32_t));
+  ranked* cand = (ranked*)malloc(sizeof(ranked) * (size_t)N);
+  ranked* grp = (ranked*)malloc(sizeof(ranked) * (size_t)G);
+  ranked* mem = (ranked*)malloc(sizeof(ranked) * (size_t)gsz);
+  float* key = (float*)malloc(sizeof(float) * (size_t)N);
+  char* kept = (char*)malloc((size_t)G);
+  if (!list || !n_el || !next || !prop || !state || !held || !cand || !grp || !mem || !key ||
+      !kept)
+    return -1;
+  /* candidates; round 0 proposes the top-K */
+  for (int32_t t = 0; t < T; ++t) {
+    double margin = INFINITY;
+    n_el[t] = rank_token(s32 + (size_t)t * N, bias, N, G, Gk, cand, grp, mem, key, kept, &margin);
+    for (int32_t r = 0; r < n_el[t]; ++r) list[(size_t)t * N + r] = cand[r].id;
+    for (int32_t k = 0; k < K; ++k) {
+      prop[(size_t)t * K + k] = list[(size_t)t * N + k];
+      state[(size_t)t * K + k] = PENDING;
+    }
+    next[t] = K;
+  }
+  int64_t pending = A;
+  while (pending > 0) {
+    /* accept in (token, slot) order up to the capacity */
+    for (int64_t a = 0; a < A; ++a) {
+      if (state[a] != PENDING) continue;
+      const int32_t e = prop[a];
+      if (held[e] < cap) { held[e] += 1; state[a] = ACCEPTED; }
+      else state[a] = REJECTED;
+    }
+    /* rejected slots take the next candidates, in slot order per token */
+    pending = 0;
+    for (int64_t a = 0; a < A; ++a) {
+      if (state[a] != REJECTED) continue;
+      const int32_t t = (int32_t)(a / K);
+      if (next[t] < n_el[t]) {
+        prop[a] = list[(size_t)t * N + next[t]];
+        next[t] += 1;
+        state[a] = PENDING;
+        ++pending;
+      } else {
+        state[a] = DROPPED;
+      }
+    }
+  }
+  int64_t rerouted = 0, dropped = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    const double* sd = s64 + (size_t)t * N;
+    double z = 0.0;
+    int32_t placed = 0;
+    for (int32_t k = 0; k < K; ++k) {
+      const int64_t a = (int64_t)t * K + k;
+      if (state[a] == DROPPED) { ++dropped; continue; }
+      if (prop[a] != list[(size_t)t * N + k]) ++rerouted;
+      z += sd[prop[a]];
+      ++placed;
+    }
+    for (int32_t k = 0; k < K; ++k) {
+      const int64_t a = (int64_t)t * K + k;
+      const int dropped_slot = state[a] == DROPPED;
+      if (idx) idx[(size_t)t * Kt + k] = dropped_slot ? -1 : prop[a];
+      if (w)
+        w[(size_t)t * Kt + k] = dropped_slot ? 0.0f
+                                : (float)(z > 0.0 ? sd[prop[a]] / z : 1.0 / placed);
+    }
+    for (int32_t j = 0; j < cfg->n_shared; ++j) {
+      if (idx) idx[(size_t)t * Kt + K + j] = N + j;
+      if (w) w[(size_t)t * Kt + K + j] = 1.0f;
+    }
+  }
+  if (n_rerouted) *n_rerouted = rerouted;
+  if (n_dropped) *n_dropped = dropped;
+  free(list); free(n_el); free(next); free(prop); free(state); free(held);
+  free(cand); free(grp); free(mem); free(key); free(kept);
+  return 0;
 }
 
 /* [P1] compute_routing_entropy: average the routing distributions over the

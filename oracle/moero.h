@@ -77,6 +77,20 @@ int moero_select(const moero_cfg* cfg, const float* s32, const double* s64,
                  const float* bias, int32_t* idx, float* w, double* tok_H,
                  double* gap);
 
+/* Capacity-limited routing ([P1] production testing section: a hard token
+ * capacity per expert; the excess goes to secondary candidates). Rounds of
+ * proposals: round 0 proposes each token's top-K; each round, an expert
+ * accepts proposals in (token, slot) order while it holds fewer than cap;
+ * a rejected slot proposes the token's next eligible candidate (decision
+ * order of moero_select) in the next round, or is dropped (id -1, weight 0)
+ * when none is left. Slots keep their positions; shared slots are not
+ * limited. Weights: unbiased scores of the placed routed slots renormalised.
+ * Inputs as moero_select; outputs idx, w [T][Kt] (nullable), and the counts
+ * of rerouted and dropped slots. Returns -1 on an invalid configuration. */
+int moero_capacity_route(const moero_cfg* cfg, const float* s32, const double* s64,
+                         const float* bias, int32_t cap, int32_t* idx, float* w,
+                         int64_t* n_rerouted, int64_t* n_dropped);
+
 /* Aggregate routing entropy ([P1] Mathematics and compute_routing_entropy):
  * the entropy in bits of the batch-mean of the per-token distributions
  * q[t][e] = s[t][e] / sum_e s[t][e]. 0 for T == 0. */

@@ -36,7 +36,8 @@ MUTANTS = [
      "for (int32_t r = 1; r <= Gk && r < G; ++r) kept[grp[r].id] = 1;"),
     ("weights from biased keys", "for (int32_t k = 0; k < K; ++k) z += sd[cand[k].id];",
      "for (int32_t k = 0; k < K; ++k) z += cand[k].v;"),
-    ("shared slot weight", "w[(size_t)t * Kt + K + j] = 1.0f;", "w[(size_t)t * Kt + K + j] = 0.0f;"),
+    ("shared slot weight", "w[(size_t)t * Kt + K + j] = 1.0f;\n        }\n        /* 6.",
+     "w[(size_t)t * Kt + K + j] = 0.0f;\n        }\n        /* 6."),
     ("entropy in nats", "if (q > 0.0) H -= q * log2(q);", "if (q > 0.0) H -= q * log(q);"),
     ("aggregate of unnormalised scores", "mean[e] += sd[e] / z;", "mean[e] += sd[e];"),
     ("layout order within an expert",
@@ -85,6 +86,17 @@ MUTANTS = [
     ("period off by one", "if ((ncall + 1) % every == 0) {", "if (ncall % every == 0) {"),
     ("sign rule against the total", "const double diff = mean - (double)l[e];",
      "const double diff = total - (double)l[e];"),
+    ("capacity admits one more", "if (held[e] < cap) { held[e] += 1; state[a] = ACCEPTED; }",
+     "if (held[e] <= cap) { held[e] += 1; state[a] = ACCEPTED; }"),
+    ("capacity accepts latest tokens first",
+     "for (int64_t a = 0; a < A; ++a) {\n      if (state[a] != PENDING) continue;",
+     "for (int64_t a = A - 1; a >= 0; --a) {\n      if (state[a] != PENDING) continue;"),
+    ("rejected slots skip a candidate", "prop[a] = list[(size_t)t * N + next[t]];\n        next[t] += 1;",
+     "next[t] += 1;\n        prop[a] = list[(size_t)t * N + (next[t] < n_el[t] ? next[t] : next[t] - 1)];"),
+    ("dropped slots keep a weight", "w[(size_t)t * Kt + k] = dropped_slot ? 0.0f",
+     "w[(size_t)t * Kt + k] = dropped_slot ? 1.0f"),
+    ("reroute count of every placed slot", "if (prop[a] != list[(size_t)t * N + k]) ++rerouted;",
+     "++rerouted;"),
 ]
 
 

@@ -437,6 +437,99 @@ def test_bias_update_closed_form():
     assert (nb[counts < mean] > b[counts < mean]).all()
 
 
+# ------------------------------------ [P1] capacity-limited routing
+def test_expert_capacity_is_the_pages_formula():
+    # [P1] production testing: capacity = 1.25 x (batch x top_k / experts)
+    assert oracle.expert_capacity(16384, 8, 256) == 640
+    assert oracle.expert_capacity(64, 1, 4) == 20
+    assert oracle.expert_capacity(100, 3, 7) == 54     # 53.57... rounded up
+    assert oracle.expert_capacity(4096, 2, 8) == 1280
+
+
+def test_capacity_routing_hand_worked_examples():
+    # Every token ranks experts 0 > 1 > 2 > 3. K = 1, cap = 2: expert 0 keeps
+    # the first two tokens, the next two move to expert 1, and so on.
+    s = np.tile(np.array([0.875, 0.75, 0.5, 0.25], np.float32), (8, 1))
+    idx, w, rr, dr = oracle.capacity_route(s, s.astype(np.float64), None, 1, 2)
+    assert idx[:, 0].tolist() == [0, 0, 1, 1, 2, 2, 3, 3] and (w == 1).all()
+    assert (rr, dr) == (6, 0)
+    # K = 2, cap = 2, three tokens: tokens 0 and 1 fill experts 0 and 1; token
+    # 2's two rejected slots take its next candidates in slot order (2, 3).
+    idx, w, rr, dr = oracle.capacity_route(s[:3], s[:3].astype(np.float64), None, 2, 2)
+    assert idx.tolist() == [[0, 1], [0, 1], [2, 3]] and (rr, dr) == (2, 0)
+    assert np.allclose(w[2], [0.5 / 0.75, 0.25 / 0.75])
+    # cap = 1 with a shared slot: the third token finds every expert full or
+    # held and drops its second slot (weight 0, the first renormalised to 1)
+    s2 = np.tile(np.array([0.875, 0.75], np.float32), (3, 1))
+    idx, w, rr, dr = oracle.capacity_route(s2, s2.astype(np.float64), None, 1, 1, n_shared=1)
+    assert idx.tolist() == [[0, 2], [1, 2], [-1, 2]] and (rr, dr) == (1, 1)
+    assert w.tolist() == [[1, 1], [1, 1], [0, 1]]
+
+
+def _ranked_eligible(s32, bias, G, Gk):
+    """Eligible experts of each token in decision order, from the keys
+    directly (numpy): group score = sum of the two largest keys."""
+    key = (s32 + (0 if bias is None else bias)).astype(np.float32)
+    T, N = key.shape
+    gsz = N // G
+    out = []
+    for t in range(T):
+        kg = key[t].reshape(G, gsz)
+        top2 = np.sort(kg, axis=1)[:, ::-1][:, :2].sum(axis=1) if G > 1 else np.zeros(1)
+        groups = sorted(range(G), key=lambda g: (-top2[g], g))[:Gk]
+        el = [e for e in range(N) if e // gsz in groups]
+        out.append(sorted(el, key=lambda e: (-key[t, e], e)))
+    return out
+
+
+@pytest.mark.parametrize("T,N,K,G,Gk,cap", [(300, 16, 2, 1, 1, 40), (200, 16, 4, 4, 2, 55),
+                                            (500, 32, 4, 8, 4, 70), (64, 8, 3, 1, 1, 20),
+                                            (90, 12, 4, 3, 2, 31), (120, 16, 2, 4, 1, 12)])
+def test_capacity_routing_properties(T, N, K, G, Gk, cap):
+    g = np.random.default_rng(T + N + cap)
+    # skewed scores: a few popular experts overflow
+    s = g.random((T, N)).astype(np.float32)
+    s[:, :3] += 0.5
+    s = (s / 2).astype(np.float32)
+    bias = (g.integers(-8, 8, N) / 1024).astype(np.float32)
+    plain, pw, _, _ = oracle.select(s, s.astype(np.float64), bias, K, G, Gk)
+    idx, w, rr, dr = oracle.capacity_route(s, s.astype(np.float64), bias, K, cap, G, Gk)
+    ranked = _ranked_eligible(s, bias, G, Gk)
+    final = np.bincount(idx[idx >= 0], minlength=N)
+    assert final.max() <= cap
+    # round 0 is first come, first served: each expert keeps the earliest
+    # min(cap, demand) of its plain top-K assignments, at the same slot
+    for e in range(N):
+        ts, ks = np.nonzero(plain == e)
+        order = np.lexsort((ks, ts))
+        keep = order[:cap]
+        assert (idx[ts[keep], ks[keep]] == e).all()
+    n_rr = n_dr = 0
+    for t in range(T):
+        placed = [e for e in idx[t] if e >= 0]
+        assert len(set(placed)) == len(placed) and set(placed) <= set(ranked[t])
+        n_dr += K - len(placed)
+        n_rr += sum(1 for k in range(K) if idx[t, k] >= 0 and idx[t, k] != plain[t, k])
+        # no candidate ranked above the token's lowest placed expert was
+        # skipped while it had room: it is held by the token or full
+        if placed:
+            worst = max(ranked[t].index(e) for e in placed)
+            for e in ranked[t][:worst]:
+                assert e in placed or final[e] == cap
+        if len(placed) < K:   # dropped only once every candidate is held or full
+            assert all(e in placed or final[e] == cap for e in ranked[t])
+        z = sum(float(s[t, e]) for e in placed)
+        for k in range(K):
+            want = 0.0 if idx[t, k] < 0 else float(s[t, idx[t, k]]) / z
+            assert abs(w[t, k] - want) < 1e-6
+    assert (n_rr, n_dr) == (rr, dr)
+    assert rr > 0
+    # a capacity at or above the largest plain load changes nothing
+    big = int(np.bincount(plain.ravel(), minlength=N).max())
+    i2, w2, r2, d2 = oracle.capacity_route(s, s.astype(np.float64), bias, K, big, G, Gk)
+    assert (i2 == plain).all() and np.allclose(w2, pw) and (r2, d2) == (0, 0)
+
+
 # ----------------------------------------- [P1]/[P2] balancing-rule variants
 def test_balance_step_sign_rule_closed_form_and_equals_bias_update():
     g = np.random.default_rng(21)
