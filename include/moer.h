@@ -112,6 +112,11 @@ typedef struct {
   int32_t dtype;       /* moer_dtype of x and W_g (HIDDEN mode) */
   int32_t input;       /* moer_input */
   int32_t bias_mode;   /* moer_bias_mode (0 = MOER_BIAS_SCORE) */
+  int32_t capacity;    /* 0 = unlimited; else the most assignments a routed
+                          expert takes per layer (dailyaiworld, production
+                          testing: 1.25 x T*K/N, rounded up). Slots beyond it
+                          move to the token's next candidates, in rounds (see
+                          moer_route); HIDDEN or SCORES input */
 } moer_route_desc;
 
 /* Per-layer record written by moer_load_stats (device memory, 64 bytes). */
@@ -160,6 +165,9 @@ typedef struct {
                                 be the same buffer): the auxiliary-loss-free
                                 balancing step of one training iteration */
   float bias_update_u;       /* step u >= 0 for bias_update */
+  int32_t* cap_stats;        /* opt [L][2] with a capacity: slots placed on
+                                another expert than their first choice, and
+                                slots dropped (no candidate left) */
   void* ev_select_wait;      /* opt hipEvent_t: the selection (and everything
                                 after it) waits for this event, the gate GEMM
                                 does not. Lets a loop overlap the next batch's
@@ -186,6 +194,15 @@ size_t moer_route_workspace_bytes(const moer_route_desc* desc);
  *   agg_entropy = entropy (bits) of the mean over tokens of s / sum_e s
  * then the dispatch layout over Nb buckets (counts, offsets, perm,
  * inv_perm), stable in (token, slot) order within an expert.
+ * With desc->capacity = c > 0 the routed slots are then limited to c per
+ * expert, in rounds: round 0 is the top-K above; in every round an expert
+ * accepts that round's proposals in (token, slot) order while it holds
+ * fewer than c, and each rejected slot proposes its token's next eligible
+ * candidate (decision order; a token's rejected slots in slot order) in the
+ * next round, or is dropped (id -1, weight 0) when none is left. Slots keep
+ * their positions; the weights are renormalised over the placed routed
+ * slots; entropies are those of the scores; the layout, load statistics and
+ * bias update use the final ids.
  * Workspace: device memory of at least moer_route_workspace_bytes(desc)
  * bytes, any contents; it is clobbered. Returns MOER_OK or an error status. */
 moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io,

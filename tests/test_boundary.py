@@ -300,3 +300,20 @@ def test_balance_monitor_alarms_against_oracle_stats():
     c = np.array([120, 80, 100, 100], np.int32)   # std/mean = sqrt(200)/100 = 0.141
     assert moer.BalanceMonitor(4).observe(c) == []
     assert oracle.load_stats(c)["cv"] < 0.2
+
+
+def test_capacity_validation():
+    st, msg = _route_raw(_desc(capacity=-1))
+    assert st == moer.MOER_EINVAL and "capacity" in msg, msg
+    st, msg = _route_raw(_desc(capacity=640, input=moer.MOER_IN_INDICES))
+    assert st == moer.MOER_EINVAL and "capacity" in msg, msg
+    # the capacity rounds need their own workspace
+    assert (moer.moer_route_workspace_bytes(_desc(capacity=640)) >
+            moer.moer_route_workspace_bytes(_desc()) + 16384 * 256 * 8)
+
+
+def test_expert_capacity_helper_matches_oracle():
+    import oracle
+
+    for T, K, N in ((16384, 8, 256), (64, 1, 4), (100, 3, 7), (4096, 2, 8), (128, 8, 256)):
+        assert moer.expert_capacity(T, K, N) == oracle.expert_capacity(T, K, N)

@@ -61,7 +61,7 @@ def _layers(t, rank):
 def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups=1, n_shared=0,
           bias=None, logit_offset=None, scores=None, idx_in=None, N=None, want_h=False,
           want_inv_perm=True, want_entropy=True, want_load_stats=False, bias_update=None,
-          bias_update_u=1e-3, bias_mode="score", workspace=None, stream=None):
+          bias_update_u=1e-3, bias_mode="score", capacity=0, workspace=None, stream=None):
     """Route a batch; returns a dict of device tensors, each with a leading
     layer dimension L.
 
@@ -73,6 +73,9 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
     bias_mode "score" adds the bias to the scores for the selection only;
     "logit" (hidden-state input) adds it to the logits, so the weights and
     entropies come from the compensated scores too.
+    capacity > 0 limits every routed expert to that many assignments per
+    layer (see expert_capacity); the result then holds "cap_stats" [L, 2]
+    (slots rerouted, slots dropped).
     """
     x, w_gate = _layers(x, 3), _layers(w_gate, 3)
     scores, idx_in, bias = _layers(scores, 3), _layers(idx_in, 3), _layers(bias, 2)
@@ -89,7 +92,8 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
     Kt, Nb = K + n_shared, N + n_shared
     desc = make_desc(n_layers=L, T=T, d=d, N=N, K=K, n_groups=n_groups, topk_groups=topk_groups,
                      n_shared=n_shared, score_fn=_SCORE_FN.get(score_fn, score_fn), dtype=dtype,
-                     input=mode, bias_mode=_BIAS_MODE.get(bias_mode, bias_mode))
+                     input=mode, bias_mode=_BIAS_MODE.get(bias_mode, bias_mode),
+                     capacity=int(capacity))
     i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
     out = {"counts": torch.empty(L, Nb, **i32), "offsets": torch.empty(L, Nb + 1, **i32),
            "perm": torch.empty(L, T * Kt, **i32)}
@@ -103,6 +107,8 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
             out["agg_entropy"] = torch.empty(L, **f32)
     if want_load_stats:
         out["load_stats"] = torch.empty(L, 64, dtype=torch.uint8, device=dev)
+    if capacity:
+        out["cap_stats"] = torch.empty(L, 2, **i32)
     if want_h and mode == MOER_IN_HIDDEN:
         out["h"] = torch.empty(L, T, N, **f32)
     if workspace is None:
@@ -114,8 +120,17 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
                agg_entropy=out.get("agg_entropy"), topk_idx=out.get("topk_idx"),
                counts=out["counts"], offsets=out["offsets"], perm=out["perm"],
                inv_perm=out.get("inv_perm"), load_stats=out.get("load_stats"),
-               bias_update=_layers(bias_update, 2), bias_update_u=bias_update_u)
+               bias_update=_layers(bias_update, 2), bias_update_u=bias_update_u,
+               cap_stats=out.get("cap_stats"))
     return out
+
+
+def expert_capacity(T, K, N, factor="1.25"):
+    """Per-expert capacity ceil(factor * T * K / N) (dailyaiworld, production
+    testing: 1.25 x batch x top-k / experts), in exact rational arithmetic."""
+    from fractions import Fraction
+    q = Fraction(factor) * T * K / N
+    return -((-q.numerator) // q.denominator)
 
 
 def load_stats(counts, N, stream=None):

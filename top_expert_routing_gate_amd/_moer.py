@@ -30,7 +30,7 @@ EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats", "moer
 class MoerRouteDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layers", "T", "d", "N", "K", "n_groups", "topk_groups", "n_shared",
-                 "score_fn", "dtype", "input", "bias_mode")]
+                 "score_fn", "dtype", "input", "bias_mode", "capacity")]
 
 
 class MoerBalanceCfg(ctypes.Structure):
@@ -43,7 +43,8 @@ class MoerRouteIO(ctypes.Structure):
                 ("x", "w_gate", "scores", "idx_in", "bias", "logit_offset", "h_out", "topk_w",
                  "tok_entropy", "agg_entropy", "topk_idx", "counts", "offsets", "perm",
                  "inv_perm", "ev_gemm_begin", "ev_gemm_end", "load_stats", "bias_update")] + \
-        [("bias_update_u", ctypes.c_float), ("ev_select_wait", ctypes.c_void_p)]
+        [("bias_update_u", ctypes.c_float), ("cap_stats", ctypes.c_void_p),
+         ("ev_select_wait", ctypes.c_void_p)]
 
 
 class MoerLoadStats(ctypes.Structure):
@@ -132,9 +133,9 @@ def moer_abi_version():
 
 def make_desc(*, T, N, K, n_layers=1, d=0, n_groups=1, topk_groups=1, n_shared=0,
               score_fn=MOER_SIGMOID, dtype=MOER_BF16, input=MOER_IN_HIDDEN,
-              bias_mode=MOER_BIAS_SCORE):
+              bias_mode=MOER_BIAS_SCORE, capacity=0):
     return MoerRouteDesc(n_layers, T, d, N, K, n_groups, topk_groups, n_shared, score_fn, dtype,
-                         input, bias_mode)
+                         input, bias_mode, capacity)
 
 
 def moer_route_workspace_bytes(desc):
@@ -145,7 +146,7 @@ def _route_io(desc, *, x=None, w_gate=None, scores=None, idx_in=None, bias=None,
               logit_offset=None, h_out=None, topk_w=None, tok_entropy=None, agg_entropy=None,
               topk_idx=None, counts=None, offsets=None, perm=None, inv_perm=None,
               ev_gemm_begin=None, ev_gemm_end=None, load_stats=None, bias_update=None,
-              bias_update_u=0.0, ev_select_wait=None):
+              bias_update_u=0.0, cap_stats=None, ev_select_wait=None):
     for name, t, dt in (("x", x, None), ("w_gate", w_gate, None), ("scores", scores, torch.float32),
                         ("idx_in", idx_in, torch.int32), ("bias", bias, torch.float32),
                         ("logit_offset", logit_offset, torch.float32),
@@ -154,7 +155,7 @@ def _route_io(desc, *, x=None, w_gate=None, scores=None, idx_in=None, bias=None,
                         ("agg_entropy", agg_entropy, torch.float32),
                         ("topk_idx", topk_idx, torch.int32), ("counts", counts, torch.int32),
                         ("offsets", offsets, torch.int32), ("perm", perm, torch.int32),
-                        ("inv_perm", inv_perm, torch.int32),
+                        ("inv_perm", inv_perm, torch.int32), ("cap_stats", cap_stats, torch.int32),
                         ("bias_update", bias_update, torch.float32)):
         if t is not None and dt is not None and t.dtype != dt:
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
@@ -168,7 +169,7 @@ def _route_io(desc, *, x=None, w_gate=None, scores=None, idx_in=None, bias=None,
                        _ptr(logit_offset), _ptr(h_out), _ptr(topk_w), _ptr(tok_entropy),
                        _ptr(agg_entropy), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
                        _ptr(inv_perm), ev_gemm_begin, ev_gemm_end, _ptr(load_stats),
-                       _ptr(bias_update), float(bias_update_u), ev_select_wait)
+                       _ptr(bias_update), float(bias_update_u), _ptr(cap_stats), ev_select_wait)
 
 
 def moer_route(desc, *, workspace, stream=None, **buffers):

@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["moer_api.hip", "gate_gemm.hip", "route_rows.hip", "score_topk.hip", "layout.hip",
            "stats.hip", "dispatch_combine.hip",
-           "forcible.hip"]
+           "forcible.hip", "capacity.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -44,6 +44,9 @@ struct Plan {
   int Kt, Nb, nsb, nlb, ksplit;
   int nseg;
   size_t off_h, off_colpart, off_cnt, off_seg, total;
+  // capacity-limited routing
+  size_t off_key, off_s, off_ranked, off_nel, off_next, off_changed, off_list0, off_list1,
+      off_inv;
 };
 
 Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
@@ -64,6 +67,27 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   p.nseg = (p.nsb + moer::kSegBlocks - 1) / moer::kSegBlocks;
   p.off_seg = o;  // expert counts per segment of histogram blocks
   o += align_up(L * p.nseg * p.Nb * sizeof(int32_t) + 16);
+  if (d.capacity > 0 && d.input != MOER_IN_INDICES) {
+    const size_t LT = L * (size_t)d.T;
+    p.off_key = o;      // selection keys, -inf outside the kept groups
+    o += align_up(LT * d.N * sizeof(float) + 16);
+    p.off_s = o;        // scores
+    o += align_up(LT * d.N * sizeof(float) + 16);
+    p.off_ranked = o;   // candidate lists, 256 ids per token
+    o += align_up(LT * moer::kMaxExperts + 16);
+    p.off_nel = o;
+    o += align_up(LT * sizeof(int32_t) + 16);
+    p.off_next = o;
+    o += align_up(LT * sizeof(int32_t) + 16);
+    p.off_changed = o;
+    o += align_up(LT + 16);
+    p.off_list0 = o;    // pending slots (two buffers)
+    o += align_up(LT * d.K * sizeof(int32_t) + 16);
+    p.off_list1 = o;
+    o += align_up(LT * d.K * sizeof(int32_t) + 16);
+    p.off_inv = o;      // the first layout's inv_perm when the caller has none
+    o += align_up(LT * p.Kt * sizeof(int32_t) + 16);
+  }
   p.total = o;
   return p;
 }
@@ -116,6 +140,9 @@ moer_status validate_desc(const moer_route_desc* d) {
     return fail(MOER_EINVAL, "unknown bias_mode %d", d->bias_mode);
   if (d->bias_mode == MOER_BIAS_LOGIT && d->input != MOER_IN_HIDDEN)
     return fail(MOER_EINVAL, "a logit-space bias needs HIDDEN input (the logits)");
+  if (d->capacity < 0) return fail(MOER_EINVAL, "capacity must be >= 0 (got %d)", d->capacity);
+  if (d->capacity > 0 && d->input == MOER_IN_INDICES)
+    return fail(MOER_EINVAL, "a capacity needs HIDDEN or SCORES input (the candidates)");
   if (d->input != MOER_IN_INDICES && selection_path(*d) == 0)
     return fail(MOER_EUNSUPPORTED,
                 "group size %d with N=%d: these kernels need N/n_groups to be a power of two "
@@ -179,6 +206,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     return fail(MOER_EINVAL, "bias_update_u must be finite and >= 0");
 
   const bool want_agg = !indices && io->agg_entropy != nullptr;
+  const bool capped = d.capacity > 0 && !indices;
   const Plan p = make_plan(d, hidden, want_agg);
   if (workspace == nullptr && p.total > 0) return fail(MOER_EWORKSPACE, "workspace is NULL");
   if (workspace_bytes < p.total)
@@ -247,6 +275,10 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     a.score_fn = d.score_fn;
     a.apply_score = hidden ? 1 : 0;
     a.bias_logit = d.bias_mode == MOER_BIAS_LOGIT ? 1 : 0;
+    if (capped) {
+      a.key_out = reinterpret_cast<float*>(ws + p.off_key);
+      a.s_out = reinterpret_cast<float*>(ws + p.off_s);
+    }
     if (path == 1) {
       a.cnt = cnt;
       a.segsum = segsum;
@@ -268,19 +300,59 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   la.counts = io->counts;
   la.offsets = io->offsets;
   la.perm = io->perm;
-  la.inv_perm = io->inv_perm;
+  int32_t* inv_perm = io->inv_perm;
+  if (capped && inv_perm == nullptr) inv_perm = reinterpret_cast<int32_t*>(ws + p.off_inv);
+  la.inv_perm = inv_perm;
   la.T = d.T;
   la.Kt = p.Kt;
   la.Nb = p.Nb;
   la.N = d.N;
   la.nlb = p.nlb;
   la.nsb = p.nsb;
-  la.stats = io->load_stats;
-  la.bias_inout = io->bias_update;
+  // with a capacity the statistics and the bias update wait for the final ids
+  la.stats = capped ? nullptr : io->load_stats;
+  la.bias_inout = capped ? nullptr : io->bias_update;
   la.bias_step = io->bias_update_u;
   la.fill_invalid = indices ? 1 : 0;
   la.need_count = (path != 1 && d.T > 0) ? 1 : 0;
   MOER_CHECK(moer::launch_layout(la, L, s));
+
+  if (capped && d.T > 0) {
+    // later rounds of the capacity limit, then the layout of the final ids
+    moer::CapArgs c{};
+    c.idx = io->topk_idx;
+    c.w = io->topk_w;
+    c.inv_perm = inv_perm;
+    c.offsets = io->offsets;
+    c.key = reinterpret_cast<const float*>(ws + p.off_key);
+    c.s = reinterpret_cast<const float*>(ws + p.off_s);
+    c.ranked = reinterpret_cast<uint8_t*>(ws + p.off_ranked);
+    c.n_el = reinterpret_cast<int32_t*>(ws + p.off_nel);
+    c.next = reinterpret_cast<int32_t*>(ws + p.off_next);
+    c.changed = reinterpret_cast<uint8_t*>(ws + p.off_changed);
+    c.list0 = reinterpret_cast<int32_t*>(ws + p.off_list0);
+    c.list1 = reinterpret_cast<int32_t*>(ws + p.off_list1);
+    c.stats = io->cap_stats;
+    c.L = L;
+    c.T = d.T;
+    c.N = d.N;
+    c.K = d.K;
+    c.Kt = p.Kt;
+    c.Nb = p.Nb;
+    c.cap = d.capacity;
+    MOER_CHECK(moer::launch_capacity(c, s));
+    MOER_CHECK(moer::launch_zero_ints(segsum, n_seg, s));
+    la.inv_perm = io->inv_perm;
+    la.colpart = nullptr;
+    la.agg_entropy = nullptr;
+    la.stats = io->load_stats;
+    la.bias_inout = io->bias_update;
+    la.fill_invalid = 1;
+    la.need_count = 1;
+    MOER_CHECK(moer::launch_layout(la, L, s));
+  } else if (capped && io->cap_stats != nullptr) {
+    MOER_CHECK(moer::launch_zero_ints(io->cap_stats, 2 * L, s));
+  }
 #undef MOER_CHECK
   return ok();
 }

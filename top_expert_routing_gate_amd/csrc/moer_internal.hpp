@@ -31,6 +31,8 @@ struct ScoreArgs {
   int32_t* segsum;        // [L][nseg][Nb] += the block counts (zero beforehand), or nullptr
   int T, N, K, G, Gk, n_shared, score_fn, apply_score, nsplit;
   int bias_logit;         // 1: the bias is added to the logits (with the offset)
+  float* key_out;         // [L][T][N] selection keys, -inf outside the kept groups, or nullptr
+  float* s_out;           // [L][T][N] scores (the weights' numerators), or nullptr
 };
 
 struct LayoutArgs {
@@ -78,6 +80,25 @@ hipError_t launch_dispatch(const void* x, int64_t row_bytes, int L, int T, int K
                            const int32_t* inv_perm, void* out, hipStream_t s);
 hipError_t launch_combine(const void* eo, int eo_bf16, const float* w, const int32_t* inv_perm,
                           int L, int T, int Kt, int d, void* y, int y_bf16, hipStream_t s);
+
+// Capacity-limited routing (after the selection and the first layout).
+struct CapArgs {
+  int32_t* idx;             // [L][T][Kt] top-K in, capacity-limited out (-1 = dropped)
+  float* w;                 // [L][T][Kt] weights, renormalised for changed tokens
+  const int32_t* inv_perm;  // [L][T*Kt] first layout (round 0 ranks)
+  const int32_t* offsets;   // [L][Nb+1] first layout
+  const float* key;         // [L][T][N] selection keys, -inf when not eligible
+  const float* s;           // [L][T][N] scores
+  uint8_t* ranked;          // [L][T][256] candidate lists (tokens with a rejection)
+  int32_t* n_el;            // [L][T] list lengths (0 = token not affected)
+  int32_t* next;            // [L][T] next candidate position
+  uint8_t* changed;         // [L][T] token's slots changed
+  int32_t* list0;           // [L][T*K] pending slots, two buffers
+  int32_t* list1;
+  int32_t* stats;           // [L][2] rerouted, dropped, or nullptr
+  int L, T, N, K, Kt, Nb, cap;
+};
+hipError_t launch_capacity(const CapArgs& c, hipStream_t s);
 
 // Balancing step with rule, moving-average loads and period (one
 // workgroup per layer).

@@ -333,6 +333,17 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     group_m2 = m2;
   }
 
+  // keys and scores for the capacity-limited rounds (candidates beyond top-K)
+  if (live && a.key_out != nullptr) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      if (e0 + j < N) {
+        a.key_out[row_off + e0 + j] = eligible ? key[j] + 0.f : NEG_INF;  // -0 -> +0
+        a.s_out[row_off + e0 + j] = s[j];
+      }
+    }
+  }
+
   // lo: a key that at least K distinct eligible experts reach, so every chosen
   // expert has key >= lo.
   float lo;

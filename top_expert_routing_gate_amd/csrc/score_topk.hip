@@ -162,6 +162,18 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
       }
     }
 
+    // keys and scores for the capacity-limited rounds (candidates beyond top-K)
+    if (a.key_out != nullptr) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int e = lane * E + j;
+        if (e < N) {
+          a.key_out[row_off + e] = key[j];
+          a.s_out[row_off + e] = s[j];
+        }
+      }
+    }
+
     // 4. top-K rounds
     int sel_e[kMaxSlots];
     float sel_s[kMaxSlots];
