@@ -265,6 +265,47 @@ def time_forcible_layout(moer, torch, wl, outs, stream, steps):
     return res
 
 
+def time_capacity(moer, torch, wl, x, Wd, bias, stream, steps):
+    """The route with the pages' capacity (1.25 x T*K/N) on the batch, and on
+    the same batch with the collapse workload's celebrity offset (+3.0 on
+    experts 2, 4, 7, 12), each over `steps` calls between two events on the
+    route's stream (bias not updated, so every call is the same work)."""
+    L, T, N, K = wl.n_layers, wl.T, wl.N, wl.K
+    cap = moer.expert_capacity(T, K, N)
+    dev = x.device
+    i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+    Kt, Nb = wl.Kt, wl.Nb
+    bufs = dict(topk_idx=torch.empty(L, T, Kt, **i32), topk_w=torch.empty(L, T, Kt, **f32),
+                tok_entropy=torch.empty(L, T, **f32), agg_entropy=torch.empty(L, **f32),
+                counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
+                perm=torch.empty(L, T * Kt, **i32), inv_perm=torch.empty(L, T * Kt, **i32),
+                cap_stats=torch.empty(L, 2, **i32))
+    desc = moer.make_desc(n_layers=L, T=T, d=wl.d, N=N, K=K, n_groups=wl.n_groups,
+                          topk_groups=wl.topk_groups, n_shared=wl.n_shared, score_fn=wl.score_fn,
+                          dtype=wl.dtype, capacity=cap)
+    ws = torch.empty(moer.moer_route_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    celeb = torch.zeros(N, **f32)
+    celeb[[2, 4, 7, 12]] = 3.0
+    res = {"capacity": cap}
+    with torch.cuda.stream(stream):
+        for name, off in (("dsv3_group", None), ("collapse_offsets", celeb)):
+            call = moer.PreparedRoute(desc, workspace=ws, x=x, w_gate=Wd, bias=bias,
+                                      logit_offset=off, **bufs)
+            for _ in range(3):
+                call()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(steps):
+                call()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            st = bufs["cap_stats"][0].tolist()
+            res[name] = {"us": ev[0].elapsed_time(ev[1]) * 1e3 / steps, "rerouted": st[0],
+                         "dropped": st[1], "max_count": int(bufs["counts"][:, :N].max())}
+    del ws
+    return res
+
+
 def time_balance_step(moer, torch, wl, outs, stream, steps):
     """The balancing-rule variants on the batch's counts, each over `steps`
     calls between two events on the route's stream (a copy of the bias, so
@@ -423,6 +464,11 @@ def main():
         print(f"[bench] layout (INDICES mode): routed ids {fl['routed_ids']['us']:.1f} us, "
               f"balanced ids {fl['balanced_ids']['us']:.1f} us", file=sys.stderr, flush=True)
 
+    cp = time_capacity(moer, torch, wl, xs[0], Wd, bias, streams[0], args.steps)
+    print(f"[bench] capacity {cp['capacity']}: {cp['dsv3_group']['us']:.1f} us "
+          f"({cp['dsv3_group']['rerouted']} rerouted), with celebrity offsets "
+          f"{cp['collapse_offsets']['us']:.1f} us ({cp['collapse_offsets']['rerouted']} rerouted, "
+          f"{cp['collapse_offsets']['dropped']} dropped)", file=sys.stderr, flush=True)
     bs = time_balance_step(moer, torch, wl, outs, streams[0], args.steps)
     print(f"[bench] balance step: sign {bs['sign']['us']:.1f} us, proportional+EMA "
           f"{bs['proportional_ema_every4']['us']:.1f} us", file=sys.stderr, flush=True)
@@ -457,6 +503,7 @@ def main():
     if fl is not None:
         line["forcible_layout"] = fl
     line["balance_step"] = bs
+    line["capacity_route"] = cp
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one batch", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, {"x": xs_cpu[0], "W": W, "bias": b0})

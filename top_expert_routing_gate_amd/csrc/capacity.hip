@@ -14,19 +14,28 @@
 // until nothing is pending. Shared slots are not limited.
 //
 // Kernels, after the selection (which wrote the masked keys and the scores)
-// and the first layout (whose bucket ranks decide round 0):
+// and the first layout (whose bucket ranks decide round 0, and which flags
+// the layers with an expert over capacity; the other layers skip all of
+// this):
 //  1. cap_rank_kernel (one wavefront per token): a token with a slot past
 //     its expert's capacity sorts its eligible experts (a 256-entry bitonic
-//     sort of (key, id) across the wavefront) into its candidate list.
-//  2. cap_rounds_kernel (one workgroup per layer): every later round. The
-//     pending slots form a list in (token, slot) order; it is walked in
-//     chunks of 1024, one slot per thread: the slot's next candidate comes
-//     from its token's list, its rank among the chunk's proposals to the
-//     same expert from per-expert bitmaps in LDS (popcounts, so the order is
-//     the list order), and the experts' running counts carry the rank across
-//     chunks. Rejected slots are compacted, in order, into the next round's
-//     list.
-//  3. cap_weights_kernel: renormalised weights of the tokens that changed.
+//     sort of (key, id) across the wavefront) into its candidate list, and
+//     makes its round-1 proposals.
+//  2. Rounds 1 and 2 use the whole chip: the layout kernels rank each
+//     round's proposals within their experts in (token, slot) order (the
+//     stable counting sort the router's layout already is), and
+//     cap_accept_kernel (one thread per token) accepts those whose rank fits
+//     under what the expert holds, and makes the rejected slots' next
+//     proposals.
+//  3. cap_rounds_kernel (one workgroup per layer): the remaining rounds,
+//     which are small. The pending slots form a list in (token, slot) order;
+//     it is walked in chunks of 1024, one slot per thread: the slot's next
+//     candidate comes from its token's list, its rank among the chunk's
+//     proposals to the same expert from per-expert bitmaps in LDS
+//     (popcounts, so the order is the list order), and the experts' running
+//     counts carry the rank across chunks. Rejected slots are compacted, in
+//     order, into the next round's list.
+//  4. cap_weights_kernel: renormalised weights of the tokens that changed.
 // The layout is then rebuilt from the final ids.
 #include "moer_internal.hpp"
 
@@ -49,12 +58,27 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
+__device__ __forceinline__ unsigned long long shfl_u64(unsigned long long v, int src) {
+  const int lo = __shfl((int)(uint32_t)v, src, kWave);
+  const int hi = __shfl((int)(uint32_t)(v >> 32), src, kWave);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
 // Per-token candidate lists for tokens with a slot rejected in round 0.
 __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) {
   const int lane = threadIdx.x & 63;
   const int layer = blockIdx.y;
+  {
+    // clear the grid rounds' segment totals and the reroute/drop counters
+    const int64_t g = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    const int64_t nseg = (int64_t)c.L * c.nseg * c.N;
+    for (int r = 0; r < kCapGridRounds; ++r)
+      for (int64_t i = g; i < nseg; i += stride) c.round[r].segsum[i] = 0;
+    for (int64_t i = g; i < 3 * (int64_t)c.L; i += stride) c.rd[i] = 0;
+  }
   const int t = blockIdx.x * kRankWaves + (threadIdx.x >> 6);
-  if (t >= c.T) return;
+  if (t >= c.T || c.flag[layer] == 0) return;
   const int N = c.N, K = c.K, Kt = c.Kt;
   const size_t tok = (size_t)layer * c.T + t;
   const int32_t* off = c.offsets + (size_t)layer * (c.Nb + 1);
@@ -65,13 +89,17 @@ __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) 
     const int p = c.inv_perm[slot];
     rejected = e >= 0 && e < N && p - off[e] >= c.cap;
   }
-  const bool affected = __ballot(rejected) != 0;
+  const unsigned long long rmask = __ballot(rejected);
+  const int n_rej = __builtin_popcountll(rmask);
   if (lane == 0) {
     c.changed[tok] = 0;
-    c.next[tok] = K;
-    if (!affected) c.n_el[tok] = 0;
+    c.round[0].mask[tok] = (int32_t)rmask;
+    c.next[tok] = K + n_rej;  // round 1 takes candidates K .. K + n_rej - 1
   }
-  if (!affected) return;
+  if (rmask == 0) {
+    if (lane < K) c.round[0].prop[tok * K + lane] = -1;
+    return;
+  }
 
   // (order(key), 0xFFFF - id): larger = earlier in decision order; 0 = not
   // eligible (or absent)
@@ -124,6 +152,92 @@ __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) 
     if (i < n_el) list[i] = (uint8_t)(0xFFFF - (unsigned)(v[r] & 0xFFFF));
   }
   if (lane == 0) c.n_el[tok] = n_el;
+  // round 1: the j-th rejected slot (slot order) proposes candidate K + j
+  // (the shuffles run in every lane; only rejected slots store)
+  const int j = __builtin_popcountll(rmask & ((1ull << lane) - 1ull));
+  const int ci = rejected ? K + j : 0;
+  int e = -1;
+#pragma unroll
+  for (int r = 0; r < kSortN / kWave; ++r) {
+    const unsigned long long x = shfl_u64(v[r], ci & 63);  // element ci
+    if (r == (ci >> 6)) e = (int)(0xFFFF - (unsigned)(x & 0xFFFF));
+  }
+  if (lane < K) c.round[0].prop[tok * K + lane] = (rejected && ci < n_el) ? e : -1;
+}
+
+// What expert e holds before grid round r (0-based): the first layout's
+// count, then each earlier round's proposals, every step capped.
+__device__ __forceinline__ int held_before(const CapArgs& c, int layer, int e, int r) {
+  const int32_t* o0 = c.offsets + (size_t)layer * (c.Nb + 1);
+  int h = min(o0[e + 1] - o0[e], c.cap);
+  for (int i = 0; i < r; ++i) {
+    const int32_t* oi = c.round[i].offsets + (size_t)layer * (c.N + 1);
+    h = min(h + (oi[e + 1] - oi[e]), c.cap);
+  }
+  return h;
+}
+
+// Grid round r (0-based): accept the round's proposals whose rank within
+// their expert fits under what the expert holds; the rejected slots of a
+// token take its next candidates, in slot order, as the next round's
+// proposals. One thread per token.
+__global__ __launch_bounds__(256) void cap_accept_kernel(CapArgs c, int r) {
+  const int layer = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (c.flag[layer] == 0) return;
+  const int K = c.K, Kt = c.Kt;
+  int rerouted = 0, dropped = 0, pending = 0;
+  if (t < c.T) {
+    const size_t tok = (size_t)layer * c.T + t;
+    const CapRound& cur = c.round[r];
+    const CapRound& nxt = c.round[r + 1];
+    const int m = cur.mask[tok];
+    const int32_t* off = cur.offsets + (size_t)layer * (c.N + 1);
+    int rej = 0;
+    for (int k = 0; k < K; ++k) {
+      if (!((m >> k) & 1)) continue;
+      const int e = cur.prop[tok * K + k];
+      if (e < 0) {
+        c.idx[tok * Kt + k] = -1;
+        c.changed[tok] = 1;
+        ++dropped;
+        continue;
+      }
+      const int rank = cur.inv[tok * K + k] - off[e];
+      if (held_before(c, layer, e, r) + rank < c.cap) {
+        c.idx[tok * Kt + k] = e;
+        c.changed[tok] = 1;
+        ++rerouted;
+      } else {
+        rej |= 1 << k;
+      }
+    }
+    int nx = c.next[tok];
+    const int ne = c.n_el[tok];
+    const uint8_t* list = c.ranked + tok * kMaxExperts;
+    for (int k = 0; k < K; ++k) {
+      int e = -1;
+      if ((rej >> k) & 1) {
+        e = nx < ne ? (int)list[nx] : -1;
+        ++nx;
+      }
+      nxt.prop[tok * K + k] = e;
+    }
+    if (rej) c.next[tok] = nx;
+    nxt.mask[tok] = rej;
+    pending = __builtin_popcount(rej);
+  }
+  // reroute / drop / still-pending counts (integer atomics: order-independent)
+  for (int o = 32; o > 0; o >>= 1) {
+    rerouted += __shfl_xor(rerouted, o, kWave);
+    dropped += __shfl_xor(dropped, o, kWave);
+    pending += __shfl_xor(pending, o, kWave);
+  }
+  if ((threadIdx.x & 63) == 0 && (rerouted | dropped | pending)) {
+    atomicAdd(&c.rd[3 * layer], rerouted);
+    atomicAdd(&c.rd[3 * layer + 1], dropped);
+    if (r == kCapGridRounds - 1) atomicAdd(&c.rd[3 * layer + 2], pending);
+  }
 }
 
 // Exclusive prefix of `flag` over the workgroup (in thread order); returns
@@ -148,7 +262,6 @@ __device__ __forceinline__ int block_prefix(int flag, int* wsum, int* total) {
 struct RoundsLds {
   int held[kMaxExperts];
   int run[kMaxExperts];
-  int off[kMaxExperts + 1];
   unsigned bits[kMaxExperts][kChunkWords];  // proposals of the chunk per expert
   int wsum[kRoundThreads / kWave];
   int red[2][kRoundThreads / kWave];
@@ -160,42 +273,54 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
   const int N = c.N, K = c.K, Kt = c.Kt, T = c.T, cap = c.cap;
   const int tid = threadIdx.x;
   const int64_t A = (int64_t)T * K;
-  const int32_t* off = c.offsets + (size_t)layer * (c.Nb + 1);
   int32_t* idx = c.idx + (size_t)layer * T * Kt;
-  const int32_t* inv = c.inv_perm + (size_t)layer * T * Kt;
   int32_t* next = c.next + (size_t)layer * T;
   const int32_t* n_el = c.n_el + (size_t)layer * T;
   const uint8_t* ranked = c.ranked + (size_t)layer * T * kMaxExperts;
   uint8_t* changed = c.changed + (size_t)layer * T;
   int32_t* lists[2] = {c.list0 + (size_t)layer * A, c.list1 + (size_t)layer * A};
 
-  for (int e = tid; e <= N; e += kRoundThreads) sh.off[e] = off[e];
-  __syncthreads();
-  int over = 0;
-  for (int e = tid; e < N; e += kRoundThreads) {
-    const int n = sh.off[e + 1] - sh.off[e];
-    sh.held[e] = n < cap ? n : cap;
-    over |= n > cap ? 1 : 0;
-  }
-  const bool any_over = __syncthreads_or(over) != 0;
+  // rounds are left only where the grid rounds left slots pending
+  const bool any_over = c.flag[layer] != 0 && c.rd[3 * layer + 2] != 0;
   int rerouted = 0, dropped = 0;
   if (any_over) {
-    // round 0's rejections, compacted in (token, slot) order
+    for (int e = tid; e < N; e += kRoundThreads) sh.held[e] = held_before(c, layer, e, kCapGridRounds);
+    // the pending slots after the grid rounds, in (token, slot) order, from
+    // the per-token masks: each wavefront takes 64 tokens, 16 per pass
     int P = 0;
-    for (int64_t a0 = 0; a0 < A; a0 += kRoundThreads) {
-      const int64_t a = a0 + tid;
-      int rej = 0;
-      if (a < A) {
-        const int64_t slot = (a / K) * Kt + a % K;
-        const int e = idx[slot];
-        rej = (e >= 0 && e < N && inv[slot] - sh.off[e] >= cap) ? 1 : 0;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int32_t* mask = c.round[kCapGridRounds].mask + (size_t)layer * T;
+    const int32_t* prop = c.round[kCapGridRounds].prop + (size_t)layer * A;
+    int32_t* le = c.list_e + (size_t)layer * A;
+    for (int t0 = 0; t0 < T; t0 += kRoundThreads) {
+      const int t = t0 + wave * kWave + lane;
+      const int m = t < T ? mask[t] : 0;
+      const int n = __builtin_popcount(m);
+      int x = n;  // inclusive scan over the wavefront's tokens
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        x += lane >= o ? y : 0;
       }
-      int total;
-      const int pos = block_prefix(rej, sh.wsum, &total);
-      if (rej) lists[0][P + pos] = (int32_t)a;
-      P += total;
+      if (lane == kWave - 1) sh.wsum[wave] = x;
+      __syncthreads();
+      int base = P, tot = 0;
+      for (int w = 0; w < kRoundThreads / kWave; ++w) {
+        base += w < wave ? sh.wsum[w] : 0;
+        tot += sh.wsum[w];
+      }
+      int pos = base + x - n;
+      for (int k = 0; k < K; ++k) {
+        if (!((m >> k) & 1)) continue;
+        const int a = t * K + k;
+        lists[0][pos] = a;
+        le[pos] = prop[a];
+        ++pos;
+      }
+      __syncthreads();  // wsum is reused
+      P += tot;
     }
     int cur = 0;
+    bool first = true;  // proposals made by the last grid round
     while (P > 0) {  // P is the same in every thread
       // run[e]: this round's proposals to e in the chunks already walked
       for (int x = tid; x < N; x += kRoundThreads) sh.run[x] = 0;
@@ -206,7 +331,11 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
         // advance: the slot's ordinal among its token's pending slots picks
         // the candidate; the token's last pending slot moves the pointer on
         int a = -1, t = -1, e = -1, new_next = -1;
-        if (i < P) {
+        if (i < P && first) {
+          a = list[i];
+          t = a / K;
+          e = le[i];
+        } else if (i < P) {
           a = list[i];
           t = a / K;
           int ord = 0;
@@ -263,7 +392,13 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
       __syncthreads();
       P = Pn;
       cur ^= 1;
+      first = false;
     }
+  }
+  if (c.flag[layer] != 0) {
+    // the final layout counts into cleared segment totals
+    int32_t* seg = c.segsum + (size_t)layer * c.nseg * c.Nb;
+    for (int x = tid; x < c.nseg * c.Nb; x += kRoundThreads) seg[x] = 0;
   }
   // counts of rerouted and dropped slots
   if (c.stats != nullptr) {
@@ -283,8 +418,9 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
         rs += sh.red[0][w];
         ds += sh.red[1][w];
       }
-      c.stats[2 * layer] = rs;
-      c.stats[2 * layer + 1] = ds;
+      const bool grid = c.flag[layer] != 0;  // the grid rounds counted too
+      c.stats[2 * layer] = rs + (grid ? c.rd[3 * layer] : 0);
+      c.stats[2 * layer + 1] = ds + (grid ? c.rd[3 * layer + 1] : 0);
     }
   }
 }
@@ -293,7 +429,7 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
 // scores over their sum (1/placed when the sum is 0); dropped slots 0.
 __global__ __launch_bounds__(256) void cap_weights_kernel(CapArgs c) {
   const int64_t tok = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (tok >= (int64_t)c.L * c.T || !c.changed[tok]) return;
+  if (tok >= (int64_t)c.L * c.T || c.flag[tok / c.T] == 0 || !c.changed[tok]) return;
   const int32_t* id = c.idx + tok * c.Kt;
   const float* s = c.s + tok * c.N;
   float z = 0.f;
@@ -316,6 +452,32 @@ hipError_t launch_capacity(const CapArgs& c, hipStream_t s) {
                      dim3(kRankWaves * kWave), 0, s, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  for (int r = 0; r < kCapGridRounds; ++r) {
+    // rank the round's proposals within their experts: the layout kernels
+    LayoutArgs la{};
+    la.idx = c.round[r].prop;
+    la.cnt = c.round[r].cnt;
+    la.segsum = c.round[r].segsum;
+    la.counts = c.round[r].counts;
+    la.offsets = c.round[r].offsets;
+    la.perm = c.round[r].perm;
+    la.inv_perm = c.round[r].inv;
+    la.T = c.T;
+    la.Kt = c.K;
+    la.Nb = c.N;
+    la.N = c.N;
+    la.nlb = c.nlb;
+    la.nsb = c.nsb;
+    la.nseg = c.nseg;
+    la.need_count = 1;
+    la.cap_phase = 2;  // layers without an expert over capacity skip
+    la.cap_flag = const_cast<int32_t*>(c.flag);
+    e = launch_layout(la, c.L, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(cap_accept_kernel, dim3((c.T + 255) / 256, c.L), dim3(256), 0, s, c, r);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(cap_rounds_kernel, dim3(c.L), dim3(kRoundThreads), 0, s, c);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -37,6 +37,7 @@ static_assert(kThreads == kBalanceThreads, "the first layout workgroup runs the 
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
   __shared__ int hist[kMaxBuckets];
   const int layer = blockIdx.y;
+  if (a.cap_phase == 2 && a.cap_flag[layer] == 0) return;  // the first layout stands
   const int blk = blockIdx.x;
   const int t0 = blk * kRowTokens;
   const int nt = min(kRowTokens, a.T - t0);
@@ -203,6 +204,16 @@ __device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* tot
   __shared__ BalanceScratch bal;
   load_totals(a, layer, -1, total, pre);
   __syncthreads();
+  if (a.cap_phase == 1) {
+    // is any routed expert over capacity? then the statistics wait for the
+    // final ids
+    int over = 0;
+    for (int e = threadIdx.x; e < a.N; e += kThreads) over |= total[e] > a.cap ? 1 : 0;
+    over = __syncthreads_or(over);
+    if (threadIdx.x == 0) a.cap_flag[layer] = over;
+    if (over) return;
+  }
+  if (a.stats == nullptr && a.bias_inout == nullptr) return;
   block_load_balance(total, a.N, a.stats != nullptr ? a.stats + layer : nullptr,
                      a.bias_inout != nullptr ? a.bias_inout + (size_t)layer * a.N : nullptr,
                      a.bias_step, bal);
@@ -219,6 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void layout_scatter_kernel(LayoutArgs 
 
   const int layer = blockIdx.y;
   const int blk = blockIdx.x;
+  if (a.cap_phase == 2 && a.cap_flag[layer] == 0) return;  // the first layout stands
   if (blk >= a.nlb) {
     if (blk == a.nlb && a.agg_entropy != nullptr)
       batch_mean_entropy(a, layer);
@@ -300,7 +312,7 @@ hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s) {
   }
   // a.nlb >= 1 (an empty batch still writes zero counts and offsets)
   const int extra = (a.agg_entropy != nullptr ? 1 : 0) +
-                    (a.stats != nullptr || a.bias_inout != nullptr ? 1 : 0);
+                    (a.stats != nullptr || a.bias_inout != nullptr || a.cap_phase == 1 ? 1 : 0);
   hipLaunchKernelGGL(layout_scatter_kernel, dim3(a.nlb + extra, L), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -46,7 +46,10 @@ struct Plan {
   size_t off_h, off_colpart, off_cnt, off_seg, total;
   // capacity-limited routing
   size_t off_key, off_s, off_ranked, off_nel, off_next, off_changed, off_list0, off_list1,
-      off_inv;
+      off_inv, off_flag, off_liste, off_rd;
+  struct Round {
+    size_t prop, mask, cnt, segsum, counts, offsets, perm, inv;
+  } round[moer::kCapGridRounds + 1];
 };
 
 Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
@@ -87,6 +90,32 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
     o += align_up(LT * d.K * sizeof(int32_t) + 16);
     p.off_inv = o;      // the first layout's inv_perm when the caller has none
     o += align_up(LT * p.Kt * sizeof(int32_t) + 16);
+    p.off_flag = o;     // layers with an expert over capacity
+    o += align_up(L * sizeof(int32_t) + 16);
+    p.off_liste = o;    // the workgroup rounds' first list: proposed experts
+    o += align_up(LT * d.K * sizeof(int32_t) + 16);
+    p.off_rd = o;       // rerouted / dropped / left pending by the grid rounds
+    o += align_up(3 * L * sizeof(int32_t) + 16);
+    for (int r = 0; r <= moer::kCapGridRounds; ++r) {  // per round: proposals ...
+      Plan::Round& q = p.round[r];
+      q.prop = o;
+      o += align_up(LT * d.K * sizeof(int32_t) + 16);
+      q.mask = o;
+      o += align_up(LT * sizeof(int32_t) + 16);
+      if (r == moer::kCapGridRounds) break;
+      q.cnt = o;        // ... and, for the grid rounds, their layout
+      o += align_up(L * d.N * p.nsb * sizeof(uint16_t) + 16);
+      q.segsum = o;
+      o += align_up(L * p.nseg * d.N * sizeof(int32_t) + 16);
+      q.counts = o;
+      o += align_up(L * d.N * sizeof(int32_t) + 16);
+      q.offsets = o;
+      o += align_up(L * (d.N + 1) * sizeof(int32_t) + 16);
+      q.perm = o;
+      o += align_up(LT * d.K * sizeof(int32_t) + 16);
+      q.inv = o;
+      o += align_up(LT * d.K * sizeof(int32_t) + 16);
+    }
   }
   p.total = o;
   return p;
@@ -309,10 +338,17 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   la.N = d.N;
   la.nlb = p.nlb;
   la.nsb = p.nsb;
-  // with a capacity the statistics and the bias update wait for the final ids
-  la.stats = capped ? nullptr : io->load_stats;
-  la.bias_inout = capped ? nullptr : io->bias_update;
+  la.stats = io->load_stats;
+  la.bias_inout = io->bias_update;
   la.bias_step = io->bias_update_u;
+  int32_t* cap_flag = capped ? reinterpret_cast<int32_t*>(ws + p.off_flag) : nullptr;
+  if (capped && d.T > 0) {
+    // statistics and bias update only for layers no expert overflows; the
+    // others wait for the final ids
+    la.cap = d.capacity;
+    la.cap_phase = 1;
+    la.cap_flag = cap_flag;
+  }
   la.fill_invalid = indices ? 1 : 0;
   la.need_count = (path != 1 && d.T > 0) ? 1 : 0;
   MOER_CHECK(moer::launch_layout(la, L, s));
@@ -333,6 +369,26 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     c.list0 = reinterpret_cast<int32_t*>(ws + p.off_list0);
     c.list1 = reinterpret_cast<int32_t*>(ws + p.off_list1);
     c.stats = io->cap_stats;
+    c.flag = cap_flag;
+    auto i32 = [&](size_t o) { return reinterpret_cast<int32_t*>(ws + o); };
+    for (int r = 0; r <= moer::kCapGridRounds; ++r) {
+      const Plan::Round& q = p.round[r];
+      c.round[r].prop = i32(q.prop);
+      c.round[r].mask = i32(q.mask);
+      if (r == moer::kCapGridRounds) break;
+      c.round[r].cnt = reinterpret_cast<uint16_t*>(ws + q.cnt);
+      c.round[r].segsum = i32(q.segsum);
+      c.round[r].counts = i32(q.counts);
+      c.round[r].offsets = i32(q.offsets);
+      c.round[r].perm = i32(q.perm);
+      c.round[r].inv = i32(q.inv);
+    }
+    c.list_e = i32(p.off_liste);
+    c.rd = i32(p.off_rd);
+    c.segsum = segsum;
+    c.nseg = p.nseg;
+    c.nsb = p.nsb;
+    c.nlb = p.nlb;
     c.L = L;
     c.T = d.T;
     c.N = d.N;
@@ -341,14 +397,12 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     c.Nb = p.Nb;
     c.cap = d.capacity;
     MOER_CHECK(moer::launch_capacity(c, s));
-    MOER_CHECK(moer::launch_zero_ints(segsum, n_seg, s));
     la.inv_perm = io->inv_perm;
     la.colpart = nullptr;
     la.agg_entropy = nullptr;
-    la.stats = io->load_stats;
-    la.bias_inout = io->bias_update;
     la.fill_invalid = 1;
     la.need_count = 1;
+    la.cap_phase = 2;
     MOER_CHECK(moer::launch_layout(la, L, s));
   } else if (capped && io->cap_stats != nullptr) {
     MOER_CHECK(moer::launch_zero_ints(io->cap_stats, 2 * L, s));

@@ -49,6 +49,13 @@ struct LayoutArgs {
   float* bias_inout;      // [L][N] updated in place, or nullptr
   float bias_step;
   int T, Kt, Nb, N, nlb, nsb, nseg, fill_invalid, need_count;
+  // capacity-limited routing: phase 1 = the layout of the top-K ids (one
+  // balance workgroup per layer sets cap_flag[l] when a routed expert holds
+  // more than cap, and does the statistics / bias update only when none
+  // does); phase 2 = the layout of the final ids (skipped, like the rest of
+  // the capacity pass, for layers whose flag is 0)
+  int cap, cap_phase;
+  int32_t* cap_flag;      // [L]
 };
 
 // Depth ranges the bf16 gate GEMM splits d into (its partial sums are
@@ -82,6 +89,19 @@ hipError_t launch_combine(const void* eo, int eo_bf16, const float* w, const int
                           int L, int T, int Kt, int d, void* y, int y_bf16, hipStream_t s);
 
 // Capacity-limited routing (after the selection and the first layout).
+// Rounds 1..kCapGridRounds are ranked by the layout kernels (all of the
+// chip); the rest by one workgroup per layer.
+constexpr int kCapGridRounds = 2;
+struct CapRound {
+  int32_t* prop;            // [L][T*K] proposals of the round (-1: none / no candidate)
+  int32_t* mask;            // [L][T] slots proposing in the round (bit k)
+  uint16_t* cnt;            // layout of the proposals (grid rounds only)
+  int32_t* segsum;
+  int32_t* counts;          // [L][N]
+  int32_t* offsets;         // [L][N+1]
+  int32_t* perm;            // [L][T*K]
+  int32_t* inv;             // [L][T*K] position of each proposal in its expert's bucket
+};
 struct CapArgs {
   int32_t* idx;             // [L][T][Kt] top-K in, capacity-limited out (-1 = dropped)
   float* w;                 // [L][T][Kt] weights, renormalised for changed tokens
@@ -96,7 +116,12 @@ struct CapArgs {
   int32_t* list0;           // [L][T*K] pending slots, two buffers
   int32_t* list1;
   int32_t* stats;           // [L][2] rerouted, dropped, or nullptr
-  int L, T, N, K, Kt, Nb, cap;
+  const int32_t* flag;      // [L] the layer has an expert over capacity
+  CapRound round[kCapGridRounds + 1];  // round[r] = round r+1
+  int32_t* list_e;          // [L][T*K] first workgroup round's list: proposed experts
+  int32_t* rd;              // [L][3] rerouted / dropped / left pending by the grid rounds
+  int32_t* segsum;          // [L][nseg][Nb] cleared for the final layout
+  int L, T, N, K, Kt, Nb, cap, nseg, nsb, nlb;
 };
 hipError_t launch_capacity(const CapArgs& c, hipStream_t s);
 

@@ -335,11 +335,24 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
 
   // keys and scores for the capacity-limited rounds (candidates beyond top-K)
   if (live && a.key_out != nullptr) {
+    float ko[EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      if (e0 + j < N) {
-        a.key_out[row_off + e0 + j] = eligible ? key[j] + 0.f : NEG_INF;  // -0 -> +0
-        a.s_out[row_off + e0 + j] = s[j];
+    for (int j = 0; j < EPL; ++j) ko[j] = eligible ? key[j] + 0.f : NEG_INF;  // -0 -> +0
+    if (EPL % 4 == 0 && full && (N & 3) == 0) {  // 16-byte stores
+#pragma unroll
+      for (int j = 0; j < EPL; j += 4) {
+        *reinterpret_cast<float4*>(a.key_out + row_off + e0 + j) =
+            make_float4(ko[j], ko[j + 1], ko[j + 2], ko[j + 3]);
+        *reinterpret_cast<float4*>(a.s_out + row_off + e0 + j) =
+            make_float4(s[j], s[j + 1], s[j + 2], s[j + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        if (e0 + j < N) {
+          a.key_out[row_off + e0 + j] = ko[j];
+          a.s_out[row_off + e0 + j] = s[j];
+        }
       }
     }
   }
