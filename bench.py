@@ -13,8 +13,9 @@ step streams its batch from HBM.
 Prints ONE JSON line with the throughput (routed tokens/s, from K
 uninstrumented steps), the roofline of the dominant kernel (the gate GEMM:
 HIP events around its launch on the route's stream, over a second pass of K
-steps, since the events themselves cost a few us per step) and the CPU
-oracle timed on the host cores.
+steps, since the events themselves cost a few us per step; less the time an
+empty event pair reads on the same stream) and the CPU oracle timed on the
+host cores.
 """
 import argparse
 import ctypes
@@ -62,15 +63,22 @@ def parse():
 COPY_BYTES = 1 << 30
 
 
-def summarize_trace(d, out, command):
+def summarize_trace(d, out, command, steps=None, warmup=None):
+    """Per-kernel table from a rocprofv3 --kernel-trace --stats directory; with
+    the profiled run's steps and warmup, also the gate GEMM over the
+    event-timed pass (its last `steps` launches of the route), the figure the
+    bench line's roofline uses."""
     import csv
     import glob
+    import statistics
 
     stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     rows = list(csv.DictReader(open(stats[0])))
     lines = ["# Kernel trace: bench.py on the DeepSeek-V3-style 16k-token batch", "",
              "Route steps (gate GEMM, selection, layout; warmup, value pass and event-timed "
-             "pass), then the local dispatch and weighted combine of the same batch.", "",
+             "pass), then the variants the bench line reports beside the route (dispatch and "
+             "combine, layout on routed and balanced ids, capacity-limited routing, balancing "
+             "step).", "",
              "Command (from /tmp, TMPDIR=/tmp):", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -79,6 +87,17 @@ def summarize_trace(d, out, command):
         lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if traces and steps:
+        tr = sorted(csv.DictReader(open(traces[0])), key=lambda r: int(r["Start_Timestamp"]))
+        g = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+             for r in tr if "gate_gemm" in r["Kernel_Name"]]
+        # launches: warmup, value pass, event-timed pass, then the variants'
+        ev = g[warmup + steps:warmup + 2 * steps]
+        lines += ["", f"Gate GEMM launches in order: {len(g)}; the event-timed pass "
+                      f"(launches {warmup + steps}..{warmup + 2 * steps - 1}): average "
+                      f"{statistics.mean(ev):.2f} us, median {statistics.median(ev):.2f} us; "
+                      f"value pass: average {statistics.mean(g[warmup:warmup + steps]):.2f} us."]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -333,7 +352,7 @@ def time_balance_step(moer, torch, wl, outs, stream, steps):
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.out, args.command)
+        summarize_trace(args.summarize_trace, args.out, args.command, args.steps, args.warmup)
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command)
@@ -445,11 +464,22 @@ def main():
         step(args.warmup + args.steps + i, ev.pairs[i])
     sync_streams()
     torch.cuda.synchronize()
-    gemm_ms = sum(ev.elapsed_ms(i) for i in range(args.steps)) / args.steps
+    event_ms = sum(ev.elapsed_ms(i) for i in range(args.steps)) / args.steps
+    # An event pair reads a few us even with nothing between its events (the
+    # markers' own processing): measure that on the same stream, the same
+    # number of times, and take it off the GEMM's bracketed time. The kernel
+    # trace of the same command shows the remainder is the kernel's duration.
+    for i in range(args.steps):
+        ev.record(ev.pairs[i][0], streams[0])
+        ev.record(ev.pairs[i][1], streams[0])
+    torch.cuda.synchronize()
+    pair_ms = sum(ev.elapsed_ms(i) for i in range(args.steps)) / args.steps
+    gemm_ms = event_ms - pair_ms
     ev.close()
     st = moer.decode_load_stats(stats.cpu())[0]
     print(f"[bench] {ms_step * 1e3:.1f} us/step (wall {t_wall / args.steps * 1e6:.1f} us), "
-          f"gate GEMM {gemm_ms * 1e3:.1f} us (event-timed pass); last imbalance "
+          f"gate GEMM {gemm_ms * 1e3:.1f} us ({event_ms * 1e3:.1f} us between its events, "
+          f"{pair_ms * 1e3:.1f} us for an empty pair); last imbalance "
           f"{st['imbalance']:.3f}", file=sys.stderr, flush=True)
 
     dc = None
@@ -496,7 +526,10 @@ def main():
                    "step": "route+load_stats+bias_update (fused)", "x_batches_rotated": len(xs),
                    "streams": nstream},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gate_gemm", "kernel_us": gemm_ms * 1e3,
+                     "event_pair_us": event_ms * 1e3, "empty_pair_us": pair_ms * 1e3,
+                     "alg_bytes": alg_bytes},
     }
     if dc is not None:
         line["dispatch_combine"] = dc
