@@ -49,6 +49,11 @@ def parse():
                         "route (reported beside the route, not part of its step)")
     p.add_argument("--no-forcible", action="store_true",
                    help="skip timing the layout on forcibly balanced ids against the routed ids")
+    p.add_argument("--report", metavar="OUT_MD",
+                   help="per-workload report (all five router shapes): medians and p10/p90 with "
+                        "the last-level cache flushed between calls, roofline shares, HIP-graph "
+                        "replay for the small batches, the collapse workload's 100-iteration "
+                        "balancing series, and the oracle at all cores and at one core")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration)")
     p.add_argument("--summarize-trace", metavar="DIR",
@@ -349,6 +354,278 @@ def time_balance_step(moer, torch, wl, outs, stream, steps):
     return res
 
 
+# ---------------------------------------------------------------- report
+HBM_PEAK_BPS = HBM_PEAK_GBS * 1e9
+MFMA_BF16_PEAK = 2.517e15  # dense bf16 flop/s (fp32 inputs use the same bound here)
+
+
+def algorithmic_bytes(wl):
+    """Bytes a route call must move: x, W_g and bias read; ids, weights, perm
+    (Kt x 12 B per token), counts, offsets and per-token entropy written."""
+    es = 2 if wl.dtype == 0 else 4
+    L, T, N, d, Kt, Nb = wl.n_layers, wl.T, wl.N, wl.d, wl.Kt, wl.Nb
+    return L * (T * d * es + N * d * es + N * 4 + T * Kt * 12 + Nb * 4 + (Nb + 1) * 4 + T * 4)
+
+
+def _pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+
+def _clocks():
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        keep = [l.strip() for l in r.stdout.splitlines() if "sclk" in l or "mclk" in l]
+        return keep[:4] or ["(rocm-smi printed no clock lines)"]
+    except (OSError, subprocess.SubprocessError) as exc:
+        return [f"(rocm-smi unavailable: {exc})"]
+
+
+def run_report(args):
+    import statistics
+
+    import torch
+
+    import oracle
+    import top_expert_routing_gate_amd as moer
+    import workloads
+
+    dev = torch.device("cuda:0")
+    out = ["# Router on every workload shape (one MI355X)", "",
+           f"Command: `python bench.py --report {args.out_report}` (from the repository root).",
+           "", "Clocks before: " + "; ".join(_clocks()), ""]
+    # read (not written) between calls: evicts the 256 MB last-level cache
+    # without leaving dirty lines to write back inside the next timed call
+    flush = torch.ones(256 << 20, dtype=torch.float16, device=dev)  # 512 MB
+    stream = torch.cuda.Stream()
+    ev = HipEvents(400)
+    empty = []
+    for i in range(200):
+        ev.record(ev.pairs[i][0], stream)
+        ev.record(ev.pairs[i][1], stream)
+    torch.cuda.synchronize()
+    empty = [ev.elapsed_ms(i) * 1e3 for i in range(200)]
+    pair_us = statistics.median(empty)
+    out += [f"An empty event pair reads {pair_us:.2f} us (median of 200); the per-call times "
+            "below are the event-bracketed medians less that.", "",
+            "| workload | L x T | reps | median us | p10 | p90 | gate GEMM us (median) | routed tokens/s "
+            "| roofline us | % of roofline | oracle tokens/s (all cores) | oracle tokens/s (1 core) |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    graph_rows = []
+    order = ["tiny_softmax", "mixtral_top2", "dsv3_group", "collapse_balance", "decode_layers"]
+    for name in order:
+        wl = workloads.WORKLOADS[name]
+        print(f"[report] {name}: inputs", file=sys.stderr, flush=True)
+        W, b0, off, gen = workloads.make_router(wl)
+        x = workloads.make_hidden(wl, gen=gen)
+        L, T, N, Kt, Nb = wl.n_layers, wl.T, wl.N, wl.Kt, wl.Nb
+        xd, Wd = x.to(dev), W.to(dev)
+        bias = b0.clone().to(dev)
+        offd = None if off is None else off.to(dev)
+        desc = moer.make_desc(n_layers=L, T=T, d=wl.d, N=N, K=wl.K, n_groups=wl.n_groups,
+                              topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                              score_fn=wl.score_fn, dtype=wl.dtype)
+        i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+        outs = dict(topk_idx=torch.empty(L, T, Kt, **i32), topk_w=torch.empty(L, T, Kt, **f32),
+                    tok_entropy=torch.empty(L, T, **f32), agg_entropy=torch.empty(L, **f32),
+                    counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
+                    perm=torch.empty(L, T * Kt, **i32), inv_perm=torch.empty(L, T * Kt, **i32))
+        stats = torch.empty(L, 64, dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(1, moer.moer_route_workspace_bytes(desc)), dtype=torch.uint8,
+                         device=dev)
+        call = moer.PreparedRoute(desc, workspace=ws, stream=stream, x=xd, w_gate=Wd, bias=bias,
+                                  logit_offset=offd, load_stats=stats, bias_update=bias,
+                                  bias_update_u=1e-3, **outs)
+        reps = 50 if T * L >= 16384 else 200
+        # warm-up: 5 calls, then keep the chip busy for a few ms so the clocks
+        # are up before the first timed call
+        for _ in range(5):
+            call()
+        with torch.cuda.stream(stream):
+            for _ in range(20):
+                flush.max()
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        times, gemm = [], []
+        for i in range(reps):
+            with torch.cuda.stream(stream):
+                # the last-level cache holds none of the inputs; on the route's
+                # stream, outside the events
+                flush.max()
+            ev.record(ev.pairs[i][0], stream)
+            call()
+            ev.record(ev.pairs[i][1], stream)
+        torch.cuda.synchronize()
+        times = [ev.elapsed_ms(i) * 1e3 - pair_us for i in range(reps)]
+        for i in range(reps):
+            with torch.cuda.stream(stream):
+                flush.max()
+            call(ev.pairs[i][0], ev.pairs[i][1])
+        torch.cuda.synchronize()
+        gemm = [ev.elapsed_ms(i) * 1e3 - pair_us for i in range(reps)]
+        med = statistics.median(times)
+        t_roof = max(algorithmic_bytes(wl) / HBM_PEAK_BPS, 2.0 * L * T * N * wl.d / MFMA_BF16_PEAK)
+        # oracle: one layer (bounded sample at one core)
+        print(f"[report] {name}: oracle", file=sys.stderr, flush=True)
+        xs = x[0].float().numpy()
+        Ws = W[0].float().numpy()
+        bs = b0[0].numpy()
+        osel = None if off is None else off.numpy()
+
+        def oracle_rate(ntok):
+            t0 = time.perf_counter()
+            o = oracle.route(x=xs[:ntok], W=Ws, offset=osel, bias=bs, K=wl.K,
+                             score_fn=wl.score_fn, n_groups=wl.n_groups,
+                             topk_groups=wl.topk_groups, n_shared=wl.n_shared)
+            oracle.load_stats(o["counts"][:N])
+            oracle.bias_update(bs, o["counts"][:N], 1e-3)
+            return ntok / (time.perf_counter() - t0)
+
+        all_cores = oracle.num_threads()
+        r_all = oracle_rate(T)
+        oracle.set_num_threads(1)
+        r_one = oracle_rate(min(T, 1024))
+        oracle.set_num_threads(all_cores)
+        out.append(f"| {name} | {L} x {T} | {reps} | {med:.1f} | {_pct(times, 0.1):.1f} | "
+                   f"{_pct(times, 0.9):.1f} | {statistics.median(gemm):.1f} | "
+                   f"{L * T / (med * 1e-6) / 1e6:.1f} M | {t_roof * 1e6:.2f} | "
+                   f"{100 * t_roof / (med * 1e-6):.1f} | {r_all / 1e3:.1f} k ({all_cores}) | "
+                   f"{r_one / 1e3:.2f} k |")
+        if name in ("tiny_softmax", "decode_layers"):
+            graph_rows += graph_timing(moer, torch, wl, desc, xd, Wd, b0.to(dev), offd, ev,
+                                       pair_us, stream)
+        del xd, Wd, ws, outs
+    out += ["", "Oracle: one layer's batch at all cores (one core: the first min(T, 1024) "
+            "tokens), including load statistics and the bias update.", "",
+            "## HIP graph replay", "",
+            "The route call (no bias update, so replays repeat the same work) captured once "
+            "and replayed; every replay's outputs equal the eager call's.", "",
+            "| case | eager median us | graph replay median us |", "|---|---|---|"] + graph_rows
+    out += ["", "## Collapse workload: 100 balancing iterations", ""] + collapse_series(
+        moer, torch, workloads, ev, pair_us, stream)
+    out += ["", "Clocks after: " + "; ".join(_clocks())]
+    ev.close()
+    with open(args.out_report, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(f"[report] written to {args.out_report}", file=sys.stderr, flush=True)
+
+
+def graph_timing(moer, torch, wl, desc, x, W, bias, off, ev, pair_us, stream):
+    """Eager vs HIP-graph replay of one route call (the whole batch, and for
+    the layered workload also one layer alone)."""
+    import statistics
+
+    rows = []
+    cases = [("all layers", desc, x, W, bias)]
+    if wl.n_layers > 1:
+        d1 = moer.make_desc(n_layers=1, T=wl.T, d=wl.d, N=wl.N, K=wl.K, n_groups=wl.n_groups,
+                            topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                            score_fn=wl.score_fn, dtype=wl.dtype)
+        cases.append(("one layer", d1, x[:1].contiguous(), W[:1].contiguous(),
+                      bias[:1].contiguous()))
+    for label, d, xx, WW, bb in cases:
+        L, T, Kt, Nb = d.n_layers, d.T, wl.Kt, wl.Nb
+        dev = xx.device
+        i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+
+        def bufs():
+            return dict(topk_idx=torch.empty(L, T, Kt, **i32), topk_w=torch.empty(L, T, Kt, **f32),
+                        counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
+                        perm=torch.empty(L, T * Kt, **i32), inv_perm=torch.empty(L, T * Kt, **i32))
+        ws = torch.empty(max(1, moer.moer_route_workspace_bytes(d)), dtype=torch.uint8, device=dev)
+        eager_out, graph_out = bufs(), bufs()
+        eager = moer.PreparedRoute(d, workspace=ws, stream=stream, x=xx, w_gate=WW, bias=bb,
+                                   logit_offset=off, **eager_out)
+        gs = torch.cuda.Stream()
+        ws2 = torch.empty_like(ws)
+        cap = moer.PreparedRoute(d, workspace=ws2, stream=gs, x=xx, w_gate=WW, bias=bb,
+                                 logit_offset=off, **graph_out)
+        for _ in range(3):
+            eager()
+        with torch.cuda.stream(gs):
+            for _ in range(3):
+                cap()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            cap()
+        torch.cuda.synchronize()
+        reps = 200
+        for _ in range(50):
+            eager()
+        for i in range(reps):
+            ev.record(ev.pairs[i][0], stream)
+            eager()
+            ev.record(ev.pairs[i][1], stream)
+        torch.cuda.synchronize()
+        te = [ev.elapsed_ms(i) * 1e3 - pair_us for i in range(reps)]
+        with torch.cuda.stream(stream):
+            for i in range(reps):
+                ev.record(ev.pairs[i][0], stream)
+                g.replay()
+                ev.record(ev.pairs[i][1], stream)
+        torch.cuda.synchronize()
+        tg = [ev.elapsed_ms(i) * 1e3 - pair_us for i in range(reps)]
+        for k in eager_out:
+            assert torch.equal(eager_out[k], graph_out[k]), f"graph replay differs: {k}"
+        rows.append(f"| {wl.name}, {label} ({L} x {T}) | {statistics.median(te):.1f} | "
+                    f"{statistics.median(tg):.1f} |")
+        del g
+    return rows
+
+
+def collapse_series(moer, torch, workloads, ev, pair_us, stream):
+    """The collapse workload (celebrity offsets +3.0 on experts 2, 4, 7, 12)
+    routed 100 times with the fused sign-step bias update (u = 1e-3); x of
+    iteration i is drawn on the GPU from seed 1000 + i (the CPU recipe's 100
+    draws of 235 MB would take minutes)."""
+    import statistics
+
+    wl = workloads.WORKLOADS["collapse_balance"]
+    dev = torch.device("cuda:0")
+    W, b0, off, _ = workloads.make_router(wl)
+    Wd, bias, offd = W.to(dev), b0.clone().to(dev), off.to(dev)
+    L, T, N, Kt, Nb = wl.n_layers, wl.T, wl.N, wl.Kt, wl.Nb
+    desc = moer.make_desc(n_layers=L, T=T, d=wl.d, N=N, K=wl.K, n_groups=wl.n_groups,
+                          topk_groups=wl.topk_groups, score_fn=wl.score_fn, dtype=wl.dtype)
+    i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+    outs = dict(topk_idx=torch.empty(L, T, Kt, **i32), topk_w=torch.empty(L, T, Kt, **f32),
+                counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
+                perm=torch.empty(L, T * Kt, **i32))
+    stats = torch.empty(L, 64, dtype=torch.uint8, device=dev)
+    ws = torch.empty(moer.moer_route_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    x = torch.empty(L, T, wl.d, dtype=torch.bfloat16, device=dev)
+    call = moer.PreparedRoute(desc, workspace=ws, stream=stream, x=x, w_gate=Wd, bias=bias,
+                              logit_offset=offd, load_stats=stats, bias_update=bias,
+                              bias_update_u=1e-3, **outs)
+    rows = ["| iteration | imbalance (max/mean) | load entropy (bits) | celebrity share | "
+            "route us |", "|---|---|---|---|---|"]
+    celeb = list(wl.celebrities)
+    times = []
+    for i in range(100):
+        g = torch.Generator(device=dev).manual_seed(1000 + i)
+        x.copy_(torch.randn(L, T, wl.d, generator=g, device=dev).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        ev.record(ev.pairs[0][0], stream)
+        call()
+        ev.record(ev.pairs[0][1], stream)
+        torch.cuda.synchronize()
+        times.append(ev.elapsed_ms(0) * 1e3 - pair_us)
+        st = moer.decode_load_stats(stats.cpu())[0]
+        c = outs["counts"][0, :N].cpu()
+        share = float(c[celeb].sum()) / max(1, int(c.sum()))
+        if i % 10 == 0 or i == 99:
+            rows.append(f"| {i} | {st['imbalance']:.3f} | {st['h_load_bits']:.3f} | "
+                        f"{share:.3f} | {times[-1]:.1f} |")
+        if i % 25 == 0:
+            print(f"[report] collapse iteration {i}", file=sys.stderr, flush=True)
+    rows += ["", f"Median route call over the 100 iterations: {statistics.median(times):.1f} us "
+             "(bias updated in place by the same call)."]
+    return rows
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -356,6 +633,10 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command)
+        return
+    if args.report:
+        args.out_report = args.report
+        run_report(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the router is measured "

@@ -28,4 +28,5 @@ from .api import (  # noqa: F401
     route,
     scores,
     select,
+    set_num_threads,
 )

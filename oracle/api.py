@@ -73,6 +73,7 @@ def _load():
         lib.moero_balance_step.argtypes = [P, P, i32, i32, ctypes.c_float, ctypes.c_float, i32,
                                            P, P]
         lib.moero_num_threads.restype = ctypes.c_int
+        lib.moero_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -87,6 +88,10 @@ def _c(a, dt):
 
 def num_threads():
     return int(_load().moero_num_threads())
+
+
+def set_num_threads(n):
+    _load().moero_set_num_threads(int(n))
 
 
 def affinities(x, W, offset=None):

@@ -35,6 +35,14 @@ int moero_num_threads(void) {
 #endif
 }
 
+void moero_set_num_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}
+
 /* [P1] Mathematics: routing logits h_i = x·W_g, with W_g's rows the expert
  * vectors ([P2] routing: similarity of the hidden state with every expert's
  * embedding vector). The optional per-expert offset is added to the logit

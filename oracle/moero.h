@@ -168,6 +168,8 @@ void moero_balance_step(float* bias, const int32_t* counts, int32_t N, int32_t r
                         float alpha, int32_t every, float* loads, int32_t* calls);
 
 int moero_num_threads(void);
+/* Threads the OpenMP loops use from now on (timing at one core). */
+void moero_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
