@@ -150,9 +150,12 @@ def _distinct_dyadic_keys(rng, n):
 @pytest.mark.parametrize("N,G,Gk,K", [(8, 4, 2, 2), (8, 2, 1, 3), (12, 3, 2, 4), (16, 4, 2, 4),
                                       (16, 4, 3, 3), (16, 8, 4, 4), (6, 3, 1, 2), (16, 1, 1, 4)])
 def test_group_limited_topk_brute_force(N, G, Gk, K):
+    # 1250 random cases per shape (10^4 in all); fewer under the pin
+    # mutation check, which reruns this file once per planted mistake
     rng = np.random.default_rng(1000 + N * 31 + G * 7 + Gk * 3 + K)
+    n_cases = 150 if os.environ.get("MOERO_LIB") else 1250
     n_checked = 0
-    for _ in range(400):
+    for _ in range(n_cases):
         keys = _distinct_dyadic_keys(rng, N)
         bias = (rng.integers(-8, 8, size=N) / 1024.0).astype(np.float32)
         s32 = (keys - bias).astype(np.float32)
@@ -167,7 +170,7 @@ def test_group_limited_topk_brute_force(N, G, Gk, K):
         idx, w, _, _ = oracle.select(s32[None], s32[None].astype(np.float64), bias, K, G, Gk)
         assert idx[0].tolist() == chosen, (keys, bias)
         n_checked += 1
-    assert n_checked > 200
+    assert n_checked > n_cases // 2
 
 
 @pytest.mark.parametrize("N,K", [(4, 1), (8, 2), (64, 8), (256, 8)])

@@ -416,6 +416,48 @@ def test_collapse_balancing_lockstep():
     assert imb[-1] < imb[0]
 
 
+def test_collapse_free_running_hidden_mode():
+    """The collapse loop in HIDDEN mode, GPU and oracle each running free
+    (each updates its own bias from its own counts) for 30 batches. Every
+    batch, the GPU's decisions are checked against the oracle run with the
+    GPU's current bias (a token may differ only under the near-tie rule, and
+    the count differences are exactly those tokens'), and the GPU's bias
+    update against the oracle's update of the GPU's counts (bit-exact). Both
+    trajectories are reported."""
+    wl = workloads.scaled(WL["collapse_balance"], T=1024, d=1024)
+    W, b0, off, _ = workloads.make_router(wl)
+    Wd, offd = W.to(DEV), off.to(DEV)
+    b_gpu = b0.clone().to(DEV)
+    b_free = b0[0].numpy().copy()
+    kw = dict(K=wl.K, score_fn=wl.score_fn, n_groups=wl.n_groups, topk_groups=wl.topk_groups)
+    traj_gpu, traj_free = [], []
+    for i in range(30):
+        x = workloads.make_hidden(wl, seed=1000 + i)
+        b_before = _np(b_gpu[0]).copy()
+        out = moer.route(x.to(DEV), Wd, bias=b_gpu, logit_offset=offd, bias_update=b_gpu,
+                         bias_update_u=1e-3, want_entropy=False, **kw)
+        torch.cuda.synchronize()
+        xs, Ws = x[0].float().numpy(), W[0].float().numpy()
+        shadow = oracle.route(x=xs, W=Ws, offset=off.numpy(), bias=b_before, **kw)
+        gi = _np(out["topk_idx"][0])
+        diff = ~(gi == shadow["idx"]).all(axis=1)
+        assert np.all(~diff | (shadow["gap"] < 1e-3)), f"batch {i}: beyond the near-tie rule"
+        gc = _np(out["counts"][0])[:wl.N]
+        expect = shadow["counts"][:wl.N].astype(np.int64)
+        for t in np.nonzero(diff)[0]:
+            np.add.at(expect, gi[t], 1)
+            np.add.at(expect, shadow["idx"][t], -1)
+        assert (gc == expect).all(), f"batch {i}: counts not explained by near ties"
+        assert (_np(b_gpu[0]) == oracle.bias_update(b_before, gc, 1e-3)).all(), f"batch {i}"
+        free = oracle.route(x=xs, W=Ws, offset=off.numpy(), bias=b_free, **kw)
+        b_free = oracle.bias_update(b_free, free["counts"][:wl.N], 1e-3)
+        traj_gpu.append(oracle.load_stats(gc)["imbalance"])
+        traj_free.append(oracle.load_stats(free["counts"][:wl.N])["imbalance"])
+    say("  imbalance, GPU free-running:    " + " ".join(f"{v:.2f}" for v in traj_gpu[::5]))
+    say("  imbalance, oracle free-running: " + " ".join(f"{v:.2f}" for v in traj_free[::5]))
+    assert traj_gpu[-1] < traj_gpu[0] and traj_free[-1] < traj_free[0]
+
+
 # ------------------------------------------- balancing-rule variants
 @pytest.mark.parametrize("wl", [
     workloads.scaled(WL["mixtral_top2"], T=600),
