@@ -4,9 +4,18 @@
  * Three calls make up the router's hot path:
  *   moer_route        gate affinities -> scores -> bias-aware group-limited
  *                     top-k -> combine weights -> routing entropy ->
- *                     dispatch layout (counts, offsets, stable permutation)
+ *                     dispatch layout (counts, offsets, stable permutation);
+ *                     optionally a per-expert capacity with rerouting, and
+ *                     the two calls below fused in
  *   moer_load_stats   load statistics of the realised per-expert counts
  *   moer_bias_update  sign-step update of the per-expert selection bias
+ * and around it:
+ *   moer_balance_step        other balancing rules (proportional update,
+ *                            moving-average loads, update period)
+ *   moer_dispatch /          the single-device dispatch of token rows to their
+ *   moer_combine             experts and the weighted combine back
+ *   moer_balanced_indices    forcible-balance expert ids (an upper bound)
+ *   moer_hotspot_accumulate  per-layer, per-expert token counts over batches
  *
  * The method is the one described on these web pages (cited by title and
  * section throughout):

@@ -478,16 +478,4 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   }
 }
 
-// Column sums of q over a wavefront's 4 rows: rows 0+1 and 2+3, then the two
-// pairs; both lanes of a pair add the same two operands, so every lane ends
-// with the bitwise-same sum. Must be called by all 64 lanes together.
-template <int EPL>
-__device__ __forceinline__ void wave_column_sums(const float (&q)[EPL], float (&col)[EPL]) {
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const float h = q[j] + __shfl_xor(q[j], 16, kWave);
-    col[j] = h + __shfl_xor(h, 32, kWave);
-  }
-}
-
 }  // namespace moer
