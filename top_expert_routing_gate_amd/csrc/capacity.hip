@@ -65,17 +65,22 @@ __device__ __forceinline__ unsigned long long shfl_u64(unsigned long long v, int
 }
 
 // Per-token candidate lists for tokens with a slot rejected in round 0.
+// SN: sort width, a power of two >= the most experts a token can be eligible
+// for (the kept groups' experts); the eligible entries are packed into the
+// first SN places before the sort.
+template <int SN>
 __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) {
+  static_assert(SN >= kWave && SN <= kSortN, "sort width");
+  __shared__ unsigned long long pack[kRankWaves][SN];
   const int lane = threadIdx.x & 63;
   const int layer = blockIdx.y;
   {
-    // clear the grid rounds' segment totals and the reroute/drop counters
+    // clear the grid rounds' segment totals
     const int64_t g = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * gridDim.y * blockDim.x;
     const int64_t nseg = (int64_t)c.L * c.nseg * c.N;
     for (int r = 0; r < kCapGridRounds; ++r)
       for (int64_t i = g; i < nseg; i += stride) c.round[r].segsum[i] = 0;
-    for (int64_t i = g; i < 3 * (int64_t)c.L; i += stride) c.rd[i] = 0;
   }
   const int t = blockIdx.x * kRankWaves + (threadIdx.x >> 6);
   if (t >= c.T || c.flag[layer] == 0) return;
@@ -102,27 +107,41 @@ __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) 
   }
 
   // (order(key), 0xFFFF - id): larger = earlier in decision order; 0 = not
-  // eligible (or absent)
-  unsigned long long v[kSortN / kWave];
+  // eligible (or absent). Eligible entries are packed (in expert order) into
+  // the wavefront's LDS row, then element i of the sort is pack[i].
   const float* key = c.key + tok * N;
+  unsigned long long* row = pack[threadIdx.x >> 6];
   int n_el = 0;
 #pragma unroll
   for (int r = 0; r < kSortN / kWave; ++r) {
     const int e = r * kWave + lane;
     const float k = e < N ? key[e] : -__builtin_inff();
     const bool el = k > -__builtin_inff();
-    v[r] = el ? ((unsigned long long)float_order(k) << 16) | (unsigned)(0xFFFF - e) : 0ull;
-    n_el += el ? 1 : 0;
+    const unsigned long long m = __ballot(el);
+    const int pos = n_el + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+    // more than SN only with non-finite scores (unspecified results): stay in bounds
+    if (el && pos < SN) row[pos] = ((unsigned long long)float_order(k) << 16) | (unsigned)(0xFFFF - e);
+    n_el += __builtin_popcountll(m);  // the same in every lane
+  }
+  n_el = n_el < SN ? n_el : SN;
+  // a wavefront's LDS operations complete in order; keep the compiler from
+  // moving the reads above the writes
+  asm volatile("" ::: "memory");
+  unsigned long long v[SN / kWave];
+#pragma unroll
+  for (int r = 0; r < SN / kWave; ++r) {
+    const int i = r * kWave + lane;
+    v[r] = i < n_el ? row[i] : 0ull;
   }
   // bitonic sort, descending, of element i = r*64 + lane
 #pragma unroll
-  for (int k = 2; k <= kSortN; k <<= 1) {
+  for (int k = 2; k <= SN; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
       if (j >= kWave) {
         const int rj = j / kWave;
 #pragma unroll
-        for (int r = 0; r < kSortN / kWave; ++r) {
+        for (int r = 0; r < SN / kWave; ++r) {
           if (r & rj) continue;
           const int i = r * kWave + lane;
           const bool desc = (i & k) == 0;
@@ -133,7 +152,7 @@ __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) 
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < kSortN / kWave; ++r) {
+        for (int r = 0; r < SN / kWave; ++r) {
           const int i = r * kWave + lane;
           const unsigned long long o = shfl_xor_u64(v[r], j);
           const bool lower = (lane & j) == 0;
@@ -144,10 +163,9 @@ __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) 
       }
     }
   }
-  for (int o = 32; o > 0; o >>= 1) n_el += __shfl_xor(n_el, o, kWave);
   uint8_t* list = c.ranked + tok * kMaxExperts;
 #pragma unroll
-  for (int r = 0; r < kSortN / kWave; ++r) {
+  for (int r = 0; r < SN / kWave; ++r) {
     const int i = r * kWave + lane;
     if (i < n_el) list[i] = (uint8_t)(0xFFFF - (unsigned)(v[r] & 0xFFFF));
   }
@@ -158,7 +176,7 @@ __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) 
   const int ci = rejected ? K + j : 0;
   int e = -1;
 #pragma unroll
-  for (int r = 0; r < kSortN / kWave; ++r) {
+  for (int r = 0; r < SN / kWave; ++r) {
     const unsigned long long x = shfl_u64(v[r], ci & 63);  // element ci
     if (r == (ci >> 6)) e = (int)(0xFFFF - (unsigned)(x & 0xFFFF));
   }
@@ -181,39 +199,55 @@ __device__ __forceinline__ int held_before(const CapArgs& c, int layer, int e, i
 // their expert fits under what the expert holds; the rejected slots of a
 // token take its next candidates, in slot order, as the next round's
 // proposals. One thread per token.
-__global__ __launch_bounds__(256) void cap_accept_kernel(CapArgs c, int r) {
+constexpr int kAcceptThreads = 64;  // small workgroups: the work is latency, spread it wide
+
+__global__ __launch_bounds__(kAcceptThreads) void cap_accept_kernel(CapArgs c, int r) {
+  __shared__ int held[kMaxExperts];
   const int layer = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.x * kAcceptThreads + threadIdx.x;
   if (c.flag[layer] == 0) return;
   const int K = c.K, Kt = c.Kt;
+  for (int e = threadIdx.x; e < c.N; e += kAcceptThreads) held[e] = held_before(c, layer, e, r);
+  __syncthreads();
   int rerouted = 0, dropped = 0, pending = 0;
   if (t < c.T) {
     const size_t tok = (size_t)layer * c.T + t;
     const CapRound& cur = c.round[r];
     const CapRound& nxt = c.round[r + 1];
     const int m = cur.mask[tok];
+    int nx = c.next[tok];
+    const int ne = c.n_el[tok];
     const int32_t* off = cur.offsets + (size_t)layer * (c.N + 1);
+    // every slot's proposal, rank and bucket start loaded together (the
+    // latency chain is three loads deep, not three per slot)
+    int pe[kMaxSlots], pos[kMaxSlots], base[kMaxSlots];
+#pragma unroll
+    for (int k = 0; k < kMaxSlots; ++k) {
+      const bool on = k < K && ((m >> k) & 1);
+      pe[k] = on ? cur.prop[tok * K + k] : -1;
+      pos[k] = on ? cur.inv[tok * K + k] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxSlots; ++k) base[k] = pe[k] >= 0 ? off[pe[k]] : 0;
     int rej = 0;
-    for (int k = 0; k < K; ++k) {
-      if (!((m >> k) & 1)) continue;
-      const int e = cur.prop[tok * K + k];
+    bool touched = false;
+#pragma unroll
+    for (int k = 0; k < kMaxSlots; ++k) {
+      if (k >= K || !((m >> k) & 1)) continue;
+      const int e = pe[k];
       if (e < 0) {
         c.idx[tok * Kt + k] = -1;
-        c.changed[tok] = 1;
+        touched = true;
         ++dropped;
-        continue;
-      }
-      const int rank = cur.inv[tok * K + k] - off[e];
-      if (held_before(c, layer, e, r) + rank < c.cap) {
+      } else if (held[e] + (pos[k] - base[k]) < c.cap) {
         c.idx[tok * Kt + k] = e;
-        c.changed[tok] = 1;
+        touched = true;
         ++rerouted;
       } else {
         rej |= 1 << k;
       }
     }
-    int nx = c.next[tok];
-    const int ne = c.n_el[tok];
+    if (touched) c.changed[tok] = 1;
     const uint8_t* list = c.ranked + tok * kMaxExperts;
     for (int k = 0; k < K; ++k) {
       int e = -1;
@@ -227,16 +261,20 @@ __global__ __launch_bounds__(256) void cap_accept_kernel(CapArgs c, int r) {
     nxt.mask[tok] = rej;
     pending = __builtin_popcount(rej);
   }
-  // reroute / drop / still-pending counts (integer atomics: order-independent)
+  // this workgroup's (one wavefront's) reroute / drop / still-pending counts,
+  // summed later by cap_rounds_kernel (one atomic per workgroup on the same
+  // three counters serialised at the cache)
+  static_assert(kAcceptThreads == kWave, "one wavefront per workgroup");
   for (int o = 32; o > 0; o >>= 1) {
     rerouted += __shfl_xor(rerouted, o, kWave);
     dropped += __shfl_xor(dropped, o, kWave);
     pending += __shfl_xor(pending, o, kWave);
   }
-  if ((threadIdx.x & 63) == 0 && (rerouted | dropped | pending)) {
-    atomicAdd(&c.rd[3 * layer], rerouted);
-    atomicAdd(&c.rd[3 * layer + 1], dropped);
-    if (r == kCapGridRounds - 1) atomicAdd(&c.rd[3 * layer + 2], pending);
+  if (threadIdx.x == 0) {
+    int32_t* part = c.part + (((size_t)r * c.L + layer) * gridDim.x + blockIdx.x) * 3;
+    part[0] = rerouted;
+    part[1] = dropped;
+    part[2] = pending;
   }
 }
 
@@ -280,8 +318,39 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
   uint8_t* changed = c.changed + (size_t)layer * T;
   int32_t* lists[2] = {c.list0 + (size_t)layer * A, c.list1 + (size_t)layer * A};
 
-  // rounds are left only where the grid rounds left slots pending
-  const bool any_over = c.flag[layer] != 0 && c.rd[3 * layer + 2] != 0;
+  // the grid rounds' counts (one record per accept workgroup); rounds are
+  // left only where they left slots pending
+  int grid_rr = 0, grid_dr = 0, grid_pend = 0;
+  if (c.flag[layer] != 0) {
+    const int nwg = (T + kAcceptThreads - 1) / kAcceptThreads;
+    for (int r = 0; r < kCapGridRounds; ++r) {
+      const int32_t* part = c.part + ((size_t)r * c.L + layer) * nwg * 3;
+      for (int w = tid; w < nwg; w += kRoundThreads) {
+        grid_rr += part[3 * w];
+        grid_dr += part[3 * w + 1];
+        if (r == kCapGridRounds - 1) grid_pend += part[3 * w + 2];
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    grid_rr += __shfl_xor(grid_rr, o, kWave);
+    grid_dr += __shfl_xor(grid_dr, o, kWave);
+    grid_pend += __shfl_xor(grid_pend, o, kWave);
+  }
+  if ((tid & 63) == 0) {
+    sh.red[0][tid >> 6] = grid_rr;
+    sh.red[1][tid >> 6] = grid_dr;
+    sh.wsum[tid >> 6] = grid_pend;
+  }
+  __syncthreads();
+  grid_rr = grid_dr = grid_pend = 0;
+  for (int w = 0; w < kRoundThreads / kWave; ++w) {
+    grid_rr += sh.red[0][w];
+    grid_dr += sh.red[1][w];
+    grid_pend += sh.wsum[w];
+  }
+  __syncthreads();  // red and wsum are reused
+  const bool any_over = c.flag[layer] != 0 && grid_pend != 0;
   int rerouted = 0, dropped = 0;
   if (any_over) {
     for (int e = tid; e < N; e += kRoundThreads) sh.held[e] = held_before(c, layer, e, kCapGridRounds);
@@ -292,9 +361,21 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
     const int32_t* mask = c.round[kCapGridRounds].mask + (size_t)layer * T;
     const int32_t* prop = c.round[kCapGridRounds].prop + (size_t)layer * A;
     int32_t* le = c.list_e + (size_t)layer * A;
+    constexpr int kBatch = 16;  // passes whose masks are loaded together
+    int mb[kBatch];
     for (int t0 = 0; t0 < T; t0 += kRoundThreads) {
+      const int q = (t0 / kRoundThreads) % kBatch;
+      if (q == 0) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int tu = t0 + u * kRoundThreads + wave * kWave + lane;
+          mb[u] = tu < T ? mask[tu] : 0;
+        }
+      }
       const int t = t0 + wave * kWave + lane;
-      const int m = t < T ? mask[t] : 0;
+      int m = 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) m = u == q ? mb[u] : m;
       const int n = __builtin_popcount(m);
       int x = n;  // inclusive scan over the wavefront's tokens
       for (int o = 1; o < kWave; o <<= 1) {
@@ -418,17 +499,16 @@ __global__ __launch_bounds__(kRoundThreads) void cap_rounds_kernel(CapArgs c) {
         rs += sh.red[0][w];
         ds += sh.red[1][w];
       }
-      const bool grid = c.flag[layer] != 0;  // the grid rounds counted too
-      c.stats[2 * layer] = rs + (grid ? c.rd[3 * layer] : 0);
-      c.stats[2 * layer + 1] = ds + (grid ? c.rd[3 * layer + 1] : 0);
+      c.stats[2 * layer] = rs + grid_rr;  // the grid rounds' counts too
+      c.stats[2 * layer + 1] = ds + grid_dr;
     }
   }
 }
 
 // Weights of the tokens whose slots changed: the placed routed slots'
 // scores over their sum (1/placed when the sum is 0); dropped slots 0.
-__global__ __launch_bounds__(256) void cap_weights_kernel(CapArgs c) {
-  const int64_t tok = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(kAcceptThreads) void cap_weights_kernel(CapArgs c) {
+  const int64_t tok = (int64_t)blockIdx.x * kAcceptThreads + threadIdx.x;
   if (tok >= (int64_t)c.L * c.T || c.flag[tok / c.T] == 0 || !c.changed[tok]) return;
   const int32_t* id = c.idx + tok * c.Kt;
   const float* s = c.s + tok * c.N;
@@ -448,8 +528,15 @@ __global__ __launch_bounds__(256) void cap_weights_kernel(CapArgs c) {
 
 hipError_t launch_capacity(const CapArgs& c, hipStream_t s) {
   if (c.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(cap_rank_kernel, dim3((c.T + kRankWaves - 1) / kRankWaves, c.L),
-                     dim3(kRankWaves * kWave), 0, s, c);
+  // sort width: the most experts a token can be eligible for, rounded up
+  const int grid_x = (c.T + kRankWaves - 1) / kRankWaves;
+  const int elig = c.G > 1 ? c.Gk * (c.N / c.G) : c.N;
+  if (elig <= 64)
+    hipLaunchKernelGGL(cap_rank_kernel<64>, dim3(grid_x, c.L), dim3(kRankWaves * kWave), 0, s, c);
+  else if (elig <= 128)
+    hipLaunchKernelGGL(cap_rank_kernel<128>, dim3(grid_x, c.L), dim3(kRankWaves * kWave), 0, s, c);
+  else
+    hipLaunchKernelGGL(cap_rank_kernel<256>, dim3(grid_x, c.L), dim3(kRankWaves * kWave), 0, s, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   for (int r = 0; r < kCapGridRounds; ++r) {
@@ -474,7 +561,8 @@ hipError_t launch_capacity(const CapArgs& c, hipStream_t s) {
     la.cap_flag = const_cast<int32_t*>(c.flag);
     e = launch_layout(la, c.L, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(cap_accept_kernel, dim3((c.T + 255) / 256, c.L), dim3(256), 0, s, c, r);
+    hipLaunchKernelGGL(cap_accept_kernel, dim3((c.T + kAcceptThreads - 1) / kAcceptThreads, c.L),
+                       dim3(kAcceptThreads), 0, s, c, r);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -482,7 +570,8 @@ hipError_t launch_capacity(const CapArgs& c, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)c.L * c.T;
-  hipLaunchKernelGGL(cap_weights_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, c);
+  hipLaunchKernelGGL(cap_weights_kernel, dim3((unsigned)((n + kAcceptThreads - 1) / kAcceptThreads)),
+                     dim3(kAcceptThreads), 0, s, c);
   return hipGetLastError();
 }
 

@@ -94,8 +94,8 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
     o += align_up(L * sizeof(int32_t) + 16);
     p.off_liste = o;    // the workgroup rounds' first list: proposed experts
     o += align_up(LT * d.K * sizeof(int32_t) + 16);
-    p.off_rd = o;       // rerouted / dropped / left pending by the grid rounds
-    o += align_up(3 * L * sizeof(int32_t) + 16);
+    p.off_rd = o;       // rerouted / dropped / left pending, per accept workgroup
+    o += align_up(moer::kCapGridRounds * L * ((d.T + 63) / 64) * 3 * sizeof(int32_t) + 16);
     for (int r = 0; r <= moer::kCapGridRounds; ++r) {  // per round: proposals ...
       Plan::Round& q = p.round[r];
       q.prop = o;
@@ -384,11 +384,13 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
       c.round[r].inv = i32(q.inv);
     }
     c.list_e = i32(p.off_liste);
-    c.rd = i32(p.off_rd);
+    c.part = i32(p.off_rd);
     c.segsum = segsum;
     c.nseg = p.nseg;
     c.nsb = p.nsb;
     c.nlb = p.nlb;
+    c.G = d.n_groups;
+    c.Gk = d.topk_groups;
     c.L = L;
     c.T = d.T;
     c.N = d.N;

@@ -119,9 +119,10 @@ struct CapArgs {
   const int32_t* flag;      // [L] the layer has an expert over capacity
   CapRound round[kCapGridRounds + 1];  // round[r] = round r+1
   int32_t* list_e;          // [L][T*K] first workgroup round's list: proposed experts
-  int32_t* rd;              // [L][3] rerouted / dropped / left pending by the grid rounds
+  int32_t* part;            // [rounds][L][accept workgroups][3] rerouted / dropped / pending
   int32_t* segsum;          // [L][nseg][Nb] cleared for the final layout
   int L, T, N, K, Kt, Nb, cap, nseg, nsb, nlb;
+  int G, Gk;                // expert groups and groups kept (eligible experts <= Gk*N/G)
 };
 hipError_t launch_capacity(const CapArgs& c, hipStream_t s);
 
