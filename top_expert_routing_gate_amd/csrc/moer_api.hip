@@ -253,12 +253,13 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
       return fail(MOER_EHIP, "%s: %s", #expr, hipGetErrorString(he));           \
   } while (0)
 
-  // segment counters start at zero: cleared by the pipelined gate GEMM when
-  // it runs, else by a fill kernel
+  // segment counters start at zero: cleared by the gate GEMM when the
+  // pipelined bf16 kernel or the fp32 kernel runs, else by a fill kernel
   int32_t* segsum = reinterpret_cast<int32_t*>(ws + p.off_seg);
   const int n_seg = L * p.nseg * p.Nb;
-  const bool gemm_clears = hidden && d.dtype == MOER_BF16 &&
-                           moer::gate_gemm_clears(L, d.T, d.d, d.N, p.ksplit);
+  const bool gemm_clears =
+      hidden && d.T > 0 &&
+      (d.dtype == MOER_BF16 ? moer::gate_gemm_clears(L, d.T, d.d, d.N, p.ksplit) : true);
   if (!gemm_clears) MOER_CHECK(moer::launch_zero_ints(segsum, n_seg, s));
 
   // a1: gate affinities
@@ -273,7 +274,9 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     else
       MOER_CHECK(moer::launch_gate_gemm_f32(static_cast<const float*>(io->x),
                                             static_cast<const float*>(io->w_gate), hbuf, L, d.T,
-                                            d.d, d.N, s));
+                                            d.d, d.N,
+                                            gemm_clears ? segsum : nullptr,
+                                            gemm_clears ? n_seg : 0, s));
     if (io->ev_gemm_end) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_end), s));
     h = hbuf;
   }

@@ -70,7 +70,7 @@ hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int 
 bool gate_gemm_clears(int L, int T, int d, int N, int ksplit);
 hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s);
 hipError_t launch_gate_gemm_f32(const float* x, const float* w, float* h, int L, int T, int d,
-                                int N, hipStream_t s);
+                                int N, int32_t* zero, int n_zero, hipStream_t s);
 hipError_t launch_score_topk(const ScoreArgs& a, int L, hipStream_t s);
 // Row-per-token selection (writes the block histograms itself).
 int route_rows_epl(int N);
