@@ -696,7 +696,8 @@ def main():
         k = i % nstream
         wait = done[(i - 1) % nstream] if (nstream > 1 and i > 0) else None
         calls[k][i % len(xs)](*(events or (None, None)), ev_select_wait=wait)
-        ev.record(done[k], streams[k])
+        if nstream > 1:  # only the overlapped schedule chains steps through events
+            ev.record(done[k], streams[k])
 
     def sync_streams():
         # every stream has reached the end of what was enqueued so far
