@@ -9,7 +9,7 @@
 // from the selection kernel or, for supplied ids, from layout_count below.
 // The same kernels add every block histogram into segsum[l][s][e], the
 // counts of segment s = 16 consecutive blocks (integer atomics: the sums do
-// not depend on the order). layout_scatter runs one workgroup per 128-token
+// not depend on the order). layout_scatter runs one workgroup per 64-token
 // layout block: an expert's total is the sum of its segments, and its
 // assignments before the block are the earlier segments plus the earlier
 // blocks of the block's own segment (at most 15 + 14 reads per expert). It
@@ -27,9 +27,9 @@ namespace moer {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBlocksPerLayoutBlock = kLayoutTokens / kRowTokens;  // 2
-constexpr int kMaxSlotsPerBlock = kLayoutTokens * kMaxSlots;       // 2048
-constexpr int kMaxChunks = kMaxSlotsPerBlock / 64;                 // 32
+constexpr int kBlocksPerLayoutBlock = kLayoutTokens / kRowTokens;  // 1
+constexpr int kMaxSlotsPerBlock = kLayoutTokens * kMaxSlots;       // 1024
+constexpr int kMaxChunks = kMaxSlotsPerBlock / 64;                 // 16
 static_assert(kLayoutTokens % kRowTokens == 0, "layout block = whole histogram blocks");
 static_assert(kThreads == kBalanceThreads, "the first layout workgroup runs the balance routines");
 
@@ -101,8 +101,21 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
   const int e = qd * 4;
   if (e < a.N) {
     if ((a.N & 3) == 0) {
-#pragma unroll 8
-      for (int r = rg; r < a.nsb; r += kGroups) {
+      // batches of kBatch rows: all their loads in flight before the adds,
+      // which still run in row order
+      constexpr int kBatch = 32;
+      int r = rg;
+      for (; r + (kBatch - 1) * kGroups < a.nsb; r += kBatch * kGroups) {
+        float4 qv[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+          qv[k] = *reinterpret_cast<const float4*>(cp + (size_t)(r + k * kGroups) * a.N + e);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          acc.x += qv[k].x; acc.y += qv[k].y; acc.z += qv[k].z; acc.w += qv[k].w;
+        }
+      }
+      for (; r < a.nsb; r += kGroups) {
         const float4 q = *reinterpret_cast<const float4*>(cp + (size_t)r * a.N + e);
         acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
       }
@@ -219,7 +232,7 @@ __device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* tot
                      a.bias_step, bal);
 }
 
-// Workgroups [0, nlb) place 128 tokens each; then, if requested, one
+// Workgroups [0, nlb) place 64 tokens each; then, if requested, one
 // workgroup for the batch-mean entropy and one for load balancing.
 __global__ __launch_bounds__(kThreads, 1) void layout_scatter_kernel(LayoutArgs a) {
   __shared__ int total[2 * kThreads];
@@ -246,6 +259,14 @@ __global__ __launch_bounds__(kThreads, 1) void layout_scatter_kernel(LayoutArgs 
   const size_t lbase = (size_t)layer * a.T * a.Kt;
   const int flat0 = t0 * a.Kt;
 
+  // the block's ids first: their loads overlap the totals' loads
+  constexpr int kIdsPerThread = kMaxSlotsPerBlock / kThreads;
+  int ids[kIdsPerThread];
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    ids[k] = i < nslot ? a.idx[lbase + flat0 + i] : -1;
+  }
   // per expert: all assignments, and those in tokens before this block
   load_totals(a, layer, blk, total, pre);
   for (int c = 0; c < nchunk; ++c)
@@ -262,13 +283,6 @@ __global__ __launch_bounds__(kThreads, 1) void layout_scatter_kernel(LayoutArgs 
   }
 
   // membership bitmaps: bit i of bits[c][e] <=> slot c*64+i of this block is e
-  constexpr int kIdsPerThread = kMaxSlotsPerBlock / kThreads;
-  int ids[kIdsPerThread];
-#pragma unroll
-  for (int k = 0; k < kIdsPerThread; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    ids[k] = i < nslot ? a.idx[lbase + flat0 + i] : -1;
-  }
 #pragma unroll
   for (int k = 0; k < kIdsPerThread; ++k) {
     const int i = threadIdx.x + k * kThreads;

@@ -14,7 +14,7 @@ constexpr int kMaxExperts = 256;    // N
 constexpr int kMaxSlots = 16;       // Kt
 constexpr int kMaxBuckets = kMaxExperts + kMaxSlots;
 constexpr int kRowTokens = 64;      // tokens per selection workgroup (= histogram block)
-constexpr int kLayoutTokens = 128;  // tokens per scatter workgroup (2 histogram blocks)
+constexpr int kLayoutTokens = 64;   // tokens per scatter workgroup (1 histogram block)
 constexpr int kSegBlocks = 16;       // histogram blocks per segment of the running totals
 
 // Everything a score/select launch needs (passed by value).
