@@ -75,8 +75,15 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   float v[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) v[j] = 0.f;
-  if (live) load_row<EPL>(a, row_off, split_stride, rl * EPL, v);
-  __syncthreads();  // histogram cleared
+  // The rows' loads go out in two halves: the first half's before the
+  // barrier (which also publishes the cleared histogram), the second half's
+  // after it. Every workgroup of the launch does the same, so the first
+  // halves' data arrives while only half of the launch's loads are in
+  // flight, and those rows are routed while the second halves stream in.
+  const bool first_half = row < kRowTokens / 2;
+  if (live && first_half) load_row<EPL>(a, row_off, split_stride, rl * EPL, v);
+  __syncthreads();  // histogram cleared; first-half rows loaded
+  if (live && !first_half) load_row<EPL>(a, row_off, split_stride, rl * EPL, v);
 
   const RowLds rs{cand[row], cand_s[row], slot_id[row], slot_s[row]};
   float q[EPL];
