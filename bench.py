@@ -60,6 +60,14 @@ def parse():
                    help="write a per-kernel table from a rocprofv3 --kernel-trace --stats dir")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="calibrated HBM bytes per gate-GEMM launch from two --pmc runs")
+    p.add_argument("--stage-run", action="store_true",
+                   help="route every workload shape STAGE_CALLS times (last-level cache flushed "
+                        "between calls), with a marker launch before each workload's warm-up "
+                        "and before its measured calls, for per-stage rocprofv3 runs")
+    p.add_argument("--summarize-stages", nargs=4,
+                   metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
+                   help="per-workload, per-stage table (us, HBM bytes and GB/s, MFMA rate) from "
+                        "a --kernel-trace run and three --pmc runs of --stage-run")
     p.add_argument("--command", default="", help="profiling command recorded in a summary")
     p.add_argument("--out", help="output file of a summary")
     return p.parse_args()
@@ -118,6 +126,163 @@ def _counter_rows(d, counter):
             if r["Counter_Name"] == counter:
                 out.append((r["Kernel_Name"], float(r["Counter_Value"])))
     return out
+
+
+MFMA_BF16_PEAK = 2.517e15  # MI355X dense bf16 matrix peak, flop/s
+STAGE_ORDER = ["tiny_softmax", "mixtral_top2", "dsv3_group", "collapse_balance", "decode_layers"]
+STAGE_WARMUP, STAGE_CALLS = 5, 20
+MARKER = "balanced_indices_kernel"  # the stage run's marker launch
+STAGES = [("gate_gemm", "gate GEMM"),
+          ("route_rows", "selection (scores, top-k, weights, entropy, histogram)"),
+          ("score_topk", "selection (scores, top-k, weights, entropy, histogram)"),
+          ("layout_count", "histogram of supplied ids"),
+          ("layout_scatter", "scan + scatter (+ batch entropy, statistics, bias update)"),
+          ("zero_ints", "clear counters")]
+
+
+def _stage_of(kernel):
+    for key, label in STAGES:
+        if key in kernel:
+            return label
+    return None
+
+
+def _split_stage_rows(rows):
+    """rows: (kernel name, value) in dispatch order. Returns {workload index:
+    [(name, value)]} for the measured calls: the run launches a marker before
+    each workload's warm-up and another before its measured calls."""
+    per, marks = {}, 0
+    for name, v in rows:
+        if MARKER in name:
+            marks += 1
+            continue
+        if marks > 0 and marks % 2 == 0:
+            per.setdefault(marks // 2 - 1, []).append((name, v))
+    return per
+
+
+def run_stage_calls(args):
+    """The route call of every workload shape (the bench step: route, fused
+    load statistics and bias update), STAGE_CALLS measured calls each after
+    STAGE_WARMUP warm-up calls, with a 512 MB read between calls so the
+    last-level cache holds none of the inputs; a 1 GiB copy first calibrates
+    the byte counters."""
+    import torch
+
+    import top_expert_routing_gate_amd as moer
+    import workloads
+
+    dev = torch.device("cuda:0")
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    bcopy = torch.empty_like(a)
+    bcopy.copy_(a)
+    torch.cuda.synchronize()
+    del a, bcopy
+    flush = torch.ones(256 << 20, dtype=torch.float16, device=dev)
+    for name in STAGE_ORDER:
+        wl = workloads.WORKLOADS[name]
+        print(f"[stages] {name}", file=sys.stderr, flush=True)
+        W, b0, off, gen = workloads.make_router(wl)
+        x = workloads.make_hidden(wl, gen=gen)
+        L, T, Kt, Nb = wl.n_layers, wl.T, wl.Kt, wl.Nb
+        desc = moer.make_desc(n_layers=L, T=T, d=wl.d, N=wl.N, K=wl.K, n_groups=wl.n_groups,
+                              topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                              score_fn=wl.score_fn, dtype=wl.dtype)
+        i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+        bias = b0.clone().to(dev)
+        outs = dict(topk_idx=torch.empty(L, T, Kt, **i32), topk_w=torch.empty(L, T, Kt, **f32),
+                    tok_entropy=torch.empty(L, T, **f32), agg_entropy=torch.empty(L, **f32),
+                    counts=torch.empty(L, Nb, **i32), offsets=torch.empty(L, Nb + 1, **i32),
+                    perm=torch.empty(L, T * Kt, **i32), inv_perm=torch.empty(L, T * Kt, **i32))
+        ws = torch.empty(max(1, moer.moer_route_workspace_bytes(desc)), dtype=torch.uint8,
+                         device=dev)
+        call = moer.PreparedRoute(desc, workspace=ws, x=x.to(dev), w_gate=W.to(dev), bias=bias,
+                                  logit_offset=None if off is None else off.to(dev),
+                                  load_stats=torch.empty(L, 64, dtype=torch.uint8, device=dev),
+                                  bias_update=bias, bias_update_u=1e-3, **outs)
+        for calls in (STAGE_WARMUP, STAGE_CALLS):
+            moer.balanced_indices(1, 1, 1, device=dev)  # marker
+            for _ in range(calls):
+                flush.max()
+                call()
+        torch.cuda.synchronize()
+    print("[stages] done", file=sys.stderr, flush=True)
+
+
+def summarize_stages(trace_dir, fetch_dir, write_dir, mfma_dir, out, command):
+    import csv
+    import glob
+    import statistics
+
+    traces = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    tr = sorted(csv.DictReader(open(traces[0])), key=lambda r: int(r["Start_Timestamp"]))
+    dur = _split_stage_rows([(r["Kernel_Name"],
+                              (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                             for r in tr])
+
+    def counter(d, name):
+        rows = []
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(fn)) if r["Counter_Name"] == name]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        return _split_stage_rows([(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]), copy
+
+    fetch, fcopy = counter(fetch_dir, "FETCH_SIZE")
+    write, wcopy = counter(write_dir, "WRITE_SIZE")
+    mops, _ = counter(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    # counters read KiB; scale each by what it reads for the known 1 GiB copy
+    fscale = COPY_BYTES / (max(fcopy) * 1024.0)
+    wscale = COPY_BYTES / (max(wcopy) * 1024.0)
+
+    def by_stage(rows):
+        acc = {}
+        for name, v in rows:
+            st = _stage_of(name)
+            if st is not None:
+                acc.setdefault(st, []).append(v)
+        return acc
+
+    lines = ["# Route stages on every workload shape: time, HBM bytes, matrix-core rate", "",
+             "Commands (from /tmp, TMPDIR=/tmp; R = repository root): one kernel-trace run and "
+             "three counter runs of the same program:", "", "```", command, "```", "",
+             f"Each workload: {STAGE_WARMUP} warm-up calls, then {STAGE_CALLS} measured calls of "
+             "the bench step (route + fused load statistics + bias update), with a 512 MB read "
+             "between calls so the last-level cache holds none of the inputs. Time per launch "
+             "comes from the kernel trace. Bytes per launch are FETCH_SIZE + WRITE_SIZE (HBM "
+             f"side of the L2). Each is scaled by what it reads for a plain 1 GiB copy "
+             f"(fetch x{fscale:.3f}, write x{wscale:.3f}). GB/s = bytes / time; peaks 8 TB/s HBM, "
+             "2.517 PFLOP/s dense bf16 (MFMA flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512).", "",
+             "| workload | stage | launches / call | us / launch | read MB | written MB | GB/s | "
+             "% of 8 TB/s | MFMA TFLOP/s | % of bf16 peak |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for i, name in enumerate(STAGE_ORDER):
+        if i not in dur:
+            continue
+        d_st, f_st = by_stage(dur[i]), by_stage(fetch.get(i, []))
+        w_st, m_st = by_stage(write.get(i, [])), by_stage(mops.get(i, []))
+        total = 0.0
+        for _, label in STAGES:
+            if label not in d_st:  # absent, or already reported (two kernels share a label)
+                continue
+            us = statistics.mean(d_st[label])
+            n = len(d_st[label]) / STAGE_CALLS
+            total += us * n
+            rb = statistics.mean(f_st[label]) * 1024.0 * fscale if label in f_st else float("nan")
+            wb = statistics.mean(w_st[label]) * 1024.0 * wscale if label in w_st else float("nan")
+            gbs = (rb + wb) / (us * 1e-6) / 1e9
+            mf = ""
+            if label in m_st and statistics.mean(m_st[label]) > 0:
+                tf = statistics.mean(m_st[label]) * 512 / (us * 1e-6)
+                mf = f"{tf / 1e12:.0f} | {100 * tf / MFMA_BF16_PEAK:.0f} %"
+            else:
+                mf = "— | —"
+            lines.append(f"| {name} | {label} | {n:g} | {us:.2f} | {rb / 1e6:.2f} | "
+                         f"{wb / 1e6:.2f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} % | {mf} |")
+            d_st.pop(label)
+        lines.append(f"| {name} | **sum of stages** | | **{total:.1f}** | | | | | | |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def summarize_traffic(fetch_dir, write_dir, out, command):
@@ -356,7 +521,7 @@ def time_balance_step(moer, torch, wl, outs, stream, steps):
 
 # ---------------------------------------------------------------- report
 HBM_PEAK_BPS = HBM_PEAK_GBS * 1e9
-MFMA_BF16_PEAK = 2.517e15  # dense bf16 flop/s (fp32 inputs use the same bound here)
+# MFMA_BF16_PEAK (above) also bounds fp32 inputs here
 
 
 def algorithmic_bytes(wl):
@@ -634,9 +799,15 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command)
         return
+    if args.summarize_stages:
+        summarize_stages(*args.summarize_stages, args.out, args.command)
+        return
     if args.report:
         args.out_report = args.report
         run_report(args)
+        return
+    if args.stage_run:
+        run_stage_calls(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the router is measured "
