@@ -72,7 +72,8 @@ extern "C" {
 typedef enum {
   MOER_OK = 0,
   MOER_EINVAL = 1,       /* invalid argument (see moer_last_error) */
-  MOER_EUNSUPPORTED = 2, /* valid, but a shape these kernels do not take */
+  MOER_EUNSUPPORTED = 2, /* reserved: valid, but a shape the kernels do not take
+                            (every descriptor that validates has a kernel today) */
   MOER_EWORKSPACE = 3,   /* workspace missing or smaller than required */
   MOER_EHIP = 4          /* the HIP runtime refused a launch */
 } moer_status;
@@ -114,7 +115,8 @@ typedef struct {
   int32_t d;           /* hidden size (HIDDEN mode); bf16 needs d % 8 == 0 */
   int32_t N;           /* routed experts, 1..256 */
   int32_t K;           /* routed experts chosen per token, 1..N */
-  int32_t n_groups;    /* G: N/G contiguous experts per group; 1 = no limit */
+  int32_t n_groups;    /* G: N/G contiguous experts per group (any N/G >= 2 that
+                          divides N); 1 = no limit */
   int32_t topk_groups; /* Gk: groups kept per token, 1..G, Gk*(N/G) >= K */
   int32_t n_shared;    /* shared-expert slots appended after the K routed */
   int32_t score_fn;    /* moer_score_fn */

@@ -88,13 +88,19 @@ def test_null_descriptor_and_io():
     assert st == moer.MOER_EINVAL
 
 
-def test_unsupported_group_geometry():
-    # 128 groups of 2 among 256 experts: valid for the method, not for these kernels
-    d = _desc(n_groups=128, topk_groups=64)
+@pytest.mark.parametrize("kw", [
+    dict(n_groups=128, topk_groups=64),           # 128 groups of 2 among 256 experts
+    dict(N=96, n_groups=8, topk_groups=4),         # groups of 12 (not a power of two)
+    dict(N=255, n_groups=17, topk_groups=3),       # groups of 15
+    dict(N=60, n_groups=20, topk_groups=3, K=6),   # groups of 3
+])
+def test_any_group_geometry_accepted(kw):
+    # every group size >= 2 that divides N is valid for the method and has a
+    # kernel: the descriptor passes, and the call stops at the empty io
+    d = _desc(**kw)
     st, msg = _route_raw(d)
-    assert st == moer.MOER_EUNSUPPORTED and "group size" in msg
-    d = _desc(N=96, n_groups=8, topk_groups=4)  # groups of 12 (not a power of two)
-    assert _route_raw(d)[0] == moer.MOER_EUNSUPPORTED
+    assert st == moer.MOER_EINVAL and "x and w_gate" in msg, msg
+    assert moer.moer_route_workspace_bytes(d) > 0
 
 
 def test_missing_buffers_and_workspace():

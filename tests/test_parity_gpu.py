@@ -550,3 +550,56 @@ def test_dailyaiworld_controller_loop():
         assert (_np(bias[0]) == b_ref).all(), f"batch {it}: bias"
     celeb = list(wl.celebrities)
     assert (b_ref[celeb] < 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Seeded random router shapes: expert counts, group geometries, K, shared
+# slots, token counts around the 32/64-token block edges, layers, score
+# functions and bias scales that the fixed cases above do not cover. A shape
+# these kernels refuse as unsupported (MOER_EUNSUPPORTED: a group width the
+# row kernels cannot split) is skipped; everything else must meet the
+# SCORES-mode (bit-exact) or HIDDEN-mode bars.
+
+def _random_router(i, hidden=False):
+    rng = np.random.default_rng(1000 + i)
+    N = int(rng.choice([1, 2, 3, 4, 7, 8, 16, 24, 32, 60, 64, 100, 128, 160, 200, 255, 256]))
+    divs = [g for g in range(1, N + 1) if N % g == 0 and (g == 1 or N // g >= 2)]
+    G = int(rng.choice(divs))
+    Gk = int(rng.integers(1, G + 1))
+    K = int(rng.integers(1, min(Gk * (N // G), 16) + 1))
+    n_shared = int(rng.integers(0, 16 - K + 1)) if rng.random() < 0.3 else 0
+    L = int(rng.choice([1, 1, 2, 3]))
+    T = int(rng.choice([1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 500, 1000, 2047, 2048,
+                        2049, 3001]))
+    score_fn = workloads.SIGMOID if rng.random() < 0.5 else workloads.SOFTMAX
+    bias_range = float(rng.choice([0.0, 0.01, 0.3]))
+    d = int(rng.choice([8, 40, 64, 72, 136, 264, 520, 1024])) if hidden else 64
+    dtype = workloads.F32 if hidden and rng.random() < 0.3 else workloads.BF16
+    if hidden:
+        T = min(T, 1000)
+    return workloads.Workload(f"random{i}", T=T, d=d, N=N, K=K, score_fn=score_fn, dtype=dtype,
+                              n_groups=G, topk_groups=Gk, n_shared=n_shared, n_layers=L,
+                              bias_range=bias_range, seed=2000 + i)
+
+
+def _run_or_skip(fn, wl):
+    try:
+        return fn()
+    except moer.MoerError as exc:
+        if exc.status == moer.MOER_EUNSUPPORTED:
+            pytest.skip(f"unsupported shape {wl}: {exc}")
+        raise
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_scores_mode_bit_exact_random_shapes(i):
+    wl = _random_router(i)
+    say(f"[scores/random {i}] {wl}")
+    _run_or_skip(lambda: _scores_case(wl, seed=3000 + i), wl)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_hidden_mode_random_shapes(i):
+    wl = _random_router(i, hidden=True)
+    say(f"[hidden/random {i}] {wl}")
+    _run_or_skip(lambda: _hidden_case(wl, wl.name), wl)

@@ -27,7 +27,6 @@ moer_status ok() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -123,12 +122,9 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
 
 // Which selection kernel takes this shape: 1 = one 16-lane row per token,
 // 2 = one wavefront per token, 0 = neither.
+// 1: the 16-lane row kernel; 2: one wavefront per token (any group size)
 int selection_path(const moer_route_desc& d) {
-  if (moer::route_rows_supports(d.N, d.n_groups)) return 1;
-  if (d.n_groups == 1) return 2;
-  const int gsz = d.N / d.n_groups;
-  const int E = moer::experts_per_lane(d.N);
-  return (gsz % E == 0 && is_pow2(gsz / E)) ? 2 : 0;
+  return moer::route_rows_supports(d.N, d.n_groups) ? 1 : 2;
 }
 
 moer_status validate_desc(const moer_route_desc* d) {
@@ -172,11 +168,6 @@ moer_status validate_desc(const moer_route_desc* d) {
   if (d->capacity < 0) return fail(MOER_EINVAL, "capacity must be >= 0 (got %d)", d->capacity);
   if (d->capacity > 0 && d->input == MOER_IN_INDICES)
     return fail(MOER_EINVAL, "a capacity needs HIDDEN or SCORES input (the candidates)");
-  if (d->input != MOER_IN_INDICES && selection_path(*d) == 0)
-    return fail(MOER_EUNSUPPORTED,
-                "group size %d with N=%d: these kernels need N/n_groups to be a power of two "
-                "multiple of the experts each lane holds",
-                gsz, d->N);
   return MOER_OK;
 }
 

@@ -13,7 +13,9 @@
 //  3. G > 1 ("DeepSeek-V3 Group-Limited Expert Routing", s.1 and s.3): the N
 //     keys are G contiguous groups; group score = fp32 sum of the group's two
 //     largest keys; the Gk best groups (score desc, group id asc) stay
-//     eligible, the others are masked out.
+//     eligible, the others are masked out. Groups that are a power-of-two
+//     number of lanes merge their lanes' top-2 by shuffles; any other group
+//     size (any N/G >= 2) goes through LDS: a lane scans whole groups.
 //  4. K rounds of a wave-wide argmax over the eligible keys, ordered by
 //     (key desc, expert id asc); the winner of round r fills slot r.
 //  5. Shared experts (same page, s.4: counted as routed slots) fill slots
@@ -44,13 +46,36 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Lane-aligned groups: every group is a power-of-two number of whole lanes.
+bool score_topk_lane_groups(int N, int G) {
+  const int gsz = N / G, E = experts_per_lane(N);
+  return gsz % E == 0 && ((gsz / E) & (gsz / E - 1)) == 0 && gsz / E <= kWave;
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-template <int E, bool GROUPED>
+// Group stage: none, lane-aligned power-of-two groups (shuffles), or any
+// group size (the wave's keys and group scores in LDS).
+enum { kNoGroups = 0, kLaneGroups = 1, kAnyGroups = 2 };
+
+// Orders the wave's LDS writes before its later LDS reads at compile time; a
+// wavefront's LDS operations are performed in program order.
+__device__ __forceinline__ void wave_lds_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int E, int GMODE>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(ScoreArgs a) {
+  constexpr bool GROUPED = GMODE != kNoGroups;
+  constexpr int kGW = GMODE == kAnyGroups ? kWavesPerBlock : 1;
   __shared__ float colsum[kWavesPerBlock][kMaxExperts];
+  __shared__ float gkey[kGW][GMODE == kAnyGroups ? kMaxExperts : 1];       // the token's keys
+  __shared__ float gscore[kGW][GMODE == kAnyGroups ? kMaxExperts / 2 : 1]; // group scores
+  __shared__ int gkeep[kGW][GMODE == kAnyGroups ? kMaxExperts / 2 : 1];    // group eligible
 
   const int layer = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -76,10 +101,11 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
     col[j] = 0.f;
   }
 
-  // Group geometry (GROUPED only): lanes per group and this lane's group.
+  // Group geometry (GROUPED only): group size, and for lane-aligned groups
+  // the lanes per group and this lane's group.
   const int gsz = GROUPED ? N / a.G : N;
-  const int lpg = GROUPED ? gsz / E : kWave;
-  const int my_group = GROUPED ? lane / lpg : 0;
+  const int lpg = GMODE == kLaneGroups ? gsz / E : kWave;
+  const int my_group = GMODE == kLaneGroups ? lane / lpg : 0;
 
   const int tbase = blockIdx.x * kRowTokens;
   for (int tt = wave; tt < kRowTokens; tt += kWavesPerBlock) {
@@ -136,7 +162,41 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
     }
 
     // 3. group-limited eligibility
-    if (GROUPED) {
+    if (GMODE == kAnyGroups) {
+      const int gw = GMODE == kAnyGroups ? wave : 0;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (lane * E + j < N) gkey[gw][lane * E + j] = key[j];
+      wave_lds_order();
+      // lane g (and g + 64) scores whole groups: the sum of the two largest keys
+      for (int g = lane; g < a.G; g += kWave) {
+        const float* gk = &gkey[gw][g * gsz];
+        float m1 = gk[0], m2 = NEG_INF;
+        for (int i = 1; i < gsz; ++i) {
+          m2 = fmaxf(m2, fminf(m1, gk[i]));
+          m1 = fmaxf(m1, gk[i]);
+        }
+        gscore[gw][g] = m1 + m2;
+      }
+      wave_lds_order();
+      // rank among all groups under (score desc, group id asc)
+      for (int g = lane; g < a.G; g += kWave) {
+        const float gs = gscore[gw][g];
+        int rank = 0;
+        for (int o = 0; o < a.G; ++o) {
+          const float og = gscore[gw][o];
+          rank += (og > gs || (og == gs && o < g)) ? 1 : 0;
+        }
+        gkeep[gw][g] = rank < a.Gk ? 1 : 0;
+      }
+      wave_lds_order();
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int e = lane * E + j;
+        if (e < N && gkeep[gw][e / gsz] == 0) key[j] = NEG_INF;
+      }
+      wave_lds_order();  // the next token's key writes come after these reads
+    } else if (GMODE == kLaneGroups) {
       float m1 = key[0], m2 = NEG_INF;
 #pragma unroll
       for (int j = 1; j < E; ++j) {
@@ -261,10 +321,13 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
 template <int E>
 hipError_t launch_e(const ScoreArgs& a, int L, hipStream_t s) {
   dim3 grid((a.T + kRowTokens - 1) / kRowTokens, L);
-  if (a.G > 1)
-    hipLaunchKernelGGL((score_topk_kernel<E, true>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
+  const dim3 block(kWavesPerBlock * kWave);
+  if (a.G > 1 && score_topk_lane_groups(a.N, a.G))
+    hipLaunchKernelGGL((score_topk_kernel<E, kLaneGroups>), grid, block, 0, s, a);
+  else if (a.G > 1)
+    hipLaunchKernelGGL((score_topk_kernel<E, kAnyGroups>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((score_topk_kernel<E, false>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
+    hipLaunchKernelGGL((score_topk_kernel<E, kNoGroups>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
