@@ -41,6 +41,11 @@ CASES = [
     (workloads.scaled(WL["dsv3_group"], T=777), 9, 3.0),              # tight: drops
     (workloads.scaled(WL["decode_layers"], n_layers=4), None, 3.0),   # shared slot
     (workloads.scaled(WL["dsv3_group"], T=300, N=64, n_groups=1, topk_groups=1, K=4), None, 2.0),
+    # group geometries of the one-wave-per-token selection kernel: groups of 4
+    # (two whole lanes each), of 12 and of 20 (scored through LDS)
+    (workloads.scaled(WL["dsv3_group"], T=640, N=128, n_groups=32, topk_groups=8), None, 3.0),
+    (workloads.scaled(WL["dsv3_group"], T=900, N=96, n_groups=8, topk_groups=4, K=6), None, 3.0),
+    (workloads.scaled(WL["dsv3_group"], T=700, N=200, n_groups=10, topk_groups=3), 40, 3.0),
 ]
 
 
