@@ -8,7 +8,9 @@ DeepSeek-V3-style router (16384 tokens, d=7168, 256 experts in 8 groups of
   call, the load statistics and the in-place sign-step bias update).
 Inputs are resident in HBM before timing; x rotates over three distinct
 batches (705 MB in all, larger than the 256 MB last-level cache) so each
-step streams its batch from HBM.
+step streams its batch from HBM. After the W warm-up steps, untimed steps
+continue for CLOCK_RAMP_S of wall time so the timed region starts at the
+chip's steady clocks.
 
 Prints ONE JSON line with the throughput (routed tokens/s, from K
 uninstrumented steps), the roofline of the dominant kernel (the gate GEMM:
@@ -74,6 +76,24 @@ def parse():
 
 
 COPY_BYTES = 1 << 30
+# After idling, the chip needs ~10-20 ms of load to reach its steady clocks
+# (measured on the 16k-token batch: the first 100 back-to-back steps average
+# 97 us, then 86-87 us); untimed calls fill this much wall time before any
+# timed region.
+CLOCK_RAMP_S = 0.06
+
+
+def clock_ramp(torch, fn, seconds=CLOCK_RAMP_S, batch=20):
+    """Untimed calls of fn() until `seconds` of wall time have passed; returns
+    how many were made."""
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(batch):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
 
 
 def summarize_trace(d, out, command, steps=None, warmup=None):
@@ -202,6 +222,8 @@ def run_stage_calls(args):
                                   bias_update=bias, bias_update_u=1e-3, **outs)
         for calls in (STAGE_WARMUP, STAGE_CALLS):
             moer.balanced_indices(1, 1, 1, device=dev)  # marker
+            if calls == STAGE_WARMUP:
+                clock_ramp(torch, call)  # between the markers: not measured
             for _ in range(calls):
                 flush.max()
                 call()
@@ -603,13 +625,8 @@ def run_report(args):
                                   logit_offset=offd, load_stats=stats, bias_update=bias,
                                   bias_update_u=1e-3, **outs)
         reps = 50 if T * L >= 16384 else 200
-        # warm-up: 5 calls, then keep the chip busy for a few ms so the clocks
-        # are up before the first timed call
-        for _ in range(5):
-            call()
-        with torch.cuda.stream(stream):
-            for _ in range(20):
-                flush.max()
+        # warm-up: calls until the clocks are steady, then 10 more
+        clock_ramp(torch, call)
         for _ in range(10):
             call()
         torch.cuda.synchronize()
@@ -885,7 +902,15 @@ def main():
         step(i)
     sync_streams()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps",
+    ramp_i = [args.warmup]
+
+    def ramp_step():
+        step(ramp_i[0])
+        ramp_i[0] += 1
+
+    n_ramp = clock_ramp(torch, ramp_step)
+    print(f"[bench] warmup done ({args.warmup} steps, then {n_ramp} more over "
+          f"{CLOCK_RAMP_S * 1e3:.0f} ms for the clocks); timing {args.steps} steps",
           file=sys.stderr, flush=True)
     # timed region 1 (value): K uninstrumented steps between two barriers; the
     # start event is on the first step's stream (the other stream's first
@@ -967,6 +992,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp": {"steps": n_ramp, "ms": CLOCK_RAMP_S * 1e3},
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
