@@ -81,6 +81,14 @@ def test_scores_mode_bit_exact_full_size(name):
     _scores_case(wl, seed=100)
 
 
+def test_scores_mode_bit_exact_many_segments():
+    # 100,003 tokens: 1563 histogram blocks in 98 segments of running totals
+    # (the layout sums them in chunks of 32), ragged last block
+    wl = workloads.scaled(WL["dsv3_group"], T=100003)
+    say(f"[scores/many segments] T={wl.T}")
+    _scores_case(wl, seed=11)
+
+
 @pytest.mark.parametrize("wl", [
     workloads.scaled(WL["dsv3_group"], T=1000),
     workloads.scaled(WL["mixtral_top2"], T=333),
