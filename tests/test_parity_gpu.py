@@ -611,3 +611,61 @@ def test_hidden_mode_random_shapes(i):
     wl = _random_router(i, hidden=True)
     say(f"[hidden/random {i}] {wl}")
     _run_or_skip(lambda: _hidden_case(wl, wl.name), wl)
+
+
+# ---------------------------------------------------------------------------
+# Non-finite inputs: the results are unspecified, but every id stays in range
+# and the layout stays a consistent stable permutation of the ids produced.
+
+def _check_consistent(out, wl):
+    for l in range(wl.n_layers):
+        gi = _np(out["topk_idx"][l])
+        routed, shared = gi[:, :wl.K], gi[:, wl.K:]
+        assert ((routed >= -1) & (routed < wl.N)).all()
+        assert (shared == wl.N + np.arange(wl.n_shared)).all()
+        ids = np.where(gi >= 0, gi, -1)
+        if (ids < 0).any():  # capacity drops: the layout skips them
+            valid = ids[ids >= 0]
+            assert _np(out["counts"][l]).sum() == valid.size
+            continue
+        _check_layout(out, l, ids, wl.Nb)
+
+
+@pytest.mark.parametrize("capacity", [0, 1])
+@pytest.mark.parametrize("wl", [
+    workloads.scaled(WL["dsv3_group"], T=700),
+    workloads.scaled(WL["decode_layers"], n_layers=2, T=130),
+    workloads.scaled(WL["dsv3_group"], T=200, N=96, n_groups=8, topk_groups=4, K=6),
+], ids=lambda w: f"{w.name}-T{w.T}-N{w.N}")
+def test_non_finite_scores_stay_in_range(wl, capacity):
+    say(f"[non-finite scores] {wl} capacity={capacity}")
+    rng = np.random.default_rng(5)
+    s = rng.random((wl.n_layers, wl.T, wl.N)).astype(np.float32)
+    mask = rng.random(s.shape)
+    s[mask < 0.02] = np.nan
+    s[(mask >= 0.02) & (mask < 0.04)] = np.inf
+    s[(mask >= 0.04) & (mask < 0.05)] = -np.inf
+    s[0, :3] = np.nan  # whole rows of NaN
+    cap = moer.expert_capacity(wl.T, wl.K, wl.N) if capacity else 0
+    out = moer.route(scores=torch.from_numpy(s).to(DEV), K=wl.K, score_fn=wl.score_fn,
+                     n_groups=wl.n_groups, topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                     capacity=cap)
+    torch.cuda.synchronize()
+    _check_consistent(out, wl)
+    if cap:
+        assert _np(out["counts"])[:, :wl.N].max() <= cap
+
+
+def test_non_finite_hidden_states_stay_in_range():
+    wl = workloads.scaled(WL["dsv3_group"], T=300, d=512)
+    say(f"[non-finite hidden] {wl}")
+    inp = workloads.make_inputs(wl)
+    x = inp["x"].clone()
+    x[0, 5, 7] = float("inf")
+    x[0, 9, :] = float("nan")
+    x[0, 11, 3] = -float("inf")
+    out = moer.route(x.to(DEV), inp["W"].to(DEV), K=wl.K, score_fn=wl.score_fn,
+                     n_groups=wl.n_groups, topk_groups=wl.topk_groups,
+                     bias=inp["bias"].to(DEV), want_h=True)
+    torch.cuda.synchronize()
+    _check_consistent(out, wl)

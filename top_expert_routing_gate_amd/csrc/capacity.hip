@@ -116,7 +116,12 @@ __global__ __launch_bounds__(kRankWaves* kWave) void cap_rank_kernel(CapArgs c) 
   for (int r = 0; r < kSortN / kWave; ++r) {
     const int e = r * kWave + lane;
     const float k = e < N ? key[e] : -__builtin_inff();
-    const bool el = k > -__builtin_inff();
+    // eligible: not -inf (masked or absent) and not NaN. Decided on the bits:
+    // the float compare k > -inf has been lowered as an ordered compare for
+    // the store below and an unordered one for the ballot, which counted NaN
+    // keys that were never stored.
+    const uint32_t kb = __float_as_uint(k);
+    const bool el = kb != 0xFF800000u && (kb & 0x7FFFFFFFu) <= 0x7F800000u;
     const unsigned long long m = __ballot(el);
     const int pos = n_el + __builtin_popcountll(m & ((1ull << lane) - 1ull));
     // more than SN only with non-finite scores (unspecified results): stay in bounds

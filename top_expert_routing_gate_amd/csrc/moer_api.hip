@@ -121,8 +121,7 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
 }
 
 // Which selection kernel takes this shape: 1 = one 16-lane row per token,
-// 2 = one wavefront per token, 0 = neither.
-// 1: the 16-lane row kernel; 2: one wavefront per token (any group size)
+// 2 = one wavefront per token (any group size).
 int selection_path(const moer_route_desc& d) {
   return moer::route_rows_supports(d.N, d.n_groups) ? 1 : 2;
 }

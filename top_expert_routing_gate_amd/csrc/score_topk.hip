@@ -250,10 +250,13 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void score_topk_kernel(Scor
         if (key[j] > bv) { bv = key[j]; bj = j; bs = s[j]; }
       }
       const float M = wave_max(bv);
-      const unsigned long long hit = __ballot(bv == M);
+      // lanes past the experts hold -inf keys: they may tie M only when every
+      // real key is -inf or NaN (non-finite input, unspecified result); the
+      // winner is then a real expert all the same
+      const unsigned long long hit = __ballot(bv == M && lane * E < N);
       const int L = hit ? __builtin_ctzll(hit) : 0;
       const int jw = __builtin_amdgcn_readlane(bj, L);
-      sel_e[r] = L * E + jw;
+      sel_e[r] = min(L * E + jw, N - 1);
       sel_s[r] = readlane_f(bs, L);
       if (lane == L) {
 #pragma unroll
