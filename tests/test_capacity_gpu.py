@@ -148,3 +148,35 @@ def test_capacity_hidden_mode_invariants():
     dropped = int((ci < 0).sum())
     assert _np(capped["cap_stats"][0]).tolist() == [moved, dropped]
     assert moved > 0
+
+
+def test_capacity_only_some_layers_overflow():
+    # layer 0 skewed (experts over capacity), layer 1 forcibly balanced (every
+    # expert exactly T*K/N, under the capacity), layer 2 skewed again: the
+    # capacity kernels must rework layers 0 and 2 and leave layer 1 as routed
+    wl = workloads.scaled(WL["dsv3_group"], T=1024, n_layers=3, n_groups=1, topk_groups=1)
+    cap = moer.expert_capacity(wl.T, wl.K, wl.N)
+    s32 = _skewed_scores(wl, seed=21)
+    bal = np.full((wl.T, wl.N), 0.1, dtype=np.float32)
+    for t in range(wl.T):
+        for k in range(wl.K):
+            bal[t, (t * wl.K + k) % wl.N] = 0.9 - 0.01 * k
+    s32[1] = bal
+    say(f"[capacity/mixed layers] T={wl.T} N={wl.N} K={wl.K} cap={cap}")
+    out = moer.route(scores=torch.from_numpy(s32).to(DEV), K=wl.K, score_fn=wl.score_fn,
+                     capacity=cap)
+    plain = moer.route(scores=torch.from_numpy(s32).to(DEV), K=wl.K, score_fn=wl.score_fn)
+    torch.cuda.synchronize()
+    for l in range(wl.n_layers):
+        idx, w, rr, dr = oracle.capacity_route(s32[l], s32[l].astype(np.float64), None, wl.K,
+                                               cap, 1, 1, 0)
+        assert (_np(out["topk_idx"][l]) == idx).all(), f"layer {l}: ids differ"
+        assert np.allclose(_np(out["topk_w"][l]), w, rtol=1e-6, atol=1e-7)
+        assert _np(out["cap_stats"][l]).tolist() == [rr, dr]
+        counts, offsets, perm, inv = oracle.layout(idx, wl.Nb)
+        assert (_np(out["perm"][l]) == perm).all() and (_np(out["inv_perm"][l]) == inv).all()
+        assert counts.max() <= cap
+    assert _np(out["cap_stats"][1]).tolist() == [0, 0]
+    for key in ("topk_idx", "topk_w", "perm", "inv_perm", "counts", "offsets"):
+        assert torch.equal(out[key][1], plain[key][1]), f"layer 1 {key} changed"
+    assert _np(out["cap_stats"][0])[0] > 0 and _np(out["cap_stats"][2])[0] > 0
