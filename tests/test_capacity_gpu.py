@@ -163,10 +163,23 @@ def test_capacity_only_some_layers_overflow():
             bal[t, (t * wl.K + k) % wl.N] = 0.9 - 0.01 * k
     s32[1] = bal
     say(f"[capacity/mixed layers] T={wl.T} N={wl.N} K={wl.K} cap={cap}")
+    b0 = workloads.make_bias(wl.N, 3, 0.01, wl.n_layers)
+    bias = b0.clone().to(DEV)
     out = moer.route(scores=torch.from_numpy(s32).to(DEV), K=wl.K, score_fn=wl.score_fn,
-                     capacity=cap)
+                     capacity=cap, want_load_stats=True, bias_update=bias, bias_update_u=1e-3)
     plain = moer.route(scores=torch.from_numpy(s32).to(DEV), K=wl.K, score_fn=wl.score_fn)
     torch.cuda.synchronize()
+    # statistics and the sign step from the final (capacity-limited) counts,
+    # applied once per layer
+    for l in range(wl.n_layers):
+        ids = _np(out["topk_idx"][l]).ravel()
+        final = np.bincount(ids[ids >= 0], minlength=wl.N)[:wl.N]
+        st = moer.decode_load_stats(out["load_stats"][l:l + 1].cpu())[0]
+        ref = oracle.load_stats(final)
+        assert st["total"] == ref["total"] and st["max_load"] == ref["max_load"]
+        expect = oracle.bias_update(b0[l].numpy(), final, 1e-3)
+        assert np.array_equal(_np(bias[l]), np.asarray(expect, dtype=np.float32)), f"layer {l}"
+
     for l in range(wl.n_layers):
         idx, w, rr, dr = oracle.capacity_route(s32[l], s32[l].astype(np.float64), None, wl.K,
                                                cap, 1, 1, 0)
