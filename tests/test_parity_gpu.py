@@ -669,3 +669,42 @@ def test_non_finite_hidden_states_stay_in_range():
                      bias=inp["bias"].to(DEV), want_h=True)
     torch.cuda.synchronize()
     _check_consistent(out, wl)
+
+
+@pytest.mark.parametrize("case", ["capacity", "indices", "decode_layers", "any_groups"])
+def test_workspace_contents_do_not_matter(case):
+    # the caller's workspace may hold anything: a zero-filled one and one of
+    # random bytes give bitwise-identical outputs
+    if case == "decode_layers":
+        wl = workloads.scaled(WL["decode_layers"], n_layers=5, T=100)
+    elif case == "any_groups":
+        wl = workloads.scaled(WL["dsv3_group"], T=500, N=96, n_groups=8, topk_groups=4, K=6)
+    else:
+        wl = workloads.scaled(WL["dsv3_group"], T=900)
+    L = wl.n_layers
+    logits = workloads.make_logits(wl.T, wl.N, 77, n_layers=L).double().numpy()
+    logits[..., :4] += 3.0  # a few experts over capacity
+    s32 = np.stack([oracle.scores(logits[l], wl.score_fn).astype(np.float32) for l in range(L)])
+    kw = dict(K=wl.K, score_fn=wl.score_fn, n_groups=wl.n_groups, topk_groups=wl.topk_groups,
+              n_shared=wl.n_shared, want_load_stats=True)
+    if case == "indices":
+        ids = torch.from_numpy(np.stack([oracle.route(s32=s32[l], K=wl.K, score_fn=wl.score_fn,
+                                                      n_groups=wl.n_groups,
+                                                      topk_groups=wl.topk_groups)["idx"]
+                                         for l in range(L)]).astype(np.int32))
+        kw = dict(K=wl.K, N=wl.N, idx_in=ids.to(DEV), want_load_stats=True)
+    else:
+        kw["scores"] = torch.from_numpy(s32).to(DEV)
+        if case == "capacity":
+            kw["capacity"] = moer.expert_capacity(wl.T, wl.K, wl.N)
+    runs = []
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    for fill in ("zeros", "random"):
+        ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)  # ample for these shapes
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, (ws.numel(),), dtype=torch.uint8, generator=gen))
+        out = moer.route(workspace=ws, **kw)
+        torch.cuda.synchronize()
+        runs.append({k: v.cpu().clone() for k, v in out.items() if torch.is_tensor(v)})
+    for k in runs[0]:
+        assert torch.equal(runs[0][k], runs[1][k]), f"{case}: {k} depends on the workspace"
