@@ -31,7 +31,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
-GEMM_SRC = os.path.join(ROOT, "top_expert_routing_gate_amd", "csrc", "gate_gemm.hip")
+# the gate GEMM kernel's sources: a change to any of them voids the counters
+GEMM_SRCS = [os.path.join(ROOT, "top_expert_routing_gate_amd", "csrc", f)
+             for f in ("gate_gemm.hip", "gemm_pipeline.hpp", "moer_internal.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_gemm_dsv3_traffic.json")
 METRIC = "routed tokens/s, 16k tok × 256 experts top-8; % of MFMA/HBM roofline"
 
@@ -368,8 +370,11 @@ class HipEvents:
 
 
 def gemm_source_hash():
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

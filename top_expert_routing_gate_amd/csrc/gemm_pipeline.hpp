@@ -1,5 +1,5 @@
 // Pipelined bf16 gate GEMM tile (d a multiple of 64 per depth range): the
-// main loop shared by the plain gate GEMM and the fused GEMM + routing kernel.
+// producer/consumer main loop of the gate GEMM.
 //
 // "MoE Routing Entropy vs Expert Saturation" (dailyaiworld), Mathematics:
 // the routing logits are h_i = x · W_g; its listing builds the gate as
