@@ -54,9 +54,8 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   __shared__ int slot_id[kRowTokens][kMaxSlots];
   __shared__ float slot_s[kRowTokens][kMaxSlots];
   __shared__ int hist[kMaxBuckets];
-  __shared__ __attribute__((aligned(16))) float colq[kRowTokens][kRowLanes * EPL];
-  constexpr int kParts = kThreads / (kRowLanes * EPL) < 4 ? kThreads / (kRowLanes * EPL) : 4;
-  __shared__ float colp[kParts > 0 ? kParts : 1][kRowLanes * EPL];
+  constexpr int kWaves = kThreads / kWave;
+  __shared__ __attribute__((aligned(16))) float colw[kWaves][kRowLanes * EPL];
 
   const int N = a.N, T = a.T;
   const int Nb = N + a.n_shared;
@@ -89,9 +88,23 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   float q[EPL];
   route_row<EPL, GROUPED, MODE, LPG>(a, layer, t, live, v, lc, rs, hist, q);
   if (a.colpart != nullptr) {
-    // this token's q (zero for tokens past T) for the block's column sums
+    // the wavefront's column sums of q over its 4 rows (zero for tokens past
+    // T), (row0 + row1) + (row2 + row3), by lane swaps between rows and
+    // between wave halves; every lane adds the same operands in the same order
+    float cs[EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) colq[row][rl * EPL + j] = q[j];
+    for (int j = 0; j < EPL; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[j]),
+                                                      __float_as_uint(q[j]), false, false);
+      const float pair = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
+                                                      __float_as_uint(pair), false, false);
+      cs[j] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    }
+    if (lane < kRowLanes) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) colw[threadIdx.x >> 6][rl * EPL + j] = cs[j];
+    }
   }
   __syncthreads();
   if (a.cnt != nullptr) {
@@ -106,22 +119,11 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
       if (hist[e] != 0) atomicAdd(&seg[e], hist[e]);
   }
   if (a.colpart != nullptr) {
-    // column sums of q over the 64 rows, in a fixed order: kParts partial
-    // sums over consecutive rows, then the partials in order
-    constexpr int kW = kRowLanes * EPL;
-    constexpr int kRowsPerPart = kRowTokens / kParts;
-    if (threadIdx.x < kParts * kW) {
-      const int e = threadIdx.x % kW, part = threadIdx.x / kW;
-      float acc = colq[part * kRowsPerPart][e];
-#pragma unroll 8
-      for (int r = 1; r < kRowsPerPart; ++r) acc += colq[part * kRowsPerPart + r][e];
-      colp[part][e] = acc;
-    }
-    __syncthreads();
+    // the block's column sums: the wavefronts' sums in wavefront order
     for (int e = threadIdx.x; e < N; e += kThreads) {
-      float acc = colp[0][e];
+      float acc = colw[0][e];
 #pragma unroll
-      for (int p = 1; p < kParts; ++p) acc += colp[p][e];
+      for (int w = 1; w < kWaves; ++w) acc += colw[w][e];
       a.colpart[((size_t)layer * gridDim.x + blockIdx.x) * N + e] = acc;
     }
   }
