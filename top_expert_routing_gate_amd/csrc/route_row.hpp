@@ -284,9 +284,12 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   ssum = row_sum(ssum);
   slog = row_sum(slog);
   if (MODE == kSoftmax) slog += log2_hw(inv_z) * ssum;
+  // hardware reciprocal and log2 (about 1 ulp each), well inside the 1e-4
+  // bit entropy tolerance
+  const float rs_sum = ssum > 0.f ? rcp_hw(ssum) : 0.f;
   if (live && rl == 0 && a.tok_entropy != nullptr)
-    a.tok_entropy[(size_t)layer * T + t] = ssum > 0.f ? log2f(ssum) - slog / ssum : 0.f;
-  const float inv_s = (live && ssum > 0.f) ? 1.f / ssum : 0.f;
+    a.tok_entropy[(size_t)layer * T + t] = ssum > 0.f ? log2_hw(ssum) - slog * rs_sum : 0.f;
+  const float inv_s = live ? rs_sum : 0.f;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) q[j] = s[j] * inv_s;
 
