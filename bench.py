@@ -72,6 +72,10 @@ def parse():
                    metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
                    help="per-workload, per-stage table (us, HBM bytes and GB/s, MFMA rate) from "
                         "a --kernel-trace run and three --pmc runs of --stage-run")
+    p.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                   help="per-launch averages of every counter in these --pmc runs for the "
+                        "gate GEMM, selection and layout kernels, with the memory-path "
+                        "figures derived from them")
     p.add_argument("--command", default="", help="profiling command recorded in a summary")
     p.add_argument("--out", help="output file of a summary")
     return p.parse_args()
@@ -305,6 +309,87 @@ def summarize_stages(trace_dir, fetch_dir, write_dir, mfma_dir, out, command):
                          f"{wb / 1e6:.2f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} % | {mf} |")
             d_st.pop(label)
         lines.append(f"| {name} | **sum of stages** | | **{total:.1f}** | | | | | | |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+N_CU, N_XCD = 256, 8  # MI355X compute units and accelerator dies
+COUNTER_KERNELS = [("gate_gemm", "gate GEMM"), ("route_rows", "selection"),
+                   ("layout_scatter", "scan + scatter")]
+
+
+def _all_counter_rows(d):
+    import csv
+    import glob
+
+    out = []
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(fn)):
+            out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_counters(dirs, out, command):
+    """Per-launch counter averages per kernel, and what follows from them:
+    the mean L2 read latency seen by the L1s (latency sum / requests), the
+    mean number of L2 reads in flight per CU (latency sum / (CUs x cycles))
+    and each unit's busy or stall share of a CU's cycles. Cycles per launch
+    are GRBM_GUI_ACTIVE / accelerator dies (it is summed over them)."""
+    avg = {}
+    for d in dirs:
+        rows = _all_counter_rows(d)
+        for key, _ in COUNTER_KERNELS:
+            for c in sorted({c for n, c, _ in rows if key in n}):
+                v = [x for n, cc, x in rows if key in n and cc == c]
+                avg[(key, c)] = sum(v) / len(v)
+    counters = sorted({c for _, c in avg})
+    lines = ["# Memory-path counters per launch: gate GEMM, selection, scan + scatter", "",
+             "Commands (from /tmp, TMPDIR=/tmp; R = repository root), one counter group per run:",
+             "", "```", command, "```", "",
+             "| counter | " + " | ".join(lab for _, lab in COUNTER_KERNELS) + " |",
+             "|---|" + "---|" * len(COUNTER_KERNELS)]
+    for c in counters:
+        cells = [f"{avg[(k, c)]:,.0f}" if (k, c) in avg else "—" for k, _ in COUNTER_KERNELS]
+        lines.append(f"| {c} | " + " | ".join(cells) + " |")
+
+    def derived(k):
+        g = lambda c: avg.get((k, c))  # noqa: E731
+        cyc = g("GRBM_GUI_ACTIVE")
+        res = []
+        if cyc:
+            cyc /= N_XCD
+            res.append(("cycles per launch (per die)", f"{cyc:,.0f}"))
+        req, lat = g("TCP_TCC_READ_REQ_sum"), g("TCP_TCC_READ_REQ_LATENCY_sum")
+        if req and lat:
+            res.append(("L2 read latency, mean (cycles)", f"{lat / req:.0f}"))
+            if cyc:
+                res.append(("L2 reads in flight per CU, mean", f"{lat / (N_CU * cyc):.0f}"))
+        hit, miss = g("TCC_HIT_sum"), g("TCC_MISS_sum")
+        if hit is not None and miss:
+            res.append(("L2 hit rate", f"{100 * hit / (hit + miss):.1f} %"))
+        if cyc:
+            for c, lab in (("TA_TA_BUSY_sum", "TA busy"),
+                           ("TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA stalled by the L1"),
+                           ("TD_TD_BUSY_sum", "TD busy"),
+                           ("TD_TC_STALL_sum", "TD waiting for the L1"),
+                           ("TCP_PENDING_STALL_CYCLES_sum", "L1 stalled on pending L2 data"),
+                           ("TCP_UTCL1_STALL_INFLIGHT_MAX_sum",
+                            "L1 stalled at the translation in-flight limit")):
+                if g(c) is not None:
+                    res.append((lab + " (share of CU cycles)", f"{100 * g(c) / (N_CU * cyc):.0f} %"))
+        return res
+
+    lines += ["", "Derived (MI355X: 256 CUs on 8 dies):", "",
+              "| figure | " + " | ".join(lab for _, lab in COUNTER_KERNELS) + " |",
+              "|---|" + "---|" * len(COUNTER_KERNELS)]
+    per = {k: dict(derived(k)) for k, _ in COUNTER_KERNELS}
+    names = []
+    for k, _ in COUNTER_KERNELS:
+        for n, _ in derived(k):
+            if n not in names:
+                names.append(n)
+    for n in names:
+        lines.append(f"| {n} | " + " | ".join(per[k].get(n, "—") for k, _ in COUNTER_KERNELS) + " |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -823,6 +908,9 @@ def main():
         return
     if args.summarize_stages:
         summarize_stages(*args.summarize_stages, args.out, args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.out, args.command)
         return
     if args.report:
         args.out_report = args.report

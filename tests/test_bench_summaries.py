@@ -109,3 +109,33 @@ def test_traffic_summary(tmp_path):
     assert res["fetch_scale"] == pytest.approx(2.0) and res["write_scale"] == pytest.approx(1.0)
     assert res["bytes_per_launch"] == pytest.approx(1000 * 1024 * 2 + 100 * 1024)
     assert res["gate_gemm_sha256_16"] == bench.gemm_source_hash()
+
+
+def test_counter_summary(tmp_path):
+    # one launch each of the GEMM and the selection kernel per counter run
+    seq = [GEMM, SEL]
+    vals = {"GRBM_GUI_ACTIVE": {GEMM: 8 * 1000.0, SEL: 8 * 500.0},
+            "TCP_TCC_READ_REQ_sum": {GEMM: 4000.0, SEL: 100.0},
+            "TCP_TCC_READ_REQ_LATENCY_sum": {GEMM: 4000.0 * 600, SEL: 100.0 * 1200},
+            "TCC_HIT_sum": {GEMM: 3.0, SEL: 1.0}, "TCC_MISS_sum": {GEMM: 1.0, SEL: 1.0},
+            "TA_TA_BUSY_sum": {GEMM: 256 * 750.0, SEL: 0.0}}
+    dirs = []
+    for i, (c, v) in enumerate(vals.items()):
+        d = str(tmp_path / f"c{i}")
+        _write_counter(d, seq, c, lambda n, v=v: v[n])
+        dirs.append(d)
+    out = str(tmp_path / "counters.md")
+    bench.summarize_counters(dirs, out, "cmd")
+    rows = {}
+    for l in open(out).read().splitlines():
+        cells = [c.strip() for c in l.strip().strip("|").split("|")]
+        if len(cells) == 4:
+            rows[cells[0]] = cells[1:]
+    assert rows["GRBM_GUI_ACTIVE"][0] == "8,000"
+    assert rows["cycles per launch (per die)"][:2] == ["1,000", "500"]
+    assert rows["L2 read latency, mean (cycles)"][:2] == ["600", "1200"]
+    # latency sum / (256 CUs x cycles): 2.4e6 / 256e3 and 1.2e5 / 128e3
+    assert rows["L2 reads in flight per CU, mean"][:2] == ["9", "1"]
+    assert rows["L2 hit rate"][:2] == ["75.0 %", "50.0 %"]
+    assert rows["TA busy (share of CU cycles)"][:2] == ["75 %", "0 %"]
+    assert rows["L2 hit rate"][2] == "—"  # no layout kernel in these runs
