@@ -599,14 +599,14 @@ def _run_or_skip(fn, wl):
         raise
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(120))
 def test_scores_mode_bit_exact_random_shapes(i):
     wl = _random_router(i)
     say(f"[scores/random {i}] {wl}")
     _run_or_skip(lambda: _scores_case(wl, seed=3000 + i), wl)
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(30))
 def test_hidden_mode_random_shapes(i):
     wl = _random_router(i, hidden=True)
     say(f"[hidden/random {i}] {wl}")
