@@ -46,7 +46,7 @@ namespace moer {
 
 constexpr int kRowLanes = 16;
 constexpr int kCandCap = 32;                // candidates ranked in LDS per token
-constexpr int kCandStride = kCandCap + 1;   // words per row; the pad staggers banks
+constexpr int kCandStride = kCandCap + 1;   // entries per row; the pad staggers banks
 
 // ---- DPP helpers (row = 16 lanes) -------------------------------------------
 template <int CTRL>
@@ -150,14 +150,20 @@ __device__ __forceinline__ float score_of(float v, float m, float inv_z) {
   return exp2_hw((v - m) * kLog2e) * inv_z;
 }
 
-// LDS scratch of one token row. A candidate is one 64-bit word written as two
-// 32-bit halves: low = 0xFFFF - expert id, high = the key's order bits, so
-// that one unsigned 64-bit compare orders (key desc, id asc).
+// LDS scratch of one token row. A candidate is one 16-byte entry written by
+// one store: its first 8 bytes are a 64-bit word whose low half is
+// 0xFFFF - expert id and high half the key's order bits, so that one
+// unsigned 64-bit compare orders (key desc, id asc); then the score.
+struct alignas(16) Cand {
+  unsigned id_inv, key, score, pad;
+};
+__device__ __forceinline__ unsigned long long cand_word(const Cand& c) {
+  return *reinterpret_cast<const unsigned long long*>(&c);
+}
 struct RowLds {
-  unsigned long long* cand;  // [kCandStride]
-  float* cand_s;             // [kCandStride] score of each candidate
-  int* slot_id;              // [kMaxSlots]
-  float* slot_s;             // [kMaxSlots]
+  Cand* cand;    // [kCandStride]
+  int* slot_id;  // [kMaxSlots]
+  float* slot_s; // [kMaxSlots]
 };
 // Order bits of a key: for keys all > 0 the raw bits already order them;
 // otherwise flip negatives (and set the sign of non-negatives).
@@ -401,35 +407,32 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   if (count <= kCandCap) {
     // 4. compact, then slot = number of candidates that beat this one
     const bool all_positive = lo > 0.f;  // every candidate key >= lo
-    unsigned* cw = reinterpret_cast<unsigned*>(rs.cand);
     int pos = incl - mine;
     if (all_positive) {
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
         if (bits & (1u << j)) {
-          cw[2 * pos] = (unsigned)(0xFFFF - (e0 + j));
-          cw[2 * pos + 1] = __builtin_bit_cast(unsigned, key[j]);
-          rs.cand_s[pos] = s[j];
+          rs.cand[pos] = Cand{(unsigned)(0xFFFF - (e0 + j)), __builtin_bit_cast(unsigned, key[j]),
+                              __builtin_bit_cast(unsigned, s[j]), 0u};
           ++pos;
         }
     } else {
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
         if (bits & (1u << j)) {
-          cw[2 * pos] = (unsigned)(0xFFFF - (e0 + j));
-          cw[2 * pos + 1] = order_bits(key[j], false);
-          rs.cand_s[pos] = s[j];
+          rs.cand[pos] = Cand{(unsigned)(0xFFFF - (e0 + j)), order_bits(key[j], false),
+                              __builtin_bit_cast(unsigned, s[j]), 0u};
           ++pos;
         }
     }
     for (int c = rl; c < count; c += kRowLanes) {
-      const unsigned long long my = rs.cand[c];
+      const unsigned long long my = cand_word(rs.cand[c]);
       int r = 0;
 #pragma unroll 4
-      for (int i = 0; i < count; ++i) r += rs.cand[i] > my ? 1 : 0;
+      for (int i = 0; i < count; ++i) r += cand_word(rs.cand[i]) > my ? 1 : 0;
       if (r < K) {
         rs.slot_id[r] = 0xFFFF - (int)(my & 0xFFFF);
-        rs.slot_s[r] = rs.cand_s[c];
+        rs.slot_s[r] = __builtin_bit_cast(float, rs.cand[c].score);
       }
     }
   } else {

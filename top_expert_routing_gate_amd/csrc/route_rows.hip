@@ -49,8 +49,7 @@ __device__ __forceinline__ void load_row(const ScoreArgs& a, size_t row_off, siz
 
 template <int EPL, bool GROUPED, int MODE, int LPG>
 __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
-  __shared__ unsigned long long cand[kRowTokens][kCandStride];
-  __shared__ float cand_s[kRowTokens][kCandStride];
+  __shared__ Cand cand[kRowTokens][kCandStride];
   __shared__ int slot_id[kRowTokens][kMaxSlots];
   __shared__ float slot_s[kRowTokens][kMaxSlots];
   __shared__ int hist[kMaxBuckets];
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   __syncthreads();  // histogram cleared; first-half rows loaded
   if (live && !first_half) load_row<EPL>(a, row_off, split_stride, rl * EPL, v);
 
-  const RowLds rs{cand[row], cand_s[row], slot_id[row], slot_s[row]};
+  const RowLds rs{cand[row], slot_id[row], slot_s[row]};
   float q[EPL];
   route_row<EPL, GROUPED, MODE, LPG>(a, layer, t, live, v, lc, rs, hist, q);
   if (a.colpart != nullptr) {
