@@ -139,3 +139,12 @@ def test_counter_summary(tmp_path):
     assert rows["L2 hit rate"][:2] == ["75.0 %", "50.0 %"]
     assert rows["TA busy (share of CU cycles)"][:2] == ["75 %", "0 %"]
     assert rows["L2 hit rate"][2] == "—"  # no layout kernel in these runs
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
