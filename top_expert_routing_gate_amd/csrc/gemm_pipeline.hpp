@@ -46,6 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define MOER_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int kKStage = 64;           // reduction depth per LDS stage (bf16)
+constexpr int kNonTemporal = 2;       // cache-policy operand of a load: the nt bit
 constexpr int kChunks = kKStage / 8;  // 16-byte chunks per staged row
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt <= n and lgkmcnt == 0: this
@@ -88,10 +89,14 @@ struct GemmPipeline {
   static constexpr int kRows = BT + BE;
   static constexpr int kStageSlots = kRows * kChunks;
   static constexpr int kLoads = kStageSlots / (NP * kWave);  // per producer per stage
+  // instruction i of a producer covers rows ((i*NP + pw)*64 + lane)/8: the
+  // first kXLoads of them are x rows, the rest W_g rows
+  static constexpr int kXLoads = BT * kChunks / (NP * kWave);
   static constexpr int MT = BT / WT / 16;
   static constexpr int ME = BE / WE / 16;
   static constexpr size_t kRingBytes = (size_t)NSTAGE * kStageSlots * sizeof(u32x4);
   static_assert(kStageSlots % (NP * kWave) == 0, "stage must split evenly over the producers");
+  static_assert((BT * kChunks) % (NP * kWave) == 0, "x rows must fill whole instructions");
   static_assert((NSTAGE - 2) * kLoads <= 63, "outstanding loads must fit the vmcnt field");
   static_assert(BT % (WT * 16) == 0 && BE % (WE * 16) == 0, "tile shape");
 
@@ -111,9 +116,17 @@ struct GemmPipeline {
                                    : W + (size_t)min(e0 + r - BT, N - 1) * d;
       src[i] = row + kbeg + q * 8;
     }
+    // x rows are read once: their loads carry the non-temporal hint, which
+    // streams them through the L2 with less disturbance of the W_g rows
+    // every workgroup of the die re-reads
     auto issue = [&](int stage_k, int buf) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i)
+      for (int i = 0; i < kXLoads; ++i)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + stage_k * kKStage),
+                                         MOER_LDS_PTR(&ring[buf][(i * NP + pw) * kWave]), 16, 0,
+                                         kNonTemporal);
+#pragma unroll
+      for (int i = kXLoads; i < kLoads; ++i)
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + stage_k * kKStage),
                                          MOER_LDS_PTR(&ring[buf][(i * NP + pw) * kWave]), 16, 0,
                                          0);
