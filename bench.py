@@ -343,7 +343,7 @@ def summarize_counters(dirs, out, command):
                 v = [x for n, cc, x in rows if key in n and cc == c]
                 avg[(key, c)] = sum(v) / len(v)
     counters = sorted({c for _, c in avg})
-    lines = ["# Memory-path counters per launch: gate GEMM, selection, scan + scatter", "",
+    lines = ["# Hardware counters per launch: gate GEMM, selection, scan + scatter", "",
              "Commands (from /tmp, TMPDIR=/tmp; R = repository root), one counter group per run:",
              "", "```", command, "```", "",
              "| counter | " + " | ".join(lab for _, lab in COUNTER_KERNELS) + " |",
@@ -364,6 +364,15 @@ def summarize_counters(dirs, out, command):
             res.append(("L2 read latency, mean (cycles)", f"{lat / req:.0f}"))
             if cyc:
                 res.append(("L2 reads in flight per CU, mean", f"{lat / (N_CU * cyc):.0f}"))
+        mops, busy = g("SQ_INSTS_VALU_MFMA_MOPS_BF16"), g("SQ_VALU_MFMA_BUSY_CYCLES")
+        if mops and cyc:
+            # one MOPS unit is 512 flop; time at the 2.4 GHz peak clock
+            res.append(("bf16 matrix flop per launch", f"{mops * 512:.4g}"))
+            res.append(("bf16 matrix rate at 2.4 GHz (TFLOP/s)",
+                        f"{mops * 512 / (cyc / 2.4e9) / 1e12:.0f}"))
+        if busy is not None and cyc:
+            res.append(("matrix cores busy (share of SIMD cycles)",
+                        f"{100 * busy / (N_CU * 4 * cyc):.0f} %"))
         hit, miss = g("TCC_HIT_sum"), g("TCC_MISS_sum")
         if hit is not None and miss:
             res.append(("L2 hit rate", f"{100 * hit / (hit + miss):.1f} %"))

@@ -118,7 +118,9 @@ def test_counter_summary(tmp_path):
             "TCP_TCC_READ_REQ_sum": {GEMM: 4000.0, SEL: 100.0},
             "TCP_TCC_READ_REQ_LATENCY_sum": {GEMM: 4000.0 * 600, SEL: 100.0 * 1200},
             "TCC_HIT_sum": {GEMM: 3.0, SEL: 1.0}, "TCC_MISS_sum": {GEMM: 1.0, SEL: 1.0},
-            "TA_TA_BUSY_sum": {GEMM: 256 * 750.0, SEL: 0.0}}
+            "TA_TA_BUSY_sum": {GEMM: 256 * 750.0, SEL: 0.0},
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16": {GEMM: 1.0e6, SEL: 0.0},
+            "SQ_VALU_MFMA_BUSY_CYCLES": {GEMM: 256 * 4 * 1000 * 0.4, SEL: 0.0}}
     dirs = []
     for i, (c, v) in enumerate(vals.items()):
         d = str(tmp_path / f"c{i}")
@@ -139,6 +141,10 @@ def test_counter_summary(tmp_path):
     assert rows["L2 hit rate"][:2] == ["75.0 %", "50.0 %"]
     assert rows["TA busy (share of CU cycles)"][:2] == ["75 %", "0 %"]
     assert rows["L2 hit rate"][2] == "—"  # no layout kernel in these runs
+    # 1e6 x 512 flop in 1000 cycles at 2.4 GHz
+    assert rows["bf16 matrix flop per launch"][0] == "5.12e+08"
+    assert rows["bf16 matrix rate at 2.4 GHz (TFLOP/s)"][0] == "1229"
+    assert rows["matrix cores busy (share of SIMD cycles)"][:2] == ["40 %", "0 %"]
 
 
 def test_bench_refuses_more_than_one_gpu():
