@@ -24,6 +24,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -34,7 +35,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # the gate GEMM kernel's sources: a change to any of them voids the counters
 GEMM_SRCS = [os.path.join(ROOT, "top_expert_routing_gate_amd", "csrc", f)
              for f in ("gate_gemm.hip", "gemm_pipeline.hpp", "moer_internal.hpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_gemm_dsv3_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "route_dsv3_traffic.json")
 METRIC = "routed tokens/s, 16k tok × 256 experts top-8; % of MFMA/HBM roofline"
 
 
@@ -51,6 +52,9 @@ def parse():
     p.add_argument("--no-dispatch-combine", action="store_true",
                    help="skip timing the local dispatch and weighted combine that follow the "
                         "route (reported beside the route, not part of its step)")
+    p.add_argument("--route-only", action="store_true",
+                   help="time the route step only (no dispatch/combine, forcible-layout, "
+                        "capacity or balance-step timings): for counter profiles of the step")
     p.add_argument("--no-forcible", action="store_true",
                    help="skip timing the layout on forcibly balanced ids against the routed ids")
     p.add_argument("--report", metavar="OUT_MD",
@@ -403,8 +407,17 @@ def summarize_counters(dirs, out, command):
         f.write("\n".join(lines) + "\n")
 
 
+# kernels of one route call of the 16k-token batch
+STEP_KERNELS = ("gate_gemm", "route_rows", "layout_scatter", "zero_ints", "route_fused")
+
+
 def summarize_traffic(fetch_dir, write_dir, out, command):
-    res = {"gate_gemm_sha256_16": gemm_source_hash(), "command": command}
+    """HBM bytes per launch of the gate GEMM, and per route call (every
+    kernel of the call: the sum of each kernel's launches divided by the
+    calls), from FETCH_SIZE / WRITE_SIZE runs of `bench.py --route-only
+    --copy-probe`, each counter scaled by what it reads for a 1 GiB copy."""
+    res = {"gate_gemm_sha256_16": gemm_source_hash(), "sources_sha256_16": all_source_hash(),
+           "command": command}
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(d, counter)
         gemm = [v for n, v in rows if "gate_gemm" in n]
@@ -413,8 +426,13 @@ def summarize_traffic(fetch_dir, write_dir, out, command):
         res[f"{key}_kib_copy_1gib"] = max(copy)
         # counter units: KiB; scale by what the counter reads for a known 1 GiB copy
         res[f"{key}_scale"] = COPY_BYTES / (max(copy) * 1024.0)
+        calls = len(gemm) or len([v for n, v in rows if "route_fused" in n])
+        res[f"{key}_kib_per_step"] = sum(v for n, v in rows
+                                         if any(k in n for k in STEP_KERNELS)) / calls
     res["bytes_per_launch"] = (res["fetch_kib_per_launch"] * 1024.0 * res["fetch_scale"] +
                                res["write_kib_per_launch"] * 1024.0 * res["write_scale"])
+    res["bytes_per_step"] = (res["fetch_kib_per_step"] * 1024.0 * res["fetch_scale"] +
+                             res["write_kib_per_step"] * 1024.0 * res["write_scale"])
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
@@ -471,47 +489,80 @@ def gemm_source_hash():
     return h.hexdigest()[:16]
 
 
+def all_source_hash():
+    """Hash of every kernel and host source of the library."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "top_expert_routing_gate_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic():
-    """HBM bytes per gate-GEMM launch from the committed counter summary, if
-    it was taken on the current kernel source (else None)."""
+    """HBM bytes per gate-GEMM launch and per route call from the committed
+    counter summary, each only if it was taken on the current sources (the
+    GEMM's own, or all of them for the whole call); else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("gate_gemm_sha256_16") != gemm_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+        return None, None
+    gemm = t.get("bytes_per_launch") if t.get("gate_gemm_sha256_16") == gemm_source_hash() else None
+    step = t.get("bytes_per_step") if t.get("sources_sha256_16") == all_source_hash() else None
+    return gemm, step
 
 
-CPU_BASELINE_MIN_S = 10.0  # the oracle repeats whole batches for at least this long
+CPU_BASELINE_RUNS = 3  # whole-batch runs at all cores; the median is reported
+
+
+def _oracle_stages(oracle, wl, x, W, b0):
+    """One whole batch through the oracle, stage by stage (the order of the
+    path): affinities; scores, selection, weights and entropies; layout; load
+    statistics and bias update. Returns seconds per stage."""
+    t = {}
+    t0 = time.perf_counter()
+    h = oracle.affinities(x, W, None)
+    t1 = time.perf_counter()
+    s64 = oracle.scores(h, wl.score_fn)
+    s32 = s64.astype("float32")
+    idx, _, _, _ = oracle.select(s32, s64, b0, wl.K, wl.n_groups, wl.topk_groups, wl.n_shared)
+    oracle.agg_entropy(s64)
+    t2 = time.perf_counter()
+    counts = oracle.layout(idx, wl.Nb)[0]
+    t3 = time.perf_counter()
+    oracle.load_stats(counts[:wl.N])
+    oracle.bias_update(b0, counts[:wl.N], 1e-3)
+    t4 = time.perf_counter()
+    t["gemm"], t["score_select"], t["layout"], t["stats_bias"] = t1 - t0, t2 - t1, t3 - t2, t4 - t3
+    t["total"] = t4 - t0
+    return t
 
 
 def cpu_baseline(wl, inp):
-    """The oracle, as it stands, on whole batches of the workload, repeated
-    until CPU_BASELINE_MIN_S have passed (each run from the same bias)."""
+    """The oracle, as it stands, on the whole batch: the median of
+    CPU_BASELINE_RUNS runs at all host cores, with the time of each stage,
+    and one run at one core."""
     import oracle
 
     x = inp["x"][0].float().numpy()
     W = inp["W"][0].float().numpy()
     b0 = inp["bias"][0].numpy()
-    runs, dt = 0, 0.0
-    while runs == 0 or dt < CPU_BASELINE_MIN_S:
-        b = b0.copy()
-        t0 = time.perf_counter()
-        out = oracle.route(x=x, W=W, bias=b, K=wl.K, score_fn=wl.score_fn,
-                           n_groups=wl.n_groups, topk_groups=wl.topk_groups,
-                           n_shared=wl.n_shared)
-        oracle.load_stats(out["counts"][:wl.N])
-        oracle.bias_update(b, out["counts"][:wl.N], 1e-3)
-        dt += time.perf_counter() - t0
-        runs += 1
-    return {"value": runs * wl.T / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{runs} run{'s' if runs != 1 else ''} of one full batch "
-                      f"({wl.T} tokens, d={wl.d}, N={wl.N}): "
-                      f"fp64 affinities, scores, selection, entropy, layout, load stats, "
-                      f"bias update; {dt:.1f} s in all"}
+    cores = oracle.num_threads()
+    runs = [_oracle_stages(oracle, wl, x, W, b0) for _ in range(CPU_BASELINE_RUNS)]
+    med = {k: statistics.median(r[k] for r in runs) for k in runs[0]}
+    oracle.set_num_threads(1)
+    try:
+        one = _oracle_stages(oracle, wl, x, W, b0)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": wl.T / med["total"], "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole batch ({wl.T} tokens, d={wl.d}, N={wl.N}), median of "
+                      f"{CPU_BASELINE_RUNS} runs at {cores} threads: fp64 affinities, scores, "
+                      "selection, entropies, layout, load statistics, bias update",
+            "stages_ms": {k: v * 1e3 for k, v in med.items()},
+            "one_core": {"value": wl.T / one["total"], "cores": 1, "runs": 1,
+                         "stages_ms": {k: v * 1e3 for k, v in one.items()}}}
 
 
 def time_dispatch_combine(moer, torch, wl, x, outs, stream, steps):
@@ -1045,32 +1096,26 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = e0.elapsed_time(e1) / args.steps
-    # timed region 2 (roofline): the same K steps with hipEvents around every
-    # gate GEMM launch on the route's stream (events cost a few us per step,
-    # so they stay out of region 1)
+    # timed region 2 (dominant kernel): the same K steps, the gate GEMM's
+    # launch recording an event pair at the kernel's own start and end
+    # (hipExtLaunchKernel: the dispatch's timestamps, as a kernel trace reads
+    # them); the events stay out of region 1
     for i in range(args.steps):
         step(args.warmup + args.steps + i, ev.pairs[i])
     sync_streams()
     torch.cuda.synchronize()
-    event_ms = sum(ev.elapsed_ms(i) for i in range(args.steps)) / args.steps
-    # An event pair reads a few us even with nothing between its events (the
-    # markers' own processing): measure that on the same stream, the same
-    # number of times, and take it off the GEMM's bracketed time. The kernel
-    # trace of the same command shows the remainder is the kernel's duration.
-    for i in range(args.steps):
-        ev.record(ev.pairs[i][0], streams[0])
-        ev.record(ev.pairs[i][1], streams[0])
-    torch.cuda.synchronize()
-    pair_ms = sum(ev.elapsed_ms(i) for i in range(args.steps)) / args.steps
-    gemm_ms = event_ms - pair_ms
+    gemm_us = [ev.elapsed_ms(i) * 1e3 for i in range(args.steps)]
+    gemm_ms = statistics.mean(gemm_us) * 1e-3
     ev.close()
     st = moer.decode_load_stats(stats.cpu())[0]
     print(f"[bench] {ms_step * 1e3:.1f} us/step (wall {t_wall / args.steps * 1e6:.1f} us), "
-          f"gate GEMM {gemm_ms * 1e3:.1f} us ({event_ms * 1e3:.1f} us between its events, "
-          f"{pair_ms * 1e3:.1f} us for an empty pair); last imbalance "
-          f"{st['imbalance']:.3f}", file=sys.stderr, flush=True)
+          f"gate GEMM {gemm_ms * 1e3:.1f} us (mean; median {statistics.median(gemm_us):.1f}, "
+          f"min {min(gemm_us):.1f}); last imbalance {st['imbalance']:.3f}", file=sys.stderr,
+          flush=True)
 
     dc = None
+    if args.route_only:
+        args.no_dispatch_combine = args.no_forcible = True
     if not args.no_dispatch_combine:
         dc = time_dispatch_combine(moer, torch, wl, xs[0], outs, streams[0], args.steps)
         print(f"[bench] dispatch {dc['dispatch']['us']:.1f} us, combine "
@@ -1082,19 +1127,23 @@ def main():
         print(f"[bench] layout (INDICES mode): routed ids {fl['routed_ids']['us']:.1f} us, "
               f"balanced ids {fl['balanced_ids']['us']:.1f} us", file=sys.stderr, flush=True)
 
-    cp = time_capacity(moer, torch, wl, xs[0], Wd, bias, streams[0], args.steps)
-    print(f"[bench] capacity {cp['capacity']}: {cp['dsv3_group']['us']:.1f} us "
-          f"({cp['dsv3_group']['rerouted']} rerouted), with celebrity offsets "
-          f"{cp['collapse_offsets']['us']:.1f} us ({cp['collapse_offsets']['rerouted']} rerouted, "
-          f"{cp['collapse_offsets']['dropped']} dropped)", file=sys.stderr, flush=True)
-    bs = time_balance_step(moer, torch, wl, outs, streams[0], args.steps)
-    print(f"[bench] balance step: sign {bs['sign']['us']:.1f} us, proportional+EMA "
-          f"{bs['proportional_ema_every4']['us']:.1f} us", file=sys.stderr, flush=True)
+    cp = bs = None
+    if not args.route_only:
+        cp = time_capacity(moer, torch, wl, xs[0], Wd, bias, streams[0], args.steps)
+        print(f"[bench] capacity {cp['capacity']}: {cp['dsv3_group']['us']:.1f} us "
+              f"({cp['dsv3_group']['rerouted']} rerouted), with celebrity offsets "
+              f"{cp['collapse_offsets']['us']:.1f} us ({cp['collapse_offsets']['rerouted']} rerouted, "
+              f"{cp['collapse_offsets']['dropped']} dropped)", file=sys.stderr, flush=True)
+        bs = time_balance_step(moer, torch, wl, outs, streams[0], args.steps)
+        print(f"[bench] balance step: sign {bs['sign']['us']:.1f} us, proportional+EMA "
+              f"{bs['proportional_ema_every4']['us']:.1f} us", file=sys.stderr, flush=True)
 
     esize = 2 if wl.dtype == workloads.BF16 else 4
-    alg_bytes = L * (T + N) * wl.d * esize  # x + W_g of every layer per launch
-    achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    gemm_bytes = L * (T + N) * wl.d * esize  # x + W_g of every layer per launch
+    gemm_achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    step_bytes = algorithmic_bytes(wl)
+    step_achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    gemm_traffic, step_traffic = measured_traffic()
     line = {
         "metric": METRIC,
         "value": T * L / (ms_step * 1e-3),
@@ -1114,21 +1163,31 @@ def main():
                    "score": "sigmoid" if wl.score_fn == 1 else "softmax",
                    "step": "route+load_stats+bias_update (fused)", "x_batches_rotated": len(xs),
                    "streams": nstream},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gate_gemm", "kernel_us": gemm_ms * 1e3,
-                     "event_pair_us": event_ms * 1e3, "empty_pair_us": pair_ms * 1e3,
-                     "alg_bytes": alg_bytes},
+        # the whole step (every kernel of the route call) against the HBM
+        # roofline of its algorithmic bytes; the dominant kernel beside it
+        "roofline": {"bound": "hbm", "achieved": step_achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": step_achieved / HBM_PEAK_GBS,
+                     "traffic": step_traffic, "scope": "step", "alg_bytes": step_bytes,
+                     "kernel": {"name": "gate_gemm", "bound": "hbm", "achieved": gemm_achieved,
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": gemm_achieved / HBM_PEAK_GBS, "traffic": gemm_traffic,
+                                "kernel_us": gemm_ms * 1e3,
+                                "kernel_us_median": statistics.median(gemm_us),
+                                "alg_bytes": gemm_bytes,
+                                "timing": "hipExtLaunchKernel events at the kernel's start and "
+                                          "end, mean over the K steps"}},
     }
     if dc is not None:
         line["dispatch_combine"] = dc
     if fl is not None:
         line["forcible_layout"] = fl
-    line["balance_step"] = bs
-    line["capacity_route"] = cp
+    if bs is not None:
+        line["balance_step"] = bs
+    if cp is not None:
+        line["capacity_route"] = cp
     if not args.no_cpu_baseline:
-        print(f"[bench] timing the CPU oracle on whole batches for {CPU_BASELINE_MIN_S:.0f} s",
-              file=sys.stderr, flush=True)
+        print(f"[bench] timing the CPU oracle: {CPU_BASELINE_RUNS} whole batches at all cores, "
+              "one at one core", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, {"x": xs_cpu[0], "W": W, "bias": b0})
     print(json.dumps(line), flush=True)
 

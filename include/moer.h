@@ -145,14 +145,19 @@ typedef struct {
 /* Buffers of one call (device pointers; Kt = K + n_shared, Nb = N + n_shared).
  * "req" = required in the modes that produce it; "opt" = may be NULL. */
 typedef struct {
-  const void* x;             /* HIDDEN: [L][T][d] bf16 or fp32 hidden states */
+  const void* x;             /* HIDDEN: [L][T][d] bf16 or fp32 hidden states;
+                                bf16: 16-byte aligned */
   const void* w_gate;        /* HIDDEN: [L][N][d] gate weights, same dtype;
-                                row e is expert e's vector (nn.Linear layout) */
-  const float* scores;       /* SCORES: [L][T][N] fp32 scores s (or p) */
+                                row e is expert e's vector (nn.Linear layout);
+                                bf16: 16-byte aligned */
+  const float* scores;       /* SCORES: [L][T][N] fp32 scores s (or p),
+                                16-byte aligned */
   const int32_t* idx_in;     /* INDICES: [L][T][Kt] expert ids; ids outside
                                 [0, Nb) are not placed (see perm) */
-  const float* bias;         /* opt [L][N] fp32 selection bias b_e (NULL = 0) */
-  const float* logit_offset; /* opt [N] fp32 added to every layer's h (HIDDEN) */
+  const float* bias;         /* opt [L][N] fp32 selection bias b_e (NULL = 0),
+                                16-byte aligned */
+  const float* logit_offset; /* opt [N] fp32 added to every layer's h (HIDDEN),
+                                16-byte aligned */
   float* h_out;              /* opt [L][T][N] fp32 affinities h (HIDDEN) */
   float* topk_w;             /* req [L][T][Kt] combine weights (not INDICES) */
   float* tok_entropy;        /* opt [L][T] per-token routing entropy, bits */
@@ -166,8 +171,11 @@ typedef struct {
                                 offsets[Nb] hold -1 */
   int32_t* inv_perm;         /* opt [L][T*Kt] position of each slot in perm,
                                 -1 for ids that were not placed */
-  void* ev_gemm_begin;       /* opt hipEvent_t recorded just before the gate */
-  void* ev_gemm_end;         /* GEMM launch and just after it (profiling)   */
+  void* ev_gemm_begin;       /* opt hipEvent_t pair for profiling the gate  */
+  void* ev_gemm_end;         /* GEMM: the bf16 kernel's launch records them
+                                at its own start and end (the dispatch's
+                                timestamps); other gate kernels are
+                                bracketed by records on the stream */
   moer_load_stats_t* load_stats; /* opt [L]: what moer_load_stats gives for this
                                     call's counts (fused, no extra launch) */
   float* bias_update;        /* opt [L][N]: moer_bias_update applied in place
@@ -215,7 +223,9 @@ size_t moer_route_workspace_bytes(const moer_route_desc* desc);
  * slots; entropies are those of the scores; the layout, load statistics and
  * bias update use the final ids.
  * Workspace: device memory of at least moer_route_workspace_bytes(desc)
- * bytes, any contents; it is clobbered. Returns MOER_OK or an error status. */
+ * bytes, any contents; it is clobbered. Returns MOER_OK or an error status
+ * (MOER_EINVAL also for a pointer below 16-byte alignment where the field
+ * above asks for it). */
 moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io,
                        void* workspace, size_t workspace_bytes, void* stream);
 

@@ -19,7 +19,6 @@ from .api import (  # noqa: F401
     capacity_route,
     combine,
     dispatch,
-    expert_capacity,
     hotspot_accumulate,
     layout,
     load_stats,

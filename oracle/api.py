@@ -131,13 +131,6 @@ def select(s32, s64, bias, K, n_groups=1, topk_groups=1, n_shared=0):
     return idx, w, H, gap
 
 
-def expert_capacity(T, K, N, factor="1.25"):
-    """ceil(factor * T * K / N) in exact rational arithmetic."""
-    from fractions import Fraction
-    q = Fraction(factor) * T * K / N
-    return -((-q.numerator) // q.denominator)
-
-
 def capacity_route(s32, s64, bias, K, cap, n_groups=1, topk_groups=1, n_shared=0):
     """Capacity-limited routing. Returns idx [T,Kt] int32 (-1 = dropped),
     w [T,Kt] f32, and the numbers of rerouted and dropped slots."""

@@ -441,14 +441,6 @@ def test_bias_update_closed_form():
 
 
 # ------------------------------------ [P1] capacity-limited routing
-def test_expert_capacity_is_the_pages_formula():
-    # [P1] production testing: capacity = 1.25 x (batch x top_k / experts)
-    assert oracle.expert_capacity(16384, 8, 256) == 640
-    assert oracle.expert_capacity(64, 1, 4) == 20
-    assert oracle.expert_capacity(100, 3, 7) == 54     # 53.57... rounded up
-    assert oracle.expert_capacity(4096, 2, 8) == 1280
-
-
 def test_capacity_routing_hand_worked_examples():
     # Every token ranks experts 0 > 1 > 2 > 3. K = 1, cap = 2: expert 0 keeps
     # the first two tokens, the next two move to expert 1, and so on.

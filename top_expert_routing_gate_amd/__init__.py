@@ -79,7 +79,15 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
     """
     x, w_gate = _layers(x, 3), _layers(w_gate, 3)
     scores, idx_in, bias = _layers(scores, 3), _layers(idx_in, 3), _layers(bias, 2)
+    bias_update = _layers(bias_update, 2)
     if x is not None:
+        if w_gate is None:
+            raise ValueError("x needs w_gate")
+        if x.dim() != 3 or w_gate.dim() != 3:
+            raise ValueError("x must be [L,T,d] and w_gate [L,N,d]")
+        if w_gate.shape[0] != x.shape[0] or w_gate.shape[2] != x.shape[2]:
+            raise ValueError(f"w_gate {tuple(w_gate.shape)} does not match x {tuple(x.shape)} "
+                             "(need [L,N,d] for x [L,T,d])")
         mode, (L, T, d), N = MOER_IN_HIDDEN, x.shape, w_gate.shape[1]
         dev = x.device
         dtype = MOER_BF16 if x.dtype == torch.bfloat16 else MOER_F32
@@ -90,6 +98,15 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
         if N is None:
             raise ValueError("N is required with idx_in")
     Kt, Nb = K + n_shared, N + n_shared
+    for name, t in (("bias", bias), ("bias_update", bias_update)):
+        if t is not None and tuple(t.shape) != (L, N):
+            raise ValueError(f"{name} must be [L,N] = [{L},{N}], got {tuple(t.shape)}")
+    if logit_offset is not None and tuple(logit_offset.shape) != (N,):
+        raise ValueError(f"logit_offset must be [N] = [{N}], got {tuple(logit_offset.shape)}")
+    if scores is not None and scores.dim() != 3:
+        raise ValueError("scores must be [L,T,N]")
+    if idx_in is not None and tuple(idx_in.shape[2:]) != (Kt,):
+        raise ValueError(f"idx_in must be [L,T,K+n_shared] = [.,.,{Kt}], got {tuple(idx_in.shape)}")
     desc = make_desc(n_layers=L, T=T, d=d, N=N, K=K, n_groups=n_groups, topk_groups=topk_groups,
                      n_shared=n_shared, score_fn=_SCORE_FN.get(score_fn, score_fn), dtype=dtype,
                      input=mode, bias_mode=_BIAS_MODE.get(bias_mode, bias_mode),
@@ -120,7 +137,7 @@ def route(x=None, w_gate=None, *, K, score_fn="sigmoid", n_groups=1, topk_groups
                agg_entropy=out.get("agg_entropy"), topk_idx=out.get("topk_idx"),
                counts=out["counts"], offsets=out["offsets"], perm=out["perm"],
                inv_perm=out.get("inv_perm"), load_stats=out.get("load_stats"),
-               bias_update=_layers(bias_update, 2), bias_update_u=bias_update_u,
+               bias_update=bias_update, bias_update_u=bias_update_u,
                cap_stats=out.get("cap_stats"))
     return out
 
@@ -241,34 +258,38 @@ def balance_step(bias, counts, *, rule="sign", step=1e-3, alpha=1.0, every=1, st
 
 
 class BalanceMonitor:
-    """Host-side balance alarms from per-batch expert counts (hotdry,
-    deployment section: keep the spread of expert activation frequency
-    within 20 % of the mean; an expert whose load stays more than 50 % above
-    the mean calls for a replica or a different bias step).
+    """Balance alarms on the device's load statistics (hotdry, deployment
+    section: keep the spread of expert activation frequency within 20 % of
+    the mean; an expert whose load stays more than 50 % above the mean calls
+    for a replica or a different bias step).
 
-    ``observe(counts)`` takes one batch's counts [N] (host integers) and
-    returns the alarms raised: ("spread", cv) when the coefficient of
-    variation exceeds ``cv_limit``, and ("hot", expert, batches) for each
-    expert above (1 + hot_margin) x mean for ``persist`` consecutive
-    batches."""
+    ``observe(stats, counts)`` takes one layer's load-statistics record of a
+    batch (from ``load_stats`` or ``route(..., want_load_stats=True)``: the
+    raw uint8 [64] record or its ``decode_load_stats`` dict) and that batch's
+    expert counts [N], and returns the alarms raised: ("spread", cv) when the
+    record's coefficient of variation exceeds ``cv_limit``, and ("hot",
+    expert, batches) for each expert whose count exceeds (1 + hot_margin) x
+    the record's mean for ``persist`` consecutive batches. Only the
+    thresholds and the streaks are kept on the host."""
 
     def __init__(self, N, cv_limit=0.20, hot_margin=0.50, persist=3):
         self.N, self.cv_limit, self.hot_margin, self.persist = N, cv_limit, hot_margin, persist
         self.streak = [0] * N
 
-    def observe(self, counts):
-        c = [int(v) for v in list(counts)[:self.N]]
-        total = sum(c)
+    def observe(self, stats, counts):
+        if not isinstance(stats, dict):
+            stats = decode_load_stats(stats.reshape(1, 64).cpu())[0]
+        c = counts.tolist() if hasattr(counts, "tolist") else list(counts)
+        c = c[:self.N]
         alarms = []
-        if total == 0:
+        if stats["total"] == 0:
             self.streak = [0] * self.N
             return alarms
-        mean = total / self.N
-        cv = (sum((v - mean) ** 2 for v in c) / self.N) ** 0.5 / mean
-        if cv > self.cv_limit:
-            alarms.append(("spread", cv))
+        if stats["cv"] > self.cv_limit:
+            alarms.append(("spread", stats["cv"]))
+        limit = (1.0 + self.hot_margin) * stats["mean"]
         for e, v in enumerate(c):
-            self.streak[e] = self.streak[e] + 1 if v > (1.0 + self.hot_margin) * mean else 0
+            self.streak[e] = self.streak[e] + 1 if v > limit else 0
             if self.streak[e] >= self.persist:
                 alarms.append(("hot", e, self.streak[e]))
         return alarms

@@ -21,7 +21,8 @@ MOER_BIAS_SCORE, MOER_BIAS_LOGIT = 0, 1
 MOER_RULE_SIGN, MOER_RULE_PROPORTIONAL = 0, 1
 MOER_MAX_EXPERTS, MOER_MAX_SLOTS = 256, 16
 
-EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats", "moer_bias_update",
+EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats",
+            "moer_bias_update",
             "moer_balance_step", "moer_dispatch", "moer_combine", "moer_balanced_indices",
             "moer_hotspot_accumulate",
             "moer_status_str", "moer_last_error", "moer_abi_version")
@@ -163,6 +164,22 @@ def _route_io(desc, *, x=None, w_gate=None, scores=None, idx_in=None, bias=None,
         want = torch.bfloat16 if desc.dtype == MOER_BF16 else torch.float32
         if x.dtype != want or (w_gate is not None and w_gate.dtype != want):
             raise TypeError(f"x and w_gate must be {want}")
+    # element counts the kernels index (include/moer.h): a buffer of another
+    # size would be read or written out of bounds, so it is refused here
+    L, T, d, N = desc.n_layers, desc.T, desc.d, desc.N
+    Kt, Nb = desc.K + desc.n_shared, desc.N + desc.n_shared
+    for name, t, n in (("x", x, L * T * d), ("w_gate", w_gate, L * N * d),
+                       ("scores", scores, L * T * N), ("idx_in", idx_in, L * T * Kt),
+                       ("bias", bias, L * N), ("logit_offset", logit_offset, N),
+                       ("h_out", h_out, L * T * N), ("topk_w", topk_w, L * T * Kt),
+                       ("tok_entropy", tok_entropy, L * T), ("agg_entropy", agg_entropy, L),
+                       ("topk_idx", topk_idx, L * T * Kt), ("counts", counts, L * Nb),
+                       ("offsets", offsets, L * (Nb + 1)), ("perm", perm, L * T * Kt),
+                       ("inv_perm", inv_perm, L * T * Kt), ("cap_stats", cap_stats, L * 2),
+                       ("bias_update", bias_update, L * N)):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements; this router needs {n} "
+                             f"(L={L}, T={T}, d={d}, N={N}, Kt={Kt})")
     if load_stats is not None and load_stats.numel() * load_stats.element_size() < 64 * desc.n_layers:
         raise ValueError("load_stats needs 64 bytes per layer")
     return MoerRouteIO(_ptr(x), _ptr(w_gate), _ptr(scores), _ptr(idx_in), _ptr(bias),

@@ -7,6 +7,8 @@
 // ... (and the logit offset), so the result is deterministic. The pipelined
 // tile (gemm_pipeline.hpp) needs d to be a multiple of 64 per range; other d
 // take the register-staged kernel below, fp32 inputs a plain FMA kernel.
+#include <hip/hip_ext.h>
+
 #include "gemm_pipeline.hpp"
 
 namespace moer {
@@ -205,17 +207,20 @@ __global__ __launch_bounds__(256) void gate_gemm_f32_kernel(const float* __restr
   h[((size_t)layer * T + t) * N + e] = acc;
 }
 
+// ev0 / ev1 (may be null): recorded by the launch itself at the kernel's
+// start and end (the dispatch's own timestamps), for profiling.
 template <int BT, int BE, int WT, int WE, int NP, int NSTAGE>
 hipError_t launch_dma(const void* x, const void* w, float* part, int L, int T, int d, int N,
-                      int ksplit, int32_t* zero, int n_zero, hipStream_t s) {
+                      int ksplit, int32_t* zero, int n_zero, hipStream_t s, hipEvent_t ev0,
+                      hipEvent_t ev1) {
   const int n_tt = (T + BT - 1) / BT;
   const int n_te = (N + BE - 1) / BE;
   const int n_work = L * ksplit * n_te * n_tt;
   const int per_xcd = (n_work + 7) / 8;
-  hipLaunchKernelGGL((gate_gemm_dma_kernel<BT, BE, WT, WE, NP, NSTAGE>), dim3(8 * per_xcd),
-                     dim3((WT * WE + NP) * kWave), 0, s, static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(w), part, L, T, d, N, ksplit, n_tt, n_te,
-                     n_work, per_xcd, zero, n_zero);
+  hipExtLaunchKernelGGL((gate_gemm_dma_kernel<BT, BE, WT, WE, NP, NSTAGE>), dim3(8 * per_xcd),
+                        dim3((WT * WE + NP) * kWave), 0, s, ev0, ev1, 0,
+                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), part, L,
+                        T, d, N, ksplit, n_tt, n_te, n_work, per_xcd, zero, n_zero);
   return hipGetLastError();
 }
 
@@ -260,15 +265,22 @@ hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s) {
 }
 
 hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int L, int T, int d,
-                                 int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s) {
+                                 int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s,
+                                 hipEvent_t ev0, hipEvent_t ev1) {
   if (d % (kKStage * ksplit) == 0) {
     if (small_n(N))
-      return launch_dma<64, 32, 4, 1, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s);
-    return launch_dma<128, 256, 2, 2, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s);
+      return launch_dma<64, 32, 4, 1, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s, ev0,
+                                            ev1);
+    return launch_dma<128, 256, 2, 2, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s, ev0,
+                                            ev1);
   }
   if (ksplit != 1) return hipErrorInvalidValue;
-  if (N <= 16) return launch_tile<16, 64, 1, 4>(x, w, part, L, T, d, N, s);
-  return launch_tile<64, 128, 1, 4>(x, w, part, L, T, d, N, s);
+  hipError_t e = ev0 != nullptr ? hipEventRecord(ev0, s) : hipSuccess;
+  if (e == hipSuccess)
+    e = N <= 16 ? launch_tile<16, 64, 1, 4>(x, w, part, L, T, d, N, s)
+                : launch_tile<64, 128, 1, 4>(x, w, part, L, T, d, N, s);
+  if (e == hipSuccess && ev1 != nullptr) e = hipEventRecord(ev1, s);
+  return e;
 }
 
 hipError_t launch_gate_gemm_f32(const float* x, const float* w, float* h, int L, int T, int d,

@@ -20,6 +20,7 @@
 // when asked, the load statistics and the bias update from the totals.
 #include <math.h>
 
+#include "layout_block.hpp"
 #include "load_balance.hpp"
 #include "moer_internal.hpp"
 
@@ -27,10 +28,6 @@ namespace moer {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBlocksPerLayoutBlock = kLayoutTokens / kRowTokens;  // 1
-constexpr int kMaxSlotsPerBlock = kLayoutTokens * kMaxSlots;       // 1024
-constexpr int kMaxChunks = kMaxSlotsPerBlock / 64;                 // 16
-static_assert(kLayoutTokens % kRowTokens == 0, "layout block = whole histogram blocks");
 static_assert(kThreads == kBalanceThreads, "the first layout workgroup runs the balance routines");
 
 // Histogram of supplied ids, one workgroup per 64-token block.
@@ -58,33 +55,6 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutArgs a) {
     out[(size_t)e * a.nsb] = (uint16_t)hist[e];
     if (hist[e] != 0) atomicAdd(&seg[e], hist[e]);
   }
-}
-
-// Exclusive scan of v[0..n) in LDS (n <= 2 * kThreads), deterministic:
-// each thread adds its pair, waves scan with lane shuffles, then the wave
-// totals are added in wave order.
-__device__ void block_exclusive_scan(int* v, int* tmp, int n) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int i0 = 2 * tid, i1 = 2 * tid + 1;
-  const int a0 = i0 < n ? v[i0] : 0;
-  const int a1 = i1 < n ? v[i1] : 0;
-  int x = a0 + a1;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    x += lane >= o ? y : 0;
-  }
-  if (lane == kWave - 1) tmp[wave] = x;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += tmp[w];
-  const int excl = base + x - (a0 + a1);
-  // each thread rewrites only the two entries it read
-  if (i0 < n) v[i0] = excl;
-  if (i1 < n) v[i1] = excl + a0;
-  __syncthreads();
 }
 
 // Entropy (bits) of the batch mean of q: thread (quad of experts, row group)
@@ -165,57 +135,11 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
   if (threadIdx.x == 0) a.agg_entropy[layer] = a.T > 0 ? red[0] : 0.f;
 }
 
-// total[e] = the layer's assignments of expert e (0 for e >= Nb) and, with
-// lb >= 0, pre[e] = those in tokens before layout block lb: the segments
-// wholly before it plus the blocks of its own segment before it.
-__device__ void load_totals(const LayoutArgs& a, int layer, int lb, int* total, int* pre) {
-  constexpr int kMaxSeg = 32;  // segments summed from registers; more take a loop
-  const int b_first = lb * kBlocksPerLayoutBlock;
-  const int s_own = lb >= 0 ? b_first / kSegBlocks : 0;
-  const int32_t* seg = a.segsum + (size_t)layer * a.nseg * a.Nb;
-  for (int e = threadIdx.x; e < 2 * kThreads; e += kThreads) {
-    int tot = 0, p = 0;
-    if (e < a.Nb) {
-      for (int s0 = 0; s0 < a.nseg; s0 += kMaxSeg) {
-        int v[kMaxSeg];
-#pragma unroll
-        for (int k = 0; k < kMaxSeg; ++k)
-          v[k] = s0 + k < a.nseg ? seg[(size_t)(s0 + k) * a.Nb + e] : 0;
-#pragma unroll
-        for (int k = 0; k < kMaxSeg; ++k) {
-          tot += v[k];
-          p += s0 + k < s_own ? v[k] : 0;
-        }
-      }
-      if (lb >= 0) {
-        const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
-        const int b0 = s_own * kSegBlocks;
-        if ((a.nsb & 7) == 0 && b0 + kSegBlocks <= a.nsb) {
-          // the segment's block counts as two 16-byte loads, masked
-          static_assert(kSegBlocks == 16, "two uint4 per segment");
-          const uint4* r4 = reinterpret_cast<const uint4*>(row + b0);
-          const uint4 q0 = r4[0], q1 = r4[1];
-          const unsigned w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int b = b0 + 2 * k;
-            p += (b < b_first ? (int)(w[k] & 0xFFFF) : 0) + (b + 1 < b_first ? (int)(w[k] >> 16) : 0);
-          }
-        } else {
-          for (int b = b0; b < b_first; ++b) p += row[b];
-        }
-        pre[e] = p;
-      }
-    }
-    total[e] = tot;
-  }
-}
-
 // Load statistics and the sign-step bias update of this call's routed counts
 // (one workgroup per layer, beside the scatter workgroups).
 __device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* total, int* pre) {
   __shared__ BalanceScratch bal;
-  load_totals(a, layer, -1, total, pre);
+  load_totals<kThreads>(a, layer, -1, total, pre);
   __syncthreads();
   if (a.cap_phase == 1) {
     // is any routed expert over capacity? then the statistics wait for the
@@ -235,12 +159,7 @@ __device__ void balance_from_histograms(const LayoutArgs& a, int layer, int* tot
 // Workgroups [0, nlb) place 64 tokens each; then, if requested, one
 // workgroup for the batch-mean entropy and one for load balancing.
 __global__ __launch_bounds__(kThreads, 1) void layout_scatter_kernel(LayoutArgs a) {
-  __shared__ int total[2 * kThreads];
-  __shared__ int pre[kMaxBuckets];
-  __shared__ int scan_tmp[kThreads];
-  __shared__ unsigned long long bits[kMaxChunks][kMaxBuckets];
-  __shared__ unsigned short chunk_pre[kMaxChunks][kMaxBuckets];
-
+  __shared__ ScatterLds sl;
   const int layer = blockIdx.y;
   const int blk = blockIdx.x;
   if (a.cap_phase == 2 && a.cap_flag[layer] == 0) return;  // the first layout stands
@@ -248,72 +167,10 @@ __global__ __launch_bounds__(kThreads, 1) void layout_scatter_kernel(LayoutArgs 
     if (blk == a.nlb && a.agg_entropy != nullptr)
       batch_mean_entropy(a, layer);
     else
-      balance_from_histograms(a, layer, total, pre);
+      balance_from_histograms(a, layer, sl.total, sl.pre);
     return;
   }
-  const int Nb = a.Nb;
-  const int t0 = blk * kLayoutTokens;
-  const int nt = max(0, min(kLayoutTokens, a.T - t0));
-  const int nslot = nt * a.Kt;
-  const int nchunk = (nslot + 63) / 64;
-  const size_t lbase = (size_t)layer * a.T * a.Kt;
-  const int flat0 = t0 * a.Kt;
-
-  // the block's ids first: their loads overlap the totals' loads
-  constexpr int kIdsPerThread = kMaxSlotsPerBlock / kThreads;
-  int ids[kIdsPerThread];
-#pragma unroll
-  for (int k = 0; k < kIdsPerThread; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    ids[k] = i < nslot ? a.idx[lbase + flat0 + i] : -1;
-  }
-  // per expert: all assignments, and those in tokens before this block
-  load_totals(a, layer, blk, total, pre);
-  for (int c = 0; c < nchunk; ++c)
-    for (int e = threadIdx.x; e < Nb; e += kThreads) bits[c][e] = 0ull;
-  __syncthreads();
-  const int last_count = total[Nb - 1];
-  if (blk == 0)
-    for (int e = threadIdx.x; e < Nb; e += kThreads) a.counts[(size_t)layer * Nb + e] = total[e];
-  block_exclusive_scan(total, scan_tmp, Nb);  // total[e] := offset of expert e
-  if (blk == 0) {
-    int32_t* off = a.offsets + (size_t)layer * (Nb + 1);
-    for (int e = threadIdx.x; e < Nb; e += kThreads) off[e] = total[e];
-    if (threadIdx.x == 0) off[Nb] = total[Nb - 1] + last_count;
-  }
-
-  // membership bitmaps: bit i of bits[c][e] <=> slot c*64+i of this block is e
-#pragma unroll
-  for (int k = 0; k < kIdsPerThread; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    const int e = ids[k];
-    if (i < nslot && e >= 0 && e < Nb) atomicOr(&bits[i >> 6][e], 1ull << (i & 63));
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < Nb; e += kThreads) {
-    int run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      chunk_pre[c][e] = (unsigned short)run;
-      run += __popcll(bits[c][e]);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kIdsPerThread; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    if (i >= nslot) break;
-    const int e = ids[k];
-    const int flat = flat0 + i;
-    if (e >= 0 && e < Nb) {
-      const int c = i >> 6;
-      const unsigned long long below = bits[c][e] & ((1ull << (i & 63)) - 1ull);
-      const int pos = total[e] + pre[e] + chunk_pre[c][e] + __popcll(below);
-      a.perm[lbase + pos] = flat;
-      if (a.inv_perm != nullptr) a.inv_perm[lbase + flat] = pos;
-    } else if (a.inv_perm != nullptr) {
-      a.inv_perm[lbase + flat] = -1;
-    }
-  }
+  scatter_block<kThreads>(a, layer, blk, sl);
 }
 
 }  // namespace

@@ -1,0 +1,180 @@
+// One layout block (64 tokens) of the dispatch layout: per-expert counts (the
+// listing's bincount in "MoE Routing Entropy vs Expert Saturation"), their
+// exclusive prefix, and the stable permutation that groups every (token,
+// slot) assignment by destination expert ("DeepSeek V4 MoE load balancing",
+// DeepEP section: dispatch needs tokens grouped by their expert). Within an
+// expert, assignments keep (token, slot) order, so the result is unique.
+//
+// Inputs: the per-64-token-block histograms cnt[l][e][b] (uint16,
+// expert-major) and the per-segment totals segsum[l][s][e] (segment = 16
+// consecutive blocks), both complete before these routines run. An expert's
+// total is the sum of its segments; its assignments before block b are the
+// earlier segments plus the earlier blocks of b's own segment. The totals
+// are scanned into offsets, and the block's assignments are placed by
+// popcount ranks in per-64-slot LDS membership bitmaps.
+//
+// Written for any workgroup size NT (a multiple of 64, 256..1024); every
+// thread of the workgroup must call these routines (they hold barriers).
+#pragma once
+
+#include "moer_internal.hpp"
+
+namespace moer {
+
+constexpr int kMaxSlotsPerBlock = kLayoutTokens * kMaxSlots;  // 1024
+constexpr int kMaxChunks = kMaxSlotsPerBlock / 64;            // 16
+static_assert(kLayoutTokens == kRowTokens, "a layout block is one histogram block");
+
+// LDS of one layout block.
+struct ScatterLds {
+  int total[kMaxBuckets];
+  int pre[kMaxBuckets];
+  int scan_tmp[16];
+  unsigned long long bits[kMaxChunks][kMaxBuckets];
+  unsigned short chunk_pre[kMaxChunks][kMaxBuckets];
+};
+
+// Exclusive scan of v[0..n) in LDS (n <= 2 * NT), deterministic: each thread
+// adds its pair, waves scan with lane shuffles, then the wave totals are
+// added in wave order.
+template <int NT>
+__device__ void block_exclusive_scan(int* v, int* tmp, int n) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int a0 = i0 < n ? v[i0] : 0;
+  const int a1 = i1 < n ? v[i1] : 0;
+  int x = a0 + a1;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    x += lane >= o ? y : 0;
+  }
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += tmp[w];
+  const int excl = base + x - (a0 + a1);
+  // each thread rewrites only the two entries it read
+  if (i0 < n) v[i0] = excl;
+  if (i1 < n) v[i1] = excl + a0;
+  __syncthreads();
+}
+
+// total[e] = the layer's assignments of expert e (e < Nb) and, with lb >= 0,
+// pre[e] = those in tokens before layout block lb: the segments wholly before
+// it plus the blocks of its own segment before it.
+template <int NT>
+__device__ void load_totals(const LayoutArgs& a, int layer, int lb, int* total, int* pre) {
+  constexpr int kMaxSeg = 32;  // segments summed from registers; more take a loop
+  const int b_first = lb;
+  const int s_own = lb >= 0 ? b_first / kSegBlocks : 0;
+  const int32_t* seg = a.segsum + (size_t)layer * a.nseg * a.Nb;
+  for (int e = threadIdx.x; e < a.Nb; e += NT) {
+    int tot = 0, p = 0;
+    for (int s0 = 0; s0 < a.nseg; s0 += kMaxSeg) {
+      int v[kMaxSeg];
+#pragma unroll
+      for (int k = 0; k < kMaxSeg; ++k)
+        v[k] = s0 + k < a.nseg ? seg[(size_t)(s0 + k) * a.Nb + e] : 0;
+#pragma unroll
+      for (int k = 0; k < kMaxSeg; ++k) {
+        tot += v[k];
+        p += s0 + k < s_own ? v[k] : 0;
+      }
+    }
+    if (lb >= 0) {
+      const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
+      const int b0 = s_own * kSegBlocks;
+      if ((a.nsb & 7) == 0 && b0 + kSegBlocks <= a.nsb) {
+        // the segment's block counts as two 16-byte loads, masked
+        static_assert(kSegBlocks == 16, "two uint4 per segment");
+        const uint4* r4 = reinterpret_cast<const uint4*>(row + b0);
+        const uint4 q0 = r4[0], q1 = r4[1];
+        const unsigned w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int b = b0 + 2 * k;
+          p += (b < b_first ? (int)(w[k] & 0xFFFF) : 0) + (b + 1 < b_first ? (int)(w[k] >> 16) : 0);
+        }
+      } else {
+        for (int b = b0; b < b_first; ++b) p += row[b];
+      }
+      pre[e] = p;
+    }
+    total[e] = tot;
+  }
+}
+
+// Place layout block blk of `layer` (blk < a.nlb): counts and offsets (block
+// 0 writes them), perm, inv_perm.
+template <int NT>
+__device__ void scatter_block(const LayoutArgs& a, int layer, int blk, ScatterLds& sl) {
+  const int Nb = a.Nb;
+  const int t0 = blk * kLayoutTokens;
+  const int nt = max(0, min(kLayoutTokens, a.T - t0));
+  const int nslot = nt * a.Kt;
+  const int nchunk = (nslot + 63) / 64;
+  const size_t lbase = (size_t)layer * a.T * a.Kt;
+  const int flat0 = t0 * a.Kt;
+
+  // the block's ids first: their loads overlap the totals' loads
+  constexpr int kIdsPerThread = kMaxSlotsPerBlock / NT;
+  static_assert(kMaxSlotsPerBlock % NT == 0, "ids split evenly over the threads");
+  int ids[kIdsPerThread];
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = threadIdx.x + k * NT;
+    ids[k] = i < nslot ? a.idx[lbase + flat0 + i] : -1;
+  }
+  // per expert: all assignments, and those in tokens before this block
+  load_totals<NT>(a, layer, blk, sl.total, sl.pre);
+  for (int c = 0; c < nchunk; ++c)
+    for (int e = threadIdx.x; e < Nb; e += NT) sl.bits[c][e] = 0ull;
+  __syncthreads();
+  const int last_count = sl.total[Nb - 1];
+  if (blk == 0)
+    for (int e = threadIdx.x; e < Nb; e += NT) a.counts[(size_t)layer * Nb + e] = sl.total[e];
+  block_exclusive_scan<NT>(sl.total, sl.scan_tmp, Nb);  // total[e] := offset of expert e
+  if (blk == 0) {
+    int32_t* off = a.offsets + (size_t)layer * (Nb + 1);
+    for (int e = threadIdx.x; e < Nb; e += NT) off[e] = sl.total[e];
+    if (threadIdx.x == 0) off[Nb] = sl.total[Nb - 1] + last_count;
+  }
+
+  // membership bitmaps: bit i of bits[c][e] <=> slot c*64+i of this block is e
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = threadIdx.x + k * NT;
+    const int e = ids[k];
+    if (i < nslot && e >= 0 && e < Nb) atomicOr(&sl.bits[i >> 6][e], 1ull << (i & 63));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < Nb; e += NT) {
+    int run = 0;
+    for (int c = 0; c < nchunk; ++c) {
+      sl.chunk_pre[c][e] = (unsigned short)run;
+      run += __popcll(sl.bits[c][e]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i >= nslot) break;
+    const int e = ids[k];
+    const int flat = flat0 + i;
+    if (e >= 0 && e < Nb) {
+      const int c = i >> 6;
+      const unsigned long long below = sl.bits[c][e] & ((1ull << (i & 63)) - 1ull);
+      const int pos = sl.total[e] + sl.pre[e] + sl.chunk_pre[c][e] + __popcll(below);
+      a.perm[lbase + pos] = flat;
+      if (a.inv_perm != nullptr) a.inv_perm[lbase + flat] = pos;
+    } else if (a.inv_perm != nullptr) {
+      a.inv_perm[lbase + flat] = -1;
+    }
+  }
+}
+
+}  // namespace moer

@@ -46,16 +46,20 @@ __device__ __forceinline__ V wave_allreduce(V v, Op op) {
 // (bias != nullptr) of the counts c[0..N) (LDS or global memory). Reductions:
 // each thread takes experts tid, tid+256, ... in order, then a butterfly per
 // wave, then the four wave results in wave order: fixed, so deterministic.
+// The first 256 threads of the workgroup do the work; a larger workgroup's
+// other threads only take part in its barriers (same results at any size).
 __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_stats_t* out,
                                           float* bias, float u, BalanceScratch& sh) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const bool worker = threadIdx.x < kBalanceThreads;
+  const int e_first = worker ? (int)threadIdx.x : N;
   // round 1: total, and the largest count with the lowest expert id on ties
   // (packed as order-preserving count bits << 32 | ~id, so one unsigned max
   // decides both)
   long long tot = 0;
   unsigned long long best = 0;
-  for (int e = threadIdx.x; e < N; e += kBalanceThreads) {
+  for (int e = e_first; e < N; e += kBalanceThreads) {
     tot += c[e];
     const unsigned ord = (unsigned)c[e] ^ 0x80000000u;
     const unsigned long long key =
@@ -64,7 +68,7 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   }
   tot = wave_allreduce(tot, [](long long x, long long y) { return x + y; });
   best = wave_allreduce(best, [](unsigned long long x, unsigned long long y) { return x > y ? x : y; });
-  if (lane == 0) {
+  if (worker && lane == 0) {
     sh.tot[wave] = tot;
     sh.best[wave] = best;
   }
@@ -78,7 +82,7 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   }
 
   if (bias != nullptr) {
-    for (int e = threadIdx.x; e < N; e += kBalanceThreads) {
+    for (int e = e_first; e < N; e += kBalanceThreads) {
       const long long diff = tot - (long long)N * c[e];
       const float step = diff > 0 ? u : (diff < 0 ? -u : 0.f);
       bias[e] = bias[e] + step;
@@ -89,7 +93,7 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   // round 2: entropy of the load distribution and the sum of squared deviations
   const double mean = (double)tot / (double)N;
   double hpart = 0.0, vpart = 0.0;
-  for (int e = threadIdx.x; e < N; e += kBalanceThreads) {
+  for (int e = e_first; e < N; e += kBalanceThreads) {
     const double v = (double)c[e];
     if (tot > 0 && c[e] > 0) {
       const double q = v / (double)tot;
@@ -99,7 +103,7 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   }
   hpart = wave_allreduce(hpart, [](double x, double y) { return x + y; });
   vpart = wave_allreduce(vpart, [](double x, double y) { return x + y; });
-  if (lane == 0) {
+  if (worker && lane == 0) {
     sh.h[wave] = hpart;
     sh.v[wave] = vpart;
   }

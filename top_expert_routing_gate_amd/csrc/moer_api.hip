@@ -3,6 +3,7 @@
 // no allocation, no global state besides the thread-local error string.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/moer.h"
 #include "moer_internal.hpp"
@@ -42,7 +43,8 @@ moer_status check_rows(int32_t n_layers, int32_t T, int32_t Kt) {
 struct Plan {
   int Kt, Nb, nsb, nlb, ksplit;
   int nseg;
-  size_t off_h, off_colpart, off_cnt, off_seg, total;
+  int nsync;  // fused pass counters, stored right after the segment totals
+  size_t off_h, off_colpart, off_cnt, off_seg, off_colmean, total;
   // capacity-limited routing
   size_t off_key, off_s, off_ranked, off_nel, off_next, off_changed, off_list0, off_list1,
       off_inv, off_flag, off_liste, off_rd;
@@ -67,8 +69,12 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   p.off_cnt = o;  // expert histograms per 64-token block (uint16)
   o += align_up(L * p.Nb * p.nsb * sizeof(uint16_t) + 16);
   p.nseg = (p.nsb + moer::kSegBlocks - 1) / moer::kSegBlocks;
-  p.off_seg = o;  // expert counts per segment of histogram blocks
-  o += align_up(L * p.nseg * p.Nb * sizeof(int32_t) + 16);
+  p.off_seg = o;  // expert counts per segment of histogram blocks, then the
+                  // fused pass's counters (one zero fill clears both)
+  p.nsync = hidden ? moer::route_fused_sync_ints(d.n_layers, d.T) : 0;
+  o += align_up((L * p.nseg * p.Nb + p.nsync) * sizeof(int32_t) + 16);
+  p.off_colmean = o;  // fused pass: batch-mean q per expert
+  if (hidden && want_agg) o += align_up(L * d.N * sizeof(float) + 16);
   if (d.capacity > 0 && d.input != MOER_IN_INDICES) {
     const size_t LT = L * (size_t)d.T;
     p.off_key = o;      // selection keys, -inf outside the kept groups
@@ -118,6 +124,19 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   }
   p.total = o;
   return p;
+}
+
+// Fused router pass, chosen by the environment variable MOER_ROUTE_FUSED:
+// 0 (the default) = never; 1 = for the batches whose separate gate GEMM also
+// splits d in two (tiles enough to fill the chip); 2 = the same with the
+// layout as a separate launch; 3 = for every shape it can take. Off by
+// default: on MI355X its in-kernel synchronisation costs more than the
+// kernel boundaries it removes (the 16k-token batch: 126 us with it, 82 us
+// without).
+int fused_mode() {
+  const char* v = getenv("MOER_ROUTE_FUSED");
+  if (v == nullptr || *v == '\0') return 0;
+  return atoi(v);
 }
 
 // Which selection kernel takes this shape: 1 = one 16-lane row per token,
@@ -217,6 +236,15 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     return fail(MOER_EINVAL, "topk_idx and topk_w are required");
   if (io->counts == nullptr || io->offsets == nullptr || (some && io->perm == nullptr))
     return fail(MOER_EINVAL, "counts, offsets and perm are required");
+  // 16-byte vector loads (the gate GEMM's DMA; four experts per load of
+  // scores, bias and logit offset)
+  if (hidden && some && d.dtype == MOER_BF16 && (!aligned16(io->x) || !aligned16(io->w_gate)))
+    return fail(MOER_EINVAL, "x and w_gate must be 16-byte aligned");
+  if (scores && some && !aligned16(io->scores))
+    return fail(MOER_EINVAL, "scores must be 16-byte aligned");
+  if ((io->bias != nullptr && !aligned16(io->bias)) ||
+      (io->logit_offset != nullptr && !aligned16(io->logit_offset)))
+    return fail(MOER_EINVAL, "bias and logit_offset must be 16-byte aligned");
   if ((io->ev_gemm_begin == nullptr) != (io->ev_gemm_end == nullptr))
     return fail(MOER_EINVAL, "ev_gemm_begin and ev_gemm_end go together");
   if (io->bias_update != nullptr &&
@@ -243,75 +271,40 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
       return fail(MOER_EHIP, "%s: %s", #expr, hipGetErrorString(he));           \
   } while (0)
 
-  // segment counters start at zero: cleared by the gate GEMM when the
-  // pipelined bf16 kernel or the fp32 kernel runs, else by a fill kernel
   int32_t* segsum = reinterpret_cast<int32_t*>(ws + p.off_seg);
   const int n_seg = L * p.nseg * p.Nb;
-  const bool gemm_clears =
-      hidden && d.T > 0 &&
-      (d.dtype == MOER_BF16 ? moer::gate_gemm_clears(L, d.T, d.d, d.N, p.ksplit) : true);
-  if (!gemm_clears) MOER_CHECK(moer::launch_zero_ints(segsum, n_seg, s));
-
-  // a1: gate affinities
-  const float* h = nullptr;
-  if (hidden && d.T > 0) {
-    float* hbuf = reinterpret_cast<float*>(ws + p.off_h);
-    if (io->ev_gemm_begin) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_begin), s));
-    if (d.dtype == MOER_BF16)
-      MOER_CHECK(moer::launch_gate_gemm_bf16(io->x, io->w_gate, hbuf, L, d.T, d.d, d.N, p.ksplit,
-                                             gemm_clears ? segsum : nullptr,
-                                             gemm_clears ? n_seg : 0, s));
-    else
-      MOER_CHECK(moer::launch_gate_gemm_f32(static_cast<const float*>(io->x),
-                                            static_cast<const float*>(io->w_gate), hbuf, L, d.T,
-                                            d.d, d.N,
-                                            gemm_clears ? segsum : nullptr,
-                                            gemm_clears ? n_seg : 0, s));
-    if (io->ev_gemm_end) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_end), s));
-    h = hbuf;
-  }
-  if (io->ev_select_wait != nullptr)
-    MOER_CHECK(hipStreamWaitEvent(s, static_cast<hipEvent_t>(io->ev_select_wait), 0));
-
-  // a2-a6: scores, selection, weights, entropy, per-block expert histograms
   float* colpart = want_agg ? reinterpret_cast<float*>(ws + p.off_colpart) : nullptr;
   uint16_t* cnt = reinterpret_cast<uint16_t*>(ws + p.off_cnt);
   const int path = indices ? 0 : selection_path(d);
-  if (!indices && d.T > 0) {
-    moer::ScoreArgs a{};
-    a.in = hidden ? h : io->scores;
-    a.offset = hidden ? io->logit_offset : nullptr;
-    a.h_out = hidden ? io->h_out : nullptr;
-    a.nsplit = p.ksplit;
-    a.bias = io->bias;
-    a.idx = io->topk_idx;
-    a.w = io->topk_w;
-    a.tok_entropy = io->tok_entropy;
-    a.colpart = colpart;
-    a.T = d.T;
-    a.N = d.N;
-    a.K = d.K;
-    a.G = d.n_groups;
-    a.Gk = d.topk_groups;
-    a.n_shared = d.n_shared;
-    a.score_fn = d.score_fn;
-    a.apply_score = hidden ? 1 : 0;
-    a.bias_logit = d.bias_mode == MOER_BIAS_LOGIT ? 1 : 0;
-    if (capped) {
-      a.key_out = reinterpret_cast<float*>(ws + p.off_key);
-      a.s_out = reinterpret_cast<float*>(ws + p.off_s);
-    }
-    if (path == 1) {
-      a.cnt = cnt;
-      a.segsum = segsum;
-      MOER_CHECK(moer::launch_route_rows(a, L, s));
-    } else {
-      a.cnt = nullptr;
-      MOER_CHECK(moer::launch_score_topk(a, L, s));
-    }
-  }
 
-  // a6-a8 (+ batch-mean entropy): layout
+  // a2-a6 arguments: scores, selection, weights, entropy, block histograms
+  moer::ScoreArgs a{};
+  a.in = hidden ? reinterpret_cast<const float*>(ws + p.off_h) : io->scores;
+  a.offset = hidden ? io->logit_offset : nullptr;
+  a.h_out = hidden ? io->h_out : nullptr;
+  a.nsplit = p.ksplit;
+  a.bias = io->bias;
+  a.idx = io->topk_idx;
+  a.w = io->topk_w;
+  a.tok_entropy = io->tok_entropy;
+  a.colpart = colpart;
+  a.T = d.T;
+  a.N = d.N;
+  a.K = d.K;
+  a.G = d.n_groups;
+  a.Gk = d.topk_groups;
+  a.n_shared = d.n_shared;
+  a.score_fn = d.score_fn;
+  a.apply_score = hidden ? 1 : 0;
+  a.bias_logit = d.bias_mode == MOER_BIAS_LOGIT ? 1 : 0;
+  if (capped) {
+    a.key_out = reinterpret_cast<float*>(ws + p.off_key);
+    a.s_out = reinterpret_cast<float*>(ws + p.off_s);
+  }
+  a.cnt = path == 1 ? cnt : nullptr;
+  a.segsum = path == 1 ? segsum : nullptr;
+
+  // a6-a8 (+ batch-mean entropy, statistics, bias update) arguments: layout
   moer::LayoutArgs la{};
   la.idx = indices ? io->idx_in : io->topk_idx;
   la.cnt = cnt;
@@ -344,6 +337,60 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   }
   la.fill_invalid = indices ? 1 : 0;
   la.need_count = (path != 1 && d.T > 0) ? 1 : 0;
+
+  // The fused pass (one co-resident launch after a fill kernel) takes the
+  // large bf16 routers it was built for; every other shape, the capacity
+  // limit and a split selection stream take the separate launches below.
+  const int fused = fused_mode();
+  if (fused != 0 && hidden && d.dtype == MOER_BF16 && d.T > 0 && !capped &&
+      io->ev_select_wait == nullptr && p.ksplit >= 2 && (fused == 3 || p.ksplit == 2) &&
+      moer::route_fused_eligible(L, d.T, d.d, d.N, d.n_groups)) {
+    MOER_CHECK(moer::launch_zero_ints(segsum, n_seg + p.nsync, s));
+    if (io->ev_gemm_begin) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_begin), s));
+    MOER_CHECK(moer::launch_route_fused(io->x, io->w_gate, reinterpret_cast<float*>(ws + p.off_h),
+                                        segsum + n_seg,
+                                        reinterpret_cast<float*>(ws + p.off_colmean), a, la, L,
+                                        d.T, d.d, d.N, fused != 2, s));
+    if (io->ev_gemm_end) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_end), s));
+    if (fused == 2) MOER_CHECK(moer::launch_layout(la, L, s));
+    return ok();
+  }
+
+  // segment counters start at zero: cleared by the gate GEMM when the
+  // pipelined bf16 kernel or the fp32 kernel runs, else by a fill kernel
+  const bool gemm_clears =
+      hidden && d.T > 0 &&
+      (d.dtype == MOER_BF16 ? moer::gate_gemm_clears(L, d.T, d.d, d.N, p.ksplit) : true);
+  if (!gemm_clears) MOER_CHECK(moer::launch_zero_ints(segsum, n_seg, s));
+
+  // a1: gate affinities (depth-range partial sums in the workspace)
+  if (hidden && d.T > 0) {
+    float* hbuf = reinterpret_cast<float*>(ws + p.off_h);
+    hipEvent_t ev0 = static_cast<hipEvent_t>(io->ev_gemm_begin);
+    hipEvent_t ev1 = static_cast<hipEvent_t>(io->ev_gemm_end);
+    if (d.dtype == MOER_BF16) {
+      MOER_CHECK(moer::launch_gate_gemm_bf16(io->x, io->w_gate, hbuf, L, d.T, d.d, d.N, p.ksplit,
+                                             gemm_clears ? segsum : nullptr,
+                                             gemm_clears ? n_seg : 0, s, ev0, ev1));
+    } else {
+      if (ev0) MOER_CHECK(hipEventRecord(ev0, s));
+      MOER_CHECK(moer::launch_gate_gemm_f32(static_cast<const float*>(io->x),
+                                            static_cast<const float*>(io->w_gate), hbuf, L, d.T,
+                                            d.d, d.N,
+                                            gemm_clears ? segsum : nullptr,
+                                            gemm_clears ? n_seg : 0, s));
+      if (ev1) MOER_CHECK(hipEventRecord(ev1, s));
+    }
+  }
+  if (io->ev_select_wait != nullptr)
+    MOER_CHECK(hipStreamWaitEvent(s, static_cast<hipEvent_t>(io->ev_select_wait), 0));
+
+  if (!indices && d.T > 0) {
+    if (path == 1)
+      MOER_CHECK(moer::launch_route_rows(a, L, s));
+    else
+      MOER_CHECK(moer::launch_score_topk(a, L, s));
+  }
   MOER_CHECK(moer::launch_layout(la, L, s));
 
   if (capped && d.T > 0) {

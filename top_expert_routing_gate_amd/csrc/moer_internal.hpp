@@ -63,8 +63,11 @@ struct LayoutArgs {
 int gate_gemm_ksplit(int dtype_bf16, int L, int T, int d, int N);
 // zero[0..n_zero) is cleared by the launch before any of its tiles finish
 // (for counters the next kernels of the call accumulate into).
+// ev0 / ev1 (may be null): profiling events recorded at the GEMM kernel's
+// start and end.
 hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int L, int T, int d,
-                                 int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s);
+                                 int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s,
+                                 hipEvent_t ev0, hipEvent_t ev1);
 // Whether launch_gate_gemm_bf16 takes the pipelined kernel (which clears
 // `zero` itself) for this shape; otherwise clear it with launch_zero_ints.
 bool gate_gemm_clears(int L, int T, int d, int N, int ksplit);
@@ -77,6 +80,16 @@ int route_rows_epl(int N);
 bool route_rows_supports(int N, int G);
 hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s);
+// Fused router pass (gate GEMM in two depth halves exchanging partials
+// pairwise, selection from LDS, then the layout after a grid barrier): can it
+// take this bf16 router (128 < N <= 256, N % 16 == 0, d % 128 == 0, its
+// whole grid resident at once)? Its exchange buffer is [2][L][T][N] fp32.
+bool route_fused_eligible(int L, int T, int d, int N, int G);
+// Counters the fused pass needs zeroed before its launch.
+int route_fused_sync_ints(int L, int T);
+hipError_t launch_route_fused(const void* x, const void* w, float* part, int32_t* sync,
+                              float* colmean, const ScoreArgs& sa, const LayoutArgs& la, int L,
+                              int T, int d, int N, bool layout, hipStream_t s);
 hipError_t launch_load_stats(const int32_t* counts, int L, int N, int stride, moer_load_stats_t* out,
                              hipStream_t s);
 hipError_t launch_bias_update(float* bias, const int32_t* counts, int L, int N, int stride,
