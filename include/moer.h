@@ -229,6 +229,23 @@ size_t moer_route_workspace_bytes(const moer_route_desc* desc);
 moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* moer_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call and results, with the scratch memory taken from a static array
+ * of MOER_NOALLOC_SCRATCH_BYTES that each GPU holds from the library's load
+ * until the process ends, instead of a caller workspace. Nothing is
+ * allocated or freed. Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (on different streams, or from different threads)
+ * race and give undefined results. The first call on a device looks the
+ * array up on that device (the current device; the stream, if not NULL,
+ * must belong to it). Returns MOER_EWORKSPACE when the router needs more
+ * scratch than the array holds (moer_route_workspace_bytes(desc) >
+ * MOER_NOALLOC_SCRATCH_BYTES: e.g. a capacity limit on a large batch),
+ * MOER_EINVAL for a stream of another device, else as moer_route. */
+#define MOER_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+moer_status moer_route_noalloc(const moer_route_desc* desc, const moer_route_io* io,
+                               void* stream);
+
 /* Load statistics ("A minimal experiment in expert-load imbalance", Run the
  * example; entropy per the dailyaiworld Mathematics section; std/mean per
  * the hotdry deployment section) of counts[l*stride + e], e < N, for each of

@@ -176,6 +176,20 @@ def test_binding_refuses_buffers_of_the_wrong_size():
         _moer._route_io(desc, counts=torch.zeros(256, dtype=torch.int32))
 
 
+def test_noalloc_rejects_routers_beyond_its_scratch_before_any_gpu_call():
+    # validation and the size check come before the device is touched
+    d = _desc(capacity=640)
+    assert moer.moer_route_workspace_bytes(d) > moer.MOER_NOALLOC_SCRATCH_BYTES
+    st = _moer._lib.moer_route_noalloc(ctypes.byref(d), ctypes.byref(_moer.MoerRouteIO()), None)
+    msg = _moer._lib.moer_last_error().decode()
+    assert st == moer.MOER_EWORKSPACE and "static scratch" in msg, msg
+    st = _moer._lib.moer_route_noalloc(ctypes.byref(_desc(n_layers=0)),
+                                       ctypes.byref(_moer.MoerRouteIO()), None)
+    assert st == moer.MOER_EINVAL
+    # the five workloads without a capacity fit
+    assert moer.moer_route_workspace_bytes(_desc()) <= moer.MOER_NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_sizes():
     # dsv3 shape: partial affinities (one or more depth ranges of 16 MiB each)
     # + entropy partials + block histograms

@@ -45,7 +45,9 @@ from ._moer import (  # noqa: F401
     moer_hotspot_accumulate,
     moer_load_stats,
     moer_route,
+    moer_route_noalloc,
     moer_route_workspace_bytes,
+    MOER_NOALLOC_SCRATCH_BYTES,
 )
 
 _SCORE_FN = {"softmax": MOER_SOFTMAX, "sigmoid": MOER_SIGMOID}

@@ -21,7 +21,7 @@ MOER_BIAS_SCORE, MOER_BIAS_LOGIT = 0, 1
 MOER_RULE_SIGN, MOER_RULE_PROPORTIONAL = 0, 1
 MOER_MAX_EXPERTS, MOER_MAX_SLOTS = 256, 16
 
-EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_load_stats",
+EXPORTED = ("moer_route_workspace_bytes", "moer_route", "moer_route_noalloc", "moer_load_stats",
             "moer_bias_update",
             "moer_balance_step", "moer_dispatch", "moer_combine", "moer_balanced_indices",
             "moer_hotspot_accumulate",
@@ -78,6 +78,8 @@ def _load():
     lib.moer_route.argtypes = [ctypes.POINTER(MoerRouteDesc), ctypes.POINTER(MoerRouteIO), P,
                                ctypes.c_size_t, P]
     lib.moer_route.restype = ctypes.c_int
+    lib.moer_route_noalloc.argtypes = [ctypes.POINTER(MoerRouteDesc), ctypes.POINTER(MoerRouteIO), P]
+    lib.moer_route_noalloc.restype = ctypes.c_int
     lib.moer_load_stats.argtypes = [P, i32, i32, i32, P, P]
     lib.moer_load_stats.restype = ctypes.c_int
     lib.moer_bias_update.argtypes = [P, P, i32, i32, i32, ctypes.c_float, P]
@@ -196,6 +198,16 @@ def moer_route(desc, *, workspace, stream=None, **buffers):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.moer_route(ctypes.byref(desc), ctypes.byref(io), _ptr(ws), nbytes,
                            _stream(stream)))
+
+
+MOER_NOALLOC_SCRATCH_BYTES = 40 << 20
+
+
+def moer_route_noalloc(desc, *, stream=None, **buffers):
+    """Calls moer_route_noalloc (the library's static scratch instead of a
+    workspace) on device tensors."""
+    io = _route_io(desc, **buffers)
+    _check(_lib.moer_route_noalloc(ctypes.byref(desc), ctypes.byref(io), _stream(stream)))
 
 
 class PreparedRoute:

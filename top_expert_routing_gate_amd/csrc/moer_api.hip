@@ -5,8 +5,18 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/moer.h"
 #include "moer_internal.hpp"
+
+// Scratch memory of moer_route_noalloc: one array per GPU, allocated with
+// the code object when the library is loaded on a device and held until the
+// process ends. Host code never passes this name to a kernel (on the host it
+// is only a stand-in symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = MOER_NOALLOC_SCRATCH_BYTES;  // 40 MiB
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -451,6 +461,49 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
   }
 #undef MOER_CHECK
   return ok();
+}
+
+moer_status moer_route_noalloc(const moer_route_desc* desc, const moer_route_io* io,
+                               void* stream) {
+  moer_status st = validate_desc(desc);
+  if (st != MOER_OK) return st;
+  const size_t need = moer_route_workspace_bytes(desc);
+  if (need > kNoAllocScratchBytes)
+    return fail(MOER_EWORKSPACE,
+                "moer_route_noalloc: this router needs %zu bytes of scratch; the static scratch "
+                "holds %zu (use moer_route with a workspace)",
+                need, kNoAllocScratchBytes);
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(MOER_EHIP, "hipGetDevice: %s", hipGetErrorString(he));
+  if (stream != nullptr) {
+    int sdev = -1;
+    he = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (he != hipSuccess) return fail(MOER_EHIP, "hipStreamGetDevice: %s", hipGetErrorString(he));
+    if (sdev != dev)
+      return fail(MOER_EINVAL, "moer_route_noalloc: the stream is on device %d, the current "
+                  "device is %d", sdev, dev);
+  }
+  // the scratch array's device address, looked up once per device with that
+  // device current (each device holds its own copy at its own address)
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOER_EUNSUPPORTED, "moer_route_noalloc: device %d beyond %d", dev, kMaxDevices);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+      void* p = nullptr;
+      he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (he != hipSuccess || p == nullptr)
+        return fail(MOER_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(he));
+      ptr[dev] = p;
+    }
+    ws = ptr[dev];
+  }
+  return moer_route(desc, io, ws, kNoAllocScratchBytes, stream);
 }
 
 moer_status moer_load_stats(const int32_t* counts, int32_t n_layers, int32_t N, int32_t stride,
