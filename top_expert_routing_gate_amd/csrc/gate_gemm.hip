@@ -14,6 +14,10 @@
 namespace moer {
 namespace {
 
+// Partial affinities leave through an LDS transpose as whole rows (true) or
+// straight from the accumulators (false).
+constexpr bool kStoreViaLds = true;
+
 // ---------------------------------------------------------------------------
 // Pipelined kernel: producer waves stream the tiles, consumer waves run the
 // MFMAs and store the depth range's partial affinities.
@@ -34,13 +38,20 @@ __global__ __launch_bounds__((WT * WE + NP) * kWave, 1) void gate_gemm_dma_kerne
   x += (size_t)w.layer * T * d;
   W += (size_t)w.layer * N * d;
   const int wave = threadIdx.x >> 6;
+  float* out = part + ((size_t)w.ks * L + w.layer) * T * N;
+  floatx4 acc[P::ME][P::MT];
   if (wave >= P::kConsumers) {
     P::produce(ring, x, W, t0, e0, T, N, d, w.ks * krange, nk, wave - P::kConsumers);
-    return;
+    if (!kStoreViaLds) return;
+  } else {
+    P::consume(ring, nk, wave / WE, wave % WE, acc);
+    if (!kStoreViaLds) {
+      P::store(acc, out, t0, e0, T, N, wave / WE, wave % WE);
+      return;
+    }
   }
-  floatx4 acc[P::ME][P::MT];
-  P::consume(ring, nk, wave / WE, wave % WE, acc);
-  P::store(acc, part + ((size_t)w.ks * L + w.layer) * T * N, t0, e0, T, N, wave / WE, wave % WE);
+  __syncthreads();  // the ring is free
+  P::store_tile_lds(ring, acc, out, t0, e0, T, N);
 }
 
 // ---------------------------------------------------------------------------

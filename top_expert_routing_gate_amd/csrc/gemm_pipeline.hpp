@@ -190,6 +190,55 @@ struct GemmPipeline {
     return (we * ME + i) * 16 + 4 * ((threadIdx.x & 63) >> 4);
   }
 
+  // Transpose the consumers' blocks through LDS (the ring, free once every
+  // wave has passed the barrier before this call): every wave of the
+  // workgroup then stores whole token rows, 1 KB per instruction (eight full
+  // 128-byte lines), instead of 64-byte pieces of sixteen rows. Chunk c
+  // (four experts) of token row r sits at chunk c ^ (r % 16) of the row (the
+  // row's chunk count, when below 16), so both the accumulator writes
+  // (sixteen rows, one chunk column) and the row reads hit different 16-byte
+  // bank groups. Every wave calls this.
+  static constexpr int kTileChunks = BE / 4;  // 16-byte chunks per token row
+  static constexpr int kSwz = (kTileChunks < 16 ? kTileChunks : 16) - 1;
+  static_assert((size_t)BT * BE * 4 <= kRingBytes, "the tile fits in the ring");
+  static_assert((kTileChunks & (kTileChunks - 1)) == 0, "power-of-two chunks per row");
+  __device__ static void store_tile_lds(u32x4 (*ring)[kStageSlots], const floatx4 (&acc)[ME][MT],
+                                        float* out, int t0, int e0, int T, int N) {
+    u32x4* tile = &ring[0][0];
+    const int wave = threadIdx.x >> 6;
+    if (wave < kConsumers) {
+      const int wt = wave / WE, we = wave % WE;
+#pragma unroll
+      for (int i = 0; i < ME; ++i) {
+        const int c = acc_expert(we, i) / 4;
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const int r = acc_token(wt, j);
+          tile[r * kTileChunks + (c ^ (r & kSwz))] = __builtin_bit_cast(u32x4, acc[i][j]);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int kWaves = kThreads / kWave;
+    constexpr int kRowsPerPass = kWaves * kWave / kTileChunks;  // token rows stored at once
+    const int lane_row = threadIdx.x / kTileChunks;
+    const int c = threadIdx.x % kTileChunks;
+    const int e = e0 + 4 * c;
+    for (int r = lane_row; r < BT; r += kRowsPerPass) {
+      const int t = t0 + r;
+      if (t >= T) break;
+      const floatx4 v = __builtin_bit_cast(floatx4, tile[r * kTileChunks + (c ^ (r & kSwz))]);
+      float* row = out + (size_t)t * N;
+      if (e + 3 < N && (N & 3) == 0) {
+        *reinterpret_cast<floatx4*>(row + e) = v;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (e + q < N) row[e + q] = v[q];
+      }
+    }
+  }
+
   // Store the consumer's block to out[t][e] (row stride N), rows < T only.
   __device__ static void store(const floatx4 (&acc)[ME][MT], float* out, int t0, int e0, int T,
                                int N, int wt, int we) {

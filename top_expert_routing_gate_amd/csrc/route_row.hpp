@@ -135,6 +135,23 @@ __device__ __forceinline__ unsigned long long pack_key(float key, int e) {
 // Score modes: the scores are given, or sigmoid / softmax of the affinities.
 enum { kGiven = 0, kSigmoid = 1, kSoftmax = 2 };
 
+// Router shape, fixed at compile time for the geometries that get kernels
+// of their own (0, or -1 for the shared slots, = taken from the arguments):
+// experts N, routed slots K, groups G, groups kept Gk, shared slots.
+template <int N_ = 0, int K_ = 0, int G_ = 0, int GK_ = 0, int NS_ = -1>
+struct RowShape {
+  __device__ static int n(const ScoreArgs& a) { return N_ > 0 ? N_ : a.N; }
+  __device__ static int k(const ScoreArgs& a) { return K_ > 0 ? K_ : a.K; }
+  __device__ static int g(const ScoreArgs& a) { return G_ > 0 ? G_ : a.G; }
+  __device__ static int gk(const ScoreArgs& a) { return GK_ > 0 ? GK_ : a.Gk; }
+  __device__ static int ns(const ScoreArgs& a) { return NS_ >= 0 ? NS_ : a.n_shared; }
+  static bool matches(const ScoreArgs& a) {
+    return (N_ == 0 || a.N == N_) && (K_ == 0 || a.K == K_) && (G_ == 0 || a.G == G_) &&
+           (GK_ == 0 || a.Gk == GK_) && (NS_ < 0 || a.n_shared == NS_);
+  }
+};
+using AnyShape = RowShape<>;
+
 // Hardware transcendentals (v_exp_f32, v_rcp_f32, v_log_f32: about 1 ulp):
 // the affinities already carry ~1e-6 GEMM rounding, so the scores only need
 // to be accurate well inside the 1e-3 weight and 1e-4 entropy tolerances.
@@ -184,14 +201,15 @@ struct LaneConsts {
   float bias[EPL];
   float offset[EPL];
 };
-template <int EPL>
+template <int EPL, class S = AnyShape>
 __device__ __forceinline__ void load_lane_consts(const ScoreArgs& a, int layer, bool with_offset,
                                                  LaneConsts<EPL>& c) {
+  const int N = S::n(a);
   const int e0 = (threadIdx.x & 15) * EPL;
-  const float* b = a.bias != nullptr ? a.bias + (size_t)layer * a.N : nullptr;
+  const float* b = a.bias != nullptr ? a.bias + (size_t)layer * N : nullptr;
   const float* o = with_offset ? a.offset : nullptr;
   auto fill = [&](const float* src, float (&dst)[EPL]) {
-    if (src != nullptr && EPL % 4 == 0 && e0 + EPL <= a.N && (a.N & 3) == 0) {
+    if (src != nullptr && EPL % 4 == 0 && e0 + EPL <= N && (N & 3) == 0) {
 #pragma unroll
       for (int j = 0; j < EPL / 4; ++j) {
         const float4 f = reinterpret_cast<const float4*>(src + e0)[j];
@@ -199,7 +217,7 @@ __device__ __forceinline__ void load_lane_consts(const ScoreArgs& a, int layer, 
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) dst[j] = (src != nullptr && e0 + j < a.N) ? src[e0 + j] : 0.f;
+      for (int j = 0; j < EPL; ++j) dst[j] = (src != nullptr && e0 + j < N) ? src[e0 + j] : 0.f;
     }
   };
   fill(b, c.bias);
@@ -220,12 +238,13 @@ __device__ __forceinline__ void load_lane_consts(const ScoreArgs& a, int layer, 
 // the clearing made visible by a barrier, before the call). q: this lane's
 // q = s / sum s (0 when dead). All 16 lanes of the row must call together;
 // rows are independent.
-template <int EPL, bool GROUPED, int MODE, int LPG = 0>
+template <int EPL, bool GROUPED, int MODE, int LPG = 0, class S = AnyShape>
 __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, bool live,
                                           float (&v)[EPL], const LaneConsts<EPL>& lc,
                                           const RowLds& rs, int* hist, float (&q)[EPL]) {
-  const int N = a.N, K = a.K, T = a.T;
-  const int Kt = K + a.n_shared;
+  const int N = S::n(a), K = S::k(a), T = a.T;
+  const int G = S::g(a), Gk = S::gk(a);
+  const int Kt = K + S::ns(a);
   const int rl = threadIdx.x & 15;  // lane within the row
   const int e0 = rl * EPL;
   const bool full = e0 + EPL <= N;  // every expert of this lane exists
@@ -300,10 +319,12 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   for (int j = 0; j < EPL; ++j) q[j] = s[j] * inv_s;
 
   // the lane's two largest keys (used by both the group stage and the bound)
+  // (lt1 >= lt2 throughout: the new second largest of {lt1, lt2, k} is the
+  // median of the three)
   float lt1 = key[0], lt2 = NEG_INF;
 #pragma unroll
   for (int j = 1; j < EPL; ++j) {
-    lt2 = fmaxf(lt2, fminf(lt1, key[j]));
+    lt2 = __builtin_amdgcn_fmed3f(lt1, lt2, key[j]);
     lt1 = fmaxf(lt1, key[j]);
   }
 
@@ -311,7 +332,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   bool eligible = true;
   float group_m2 = NEG_INF;  // second largest key of this lane's group
   if (GROUPED) {
-    const int lpg = LPG > 0 ? LPG : (N / a.G) / EPL;  // lanes per group (power of two, <= 16)
+    const int lpg = LPG > 0 ? LPG : (N / G) / EPL;  // lanes per group (power of two, <= 16)
     const int g = rl / lpg;
     float m1 = lt1, m2 = lt2;
     // merge the group's lanes (lanes of a group are aligned, lpg a power of 2)
@@ -324,21 +345,21 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     if (lpg >= 4) merge(dpp_f<kXor2>(m1), dpp_f<kXor2>(m2));
     if (lpg >= 8) merge(dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
     if (lpg >= 16) merge(dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
-    const float gs = (g < a.G) ? m1 + m2 : NEG_INF;
-    const int gid = g < a.G ? g : 0x7FFF;
+    const float gs = (g < G) ? m1 + m2 : NEG_INF;
+    const int gid = g < G ? g : 0x7FFF;
     // rank among the row's groups: rotate (score, id) by whole groups
     int rank = 0;
 #define MOER_ROT(n)                                                                  \
     if ((n) % lpg == 0) {                                                            \
       const float og = dpp_f<0x120 + (n)>(gs);                                       \
       const int oid = dpp_i<0x120 + (n)>(gid);                                       \
-      rank += (oid < a.G && (og > gs || (og == gs && oid < gid))) ? 1 : 0;           \
+      rank += (oid < G && (og > gs || (og == gs && oid < gid))) ? 1 : 0;             \
     }
     MOER_ROT(1) MOER_ROT(2) MOER_ROT(3) MOER_ROT(4) MOER_ROT(5) MOER_ROT(6) MOER_ROT(7)
     MOER_ROT(8) MOER_ROT(9) MOER_ROT(10) MOER_ROT(11) MOER_ROT(12) MOER_ROT(13) MOER_ROT(14)
     MOER_ROT(15)
 #undef MOER_ROT
-    eligible = g < a.G && rank < a.Gk;
+    eligible = g < G && rank < Gk;
     group_m2 = m2;
   }
 
@@ -369,7 +390,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   // lo: a key that at least K distinct eligible experts reach, so every chosen
   // expert has key >= lo.
   float lo;
-  if (GROUPED && 2 * a.Gk == K) {
+  if (GROUPED && 2 * Gk == K) {
     // the kept groups' two largest keys are exactly K such experts: lo is
     // the smallest of them (the groups' second keys)
     lo = row_min(eligible ? group_m2 : __builtin_inff());

@@ -13,15 +13,16 @@ namespace {
 
 constexpr int kThreads = kRowTokens * kRowLanes;  // 1024: one row per token
 
-template <int EPL>
+template <int EPL, class S>
 __device__ __forceinline__ void load_row(const ScoreArgs& a, size_t row_off, size_t split_stride,
                                          int e0, float (&v)[EPL]) {
   // EPL consecutive experts per lane, depth-range partials added in order;
   // 16-byte loads when the lane's range is whole and aligned
+  const int N = S::n(a);
 #pragma unroll
   for (int j = 0; j < EPL; ++j) v[j] = 0.f;
-  if (e0 >= a.N) return;
-  if (EPL % 4 == 0 && e0 + EPL <= a.N && (a.N & 3) == 0) {
+  if (e0 >= N) return;
+  if (EPL % 4 == 0 && e0 + EPL <= N && (N & 3) == 0) {
     for (int sp = 0; sp < a.nsplit; ++sp) {
       const float4* src = reinterpret_cast<const float4*>(a.in + sp * split_stride + row_off + e0);
 #pragma unroll
@@ -40,14 +41,14 @@ __device__ __forceinline__ void load_row(const ScoreArgs& a, size_t row_off, siz
     const float* src = a.in + sp * split_stride + row_off;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-      const int e = min(e0 + j, a.N - 1);
-      const float q = (e0 + j < a.N) ? src[e] : 0.f;
+      const int e = min(e0 + j, N - 1);
+      const float q = (e0 + j < N) ? src[e] : 0.f;
       v[j] = sp == 0 ? q : v[j] + q;
     }
   }
 }
 
-template <int EPL, bool GROUPED, int MODE, int LPG>
+template <int EPL, bool GROUPED, int MODE, int LPG, class S>
 __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   __shared__ Cand cand[kRowTokens][kCandStride];
   __shared__ int slot_id[kRowTokens][kMaxSlots];
@@ -56,8 +57,8 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   constexpr int kWaves = kThreads / kWave;
   __shared__ __attribute__((aligned(16))) float colw[kWaves][kRowLanes * EPL];
 
-  const int N = a.N, T = a.T;
-  const int Nb = N + a.n_shared;
+  const int N = S::n(a), T = a.T;
+  const int Nb = N + S::ns(a);
   const int layer = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int rl = lane & 15;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
 
   for (int i = threadIdx.x; i < Nb; i += kThreads) hist[i] = 0;
   LaneConsts<EPL> lc;
-  load_lane_consts<EPL>(a, layer, MODE != kGiven, lc);
+  load_lane_consts<EPL, S>(a, layer, MODE != kGiven, lc);
   const size_t row_off = ((size_t)layer * T + (live ? t : 0)) * N;
   const size_t split_stride = (size_t)gridDim.y * T * N;
   float v[EPL];
@@ -79,13 +80,13 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   // halves' data arrives while only half of the launch's loads are in
   // flight, and those rows are routed while the second halves stream in.
   const bool first_half = row < kRowTokens / 2;
-  if (live && first_half) load_row<EPL>(a, row_off, split_stride, rl * EPL, v);
+  if (live && first_half) load_row<EPL, S>(a, row_off, split_stride, rl * EPL, v);
   __syncthreads();  // histogram cleared; first-half rows loaded
-  if (live && !first_half) load_row<EPL>(a, row_off, split_stride, rl * EPL, v);
+  if (live && !first_half) load_row<EPL, S>(a, row_off, split_stride, rl * EPL, v);
 
   const RowLds rs{cand[row], slot_id[row], slot_s[row]};
   float q[EPL];
-  route_row<EPL, GROUPED, MODE, LPG>(a, layer, t, live, v, lc, rs, hist, q);
+  route_row<EPL, GROUPED, MODE, LPG, S>(a, layer, t, live, v, lc, rs, hist, q);
   if (a.colpart != nullptr) {
     // the wavefront's column sums of q over its 4 rows (zero for tokens past
     // T), (row0 + row1) + (row2 + row3), by lane swaps between rows and
@@ -128,12 +129,18 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   }
 }
 
-template <int EPL, bool GROUPED, int LPG = 0>
+template <int EPL, bool GROUPED, int LPG = 0, class S = AnyShape>
 auto pick_kernel(const ScoreArgs& a) {
-  if (!a.apply_score) return route_rows_kernel<EPL, GROUPED, kGiven, LPG>;
-  if (a.score_fn == 1) return route_rows_kernel<EPL, GROUPED, kSigmoid, LPG>;
-  return route_rows_kernel<EPL, GROUPED, kSoftmax, LPG>;
+  if (!a.apply_score) return route_rows_kernel<EPL, GROUPED, kGiven, LPG, S>;
+  if (a.score_fn == 1) return route_rows_kernel<EPL, GROUPED, kSigmoid, LPG, S>;
+  return route_rows_kernel<EPL, GROUPED, kSoftmax, LPG, S>;
 }
+
+// Shapes with kernels of their own (everything fixed at compile time): the
+// DeepSeek-V3 router (256 experts, 8 groups of 32, keep 4, top-8) and the
+// decode-shaped router (256 experts, top-8 plus one shared slot).
+using DeepSeekV3Shape = RowShape<256, 8, 8, 4, 0>;
+using DecodeShape = RowShape<256, 8, 1, 1, 1>;
 
 template <int EPL>
 hipError_t launch_epl(const ScoreArgs& a, int L, hipStream_t s) {
@@ -143,6 +150,10 @@ hipError_t launch_epl(const ScoreArgs& a, int L, hipStream_t s) {
   const bool two_lane_groups = EPL == 16 && a.G > 1 && a.N / a.G == 2 * EPL;
   auto k = a.G > 1 ? (two_lane_groups ? pick_kernel<EPL, true, 2>(a) : pick_kernel<EPL, true>(a))
                    : pick_kernel<EPL, false>(a);
+  if constexpr (EPL == 16) {
+    if (DeepSeekV3Shape::matches(a)) k = pick_kernel<EPL, true, 2, DeepSeekV3Shape>(a);
+    if (DecodeShape::matches(a)) k = pick_kernel<EPL, false, 0, DecodeShape>(a);
+  }
   hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
