@@ -64,42 +64,53 @@ __device__ void block_exclusive_scan(int* v, int* tmp, int n) {
 
 // total[e] = the layer's assignments of expert e (e < Nb) and, with lb >= 0,
 // pre[e] = those in tokens before layout block lb: the segments wholly before
-// it plus the blocks of its own segment before it.
+// it plus the blocks of its own segment before it. Every load is issued before
+// any is used (clamped indices, values masked afterwards), so the block
+// counts and the segment totals share one memory round trip.
 template <int NT>
 __device__ void load_totals(const LayoutArgs& a, int layer, int lb, int* total, int* pre) {
-  constexpr int kMaxSeg = 32;  // segments summed from registers; more take a loop
-  const int b_first = lb;
-  const int s_own = lb >= 0 ? b_first / kSegBlocks : 0;
-  const int32_t* seg = a.segsum + (size_t)layer * a.nseg * a.Nb;
+  constexpr int kSegChunk = 16;  // segment totals loaded at once per expert
+  static_assert(kSegBlocks % 8 == 0, "whole 16-byte loads of block counts per segment");
+  constexpr int kVec = kSegBlocks / 8;
+  const int nseg = a.nseg;
+  const int s_own = lb >= 0 ? lb / kSegBlocks : 0;
+  const int b0 = s_own * kSegBlocks;
+  const bool vec = lb >= 0 && (a.nsb & 7) == 0 && b0 + kSegBlocks <= a.nsb;
+  const int32_t* seg = a.segsum + (size_t)layer * nseg * a.Nb;
   for (int e = threadIdx.x; e < a.Nb; e += NT) {
+    const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
+    uint4 q[kVec];
+    if (vec) {
+      const uint4* r4 = reinterpret_cast<const uint4*>(row + b0);
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) q[k] = r4[k];
+    }
     int tot = 0, p = 0;
-    for (int s0 = 0; s0 < a.nseg; s0 += kMaxSeg) {
-      int v[kMaxSeg];
+    for (int s0 = 0; s0 < nseg; s0 += kSegChunk) {
+      int v[kSegChunk];
 #pragma unroll
-      for (int k = 0; k < kMaxSeg; ++k)
-        v[k] = s0 + k < a.nseg ? seg[(size_t)(s0 + k) * a.Nb + e] : 0;
+      for (int k = 0; k < kSegChunk; ++k) v[k] = seg[(size_t)min(s0 + k, nseg - 1) * a.Nb + e];
 #pragma unroll
-      for (int k = 0; k < kMaxSeg; ++k) {
-        tot += v[k];
-        p += s0 + k < s_own ? v[k] : 0;
+      for (int k = 0; k < kSegChunk; ++k) {
+        const bool in = s0 + k < nseg;
+        tot += in ? v[k] : 0;
+        p += (in && s0 + k < s_own) ? v[k] : 0;
       }
     }
     if (lb >= 0) {
-      const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
-      const int b0 = s_own * kSegBlocks;
-      if ((a.nsb & 7) == 0 && b0 + kSegBlocks <= a.nsb) {
-        // the segment's block counts as two 16-byte loads, masked
-        static_assert(kSegBlocks == 16, "two uint4 per segment");
-        const uint4* r4 = reinterpret_cast<const uint4*>(row + b0);
-        const uint4 q0 = r4[0], q1 = r4[1];
-        const unsigned w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      if (vec) {
+        // the own segment's earlier blocks, eight uint16 counts per load
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int b = b0 + 2 * k;
-          p += (b < b_first ? (int)(w[k] & 0xFFFF) : 0) + (b + 1 < b_first ? (int)(w[k] >> 16) : 0);
+        for (int k = 0; k < kVec; ++k) {
+          const unsigned w[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int b = b0 + 8 * k + 2 * m;
+            p += (b < lb ? (int)(w[m] & 0xFFFF) : 0) + (b + 1 < lb ? (int)(w[m] >> 16) : 0);
+          }
         }
       } else {
-        for (int b = b0; b < b_first; ++b) p += row[b];
+        for (int b = b0; b < lb; ++b) p += row[b];
       }
       pre[e] = p;
     }
