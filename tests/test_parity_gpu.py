@@ -162,6 +162,46 @@ def test_hidden_mode_small(wl):
     _hidden_case(wl, wl.name)
 
 
+# Routers with at most 16 experts and 4096 tokens take the one-launch gate
+# GEMM + selection kernel (bf16 with d a multiple of 128, fp32 with d a
+# multiple of 64); the variable MOER_ROUTE_SMALL=0 keeps them on the
+# separate GEMM and selection launches.
+# Shapes: depth with fewer 128-element steps than the kernel's four depth
+# parts (d = 128, 384) and an odd step count, ragged token tails, one token,
+# a single expert, grouped experts (16 in 4 groups of 4), shared slots,
+# several layers, a logit offset (the collapse recipe's celebrity experts)
+# and logit-space bias, fp32 at the depth
+# limit and just past it.
+SMALL_ROUTERS = [
+    workloads.scaled(WL["mixtral_top2"], T=4096),
+    workloads.scaled(WL["mixtral_top2"], T=77, d=128),
+    workloads.scaled(WL["mixtral_top2"], T=1, d=384, N=5, K=3),
+    workloads.scaled(WL["mixtral_top2"], T=200, d=4224, N=16, K=4, n_groups=4, topk_groups=2,
+                     n_shared=2),
+    workloads.scaled(WL["mixtral_top2"], T=130, d=640, N=1, K=1),
+    workloads.scaled(WL["mixtral_top2"], T=150, d=1024, N=12, K=2, n_layers=3),
+    workloads.scaled(WL["dsv3_group"], T=300, d=896, N=16, K=6, n_groups=2, topk_groups=1),
+    workloads.scaled(WL["collapse_balance"], T=100, d=512, N=16, K=2, n_groups=1,
+                     topk_groups=1),
+    workloads.scaled(WL["tiny_softmax"], T=130, d=2048, N=16, K=3),
+    workloads.scaled(WL["tiny_softmax"], T=70, d=2052, N=9, K=2),
+    workloads.scaled(WL["tiny_softmax"], T=65, d=12, N=3, K=2, n_shared=1),
+    workloads.scaled(WL["mixtral_top2"], T=5000, d=512),
+]
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["one_launch", "split_launches"])
+@pytest.mark.parametrize("wl", SMALL_ROUTERS,
+                         ids=lambda w: f"{w.name}-T{w.T}-d{w.d}-N{w.N}-G{w.n_groups}-L{w.n_layers}")
+def test_hidden_mode_small_routers(wl, split, monkeypatch):
+    if split:
+        monkeypatch.setenv("MOER_ROUTE_SMALL", "0")
+    say(f"[hidden/small-router] split={split} {wl}")
+    _hidden_case(wl, wl.name)
+    if wl.N <= 12 and wl.n_layers == 1:
+        _hidden_case(wl, wl.name + " logit-space bias", bias_mode="logit")
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["mixtral_top2", "dsv3_group", "collapse_balance",
                                   "decode_layers"])

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoer.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["moer_api.hip", "gate_gemm.hip", "route_rows.hip", "route_fused.hip", "score_topk.hip", "layout.hip",
+SOURCES = ["moer_api.hip", "gate_gemm.hip", "route_rows.hip", "route_small.hip", "route_fused.hip", "score_topk.hip", "layout.hip",
            "stats.hip", "dispatch_combine.hip",
            "forcible.hip", "capacity.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -62,23 +62,69 @@ __device__ void block_exclusive_scan(int* v, int* tmp, int n) {
   __syncthreads();
 }
 
+// No segment totals (16-token histogram blocks): the block counts of every
+// expert, eight per 16-byte load, spread over the whole workgroup and added
+// into total / pre with LDS integer atomics (any order gives the same sums).
+// Layout block lb starts at histogram block lb << hist_shift.
+template <int NT>
+__device__ void sum_block_counts(const LayoutArgs& a, int layer, int lb, int* total, int* pre) {
+  const int hb = lb >= 0 ? lb << a.hist_shift : 0;
+  const int nch = (a.nsb + 7) / 8;
+  for (int e = threadIdx.x; e < a.Nb; e += NT) {
+    total[e] = 0;
+    if (lb >= 0) pre[e] = 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.Nb * nch; i += NT) {
+    const int e = i / nch, c = i - e * nch;
+    const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
+    const int b0 = 8 * c;
+    int tot = 0, p = 0;
+    if ((a.nsb & 7) == 0) {
+      const uint4 w4 = reinterpret_cast<const uint4*>(row)[c];
+      const unsigned w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int b = b0 + 2 * m;
+        const int c0 = (int)(w[m] & 0xFFFF), c1 = (int)(w[m] >> 16);
+        tot += c0 + c1;
+        p += (b < hb ? c0 : 0) + (b + 1 < hb ? c1 : 0);
+      }
+    } else {
+      for (int b = b0; b < min(b0 + 8, a.nsb); ++b) {
+        const int cb = row[b];
+        tot += cb;
+        p += b < hb ? cb : 0;
+      }
+    }
+    if (tot != 0) atomicAdd(&total[e], tot);
+    if (p != 0) atomicAdd(&pre[e], p);
+  }
+}
+
 // total[e] = the layer's assignments of expert e (e < Nb) and, with lb >= 0,
 // pre[e] = those in tokens before layout block lb: the segments wholly before
-// it plus the blocks of its own segment before it. Every load is issued before
-// any is used (clamped indices, values masked afterwards), so the block
-// counts and the segment totals share one memory round trip.
+// it plus the blocks of its own segment before it (with no segment totals:
+// sums of the block counts, above). Complete after the caller's next
+// barrier. Every load is issued before any is used (clamped indices, values
+// masked afterwards), so the block counts and the segment totals share one
+// memory round trip.
 template <int NT>
 __device__ void load_totals(const LayoutArgs& a, int layer, int lb, int* total, int* pre) {
   constexpr int kSegChunk = 16;  // segment totals loaded at once per expert
   static_assert(kSegBlocks % 8 == 0, "whole 16-byte loads of block counts per segment");
   constexpr int kVec = kSegBlocks / 8;
+  if (a.segsum == nullptr) {
+    sum_block_counts<NT>(a, layer, lb, total, pre);
+    return;
+  }
   const int nseg = a.nseg;
   const int s_own = lb >= 0 ? lb / kSegBlocks : 0;
   const int b0 = s_own * kSegBlocks;
   const bool vec = lb >= 0 && (a.nsb & 7) == 0 && b0 + kSegBlocks <= a.nsb;
-  const int32_t* seg = a.segsum + (size_t)layer * nseg * a.Nb;
   for (int e = threadIdx.x; e < a.Nb; e += NT) {
     const uint16_t* row = a.cnt + ((size_t)layer * a.Nb + e) * a.nsb;
+    const int32_t* seg = a.segsum + (size_t)layer * nseg * a.Nb;
     uint4 q[kVec];
     if (vec) {
       const uint4* r4 = reinterpret_cast<const uint4*>(row + b0);

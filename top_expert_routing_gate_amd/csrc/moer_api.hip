@@ -4,7 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/moer.h"
@@ -52,6 +54,7 @@ moer_status check_rows(int32_t n_layers, int32_t T, int32_t Kt) {
 // Workspace regions (byte offsets) for a validated descriptor.
 struct Plan {
   int Kt, Nb, nsb, nlb, ksplit;
+  int nsb_small;  // 16-token histogram blocks of the one-launch small-router kernel (0: none)
   int nseg;
   int nsync;  // fused pass counters, stored right after the segment totals
   size_t off_h, off_colpart, off_cnt, off_seg, off_colmean, total;
@@ -71,13 +74,17 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   p.nsb = (d.T + moer::kRowTokens - 1) / moer::kRowTokens;
   p.nlb = d.T > 0 ? (d.T + moer::kLayoutTokens - 1) / moer::kLayoutTokens : 1;
   p.ksplit = hidden ? moer::gate_gemm_ksplit(d.dtype == MOER_BF16, d.n_layers, d.T, d.d, d.N) : 1;
+  // routers the one-launch small kernel may take: room for its finer blocks
+  p.nsb_small = hidden && d.N <= moer::kSmallMaxExperts
+                    ? (d.T + moer::kSmallTokens - 1) / moer::kSmallTokens : 0;
+  const size_t nsb_room = (size_t)std::max(p.nsb, p.nsb_small);
   size_t o = 0;
   p.off_h = o;  // partial affinities of the gate GEMM
   if (hidden) o += align_up((size_t)p.ksplit * L * d.T * d.N * sizeof(float));
-  p.off_colpart = o;  // column sums of q per 64-token block
-  if (want_agg) o += align_up(L * p.nsb * d.N * sizeof(float) + 16);
-  p.off_cnt = o;  // expert histograms per 64-token block (uint16)
-  o += align_up(L * p.Nb * p.nsb * sizeof(uint16_t) + 16);
+  p.off_colpart = o;  // column sums of q per histogram block
+  if (want_agg) o += align_up(L * nsb_room * d.N * sizeof(float) + 16);
+  p.off_cnt = o;  // expert histograms per histogram block (uint16)
+  o += align_up(L * p.Nb * nsb_room * sizeof(uint16_t) + 16);
   p.nseg = (p.nsb + moer::kSegBlocks - 1) / moer::kSegBlocks;
   p.off_seg = o;  // expert counts per segment of histogram blocks, then the
                   // fused pass's counters (one zero fill clears both)
@@ -147,6 +154,15 @@ int fused_mode() {
   const char* v = getenv("MOER_ROUTE_FUSED");
   if (v == nullptr || *v == '\0') return 0;
   return atoi(v);
+}
+
+// One-launch gate GEMM + selection for routers with at most 16 experts,
+// chosen by the environment variable MOER_ROUTE_SMALL: on (the default)
+// unless it is "0", which keeps such routers on the separate gate GEMM and
+// selection launches.
+bool small_enabled() {
+  const char* v = getenv("MOER_ROUTE_SMALL");
+  return v == nullptr || strcmp(v, "0") != 0;
 }
 
 // Which selection kernel takes this shape: 1 = one 16-lane row per token,
@@ -363,6 +379,23 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
                                         d.T, d.d, d.N, fused != 2, s));
     if (io->ev_gemm_end) MOER_CHECK(hipEventRecord(static_cast<hipEvent_t>(io->ev_gemm_end), s));
     if (fused == 2) MOER_CHECK(moer::launch_layout(la, L, s));
+    return ok();
+  }
+
+  // Routers with at most 16 experts: every expert of a token fits one
+  // workgroup, which forms the affinities and routes them in one launch.
+  if (hidden && d.T > 0 && !capped && path == 1 && io->ev_select_wait == nullptr &&
+      small_enabled() &&
+      moer::route_small_eligible(d.dtype == MOER_BF16, d.T, d.d, d.N, d.n_groups,
+                                 aligned16(io->x) && aligned16(io->w_gate))) {
+    a.segsum = nullptr;  // the layout sums the block counts itself
+    la.segsum = nullptr;
+    la.nsb = p.nsb_small;
+    la.hist_shift = moer::kSmallShift;
+    MOER_CHECK(moer::launch_route_small(a, io->x, io->w_gate, d.d, d.dtype == MOER_BF16, L, s,
+                                        static_cast<hipEvent_t>(io->ev_gemm_begin),
+                                        static_cast<hipEvent_t>(io->ev_gemm_end)));
+    MOER_CHECK(moer::launch_layout(la, L, s));
     return ok();
   }
 

@@ -49,6 +49,9 @@ struct LayoutArgs {
   float* bias_inout;      // [L][N] updated in place, or nullptr
   float bias_step;
   int T, Kt, Nb, N, nlb, nsb, nseg, fill_invalid, need_count;
+  // histogram blocks per layout block = 1 << hist_shift (> 0 only for
+  // 16-token histogram blocks, which carry no segment totals: segsum null)
+  int hist_shift;
   // capacity-limited routing: phase 1 = the layout of the top-K ids (one
   // balance workgroup per layer sets cap_flag[l] when a routed expert holds
   // more than cap, and does the statistics / bias update only when none
@@ -79,6 +82,18 @@ hipError_t launch_score_topk(const ScoreArgs& a, int L, hipStream_t s);
 int route_rows_epl(int N);
 bool route_rows_supports(int N, int G);
 hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s);
+// Gate GEMM and selection in one launch for at most 16 experts and 4096
+// tokens (bf16 with d a multiple of 128, or fp32 with d a multiple of 64;
+// x and W_g 16-byte aligned). Its histogram blocks are kSmallTokens tokens
+// (cnt [L][Nb][ceil(T / kSmallTokens)], colpart likewise) and carry no
+// segment totals: ScoreArgs segsum null, LayoutArgs segsum null with
+// hist_shift = kSmallShift. ev0 / ev1 (optional) bracket the launch.
+constexpr int kSmallTokens = 16;
+constexpr int kSmallShift = 2;  // kRowTokens / kSmallTokens = 4 blocks per layout block
+constexpr int kSmallMaxExperts = 16;
+bool route_small_eligible(bool bf16, int T, int d, int N, int G, bool aligned);
+hipError_t launch_route_small(const ScoreArgs& a, const void* x, const void* W, int d, bool bf16,
+                              int L, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_layout(const LayoutArgs& a, int L, hipStream_t s);
 // Fused router pass (gate GEMM in two depth halves exchanging partials
 // pairwise, selection from LDS, then the layout after a grid barrier): can it

@@ -505,4 +505,58 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   }
 }
 
+// The block outputs of a selection workgroup of NT threads (NT / 16 rows, one
+// 64-token histogram block per workgroup, blockIdx.x = block), once every row
+// has been routed: the block's expert histogram cnt[l][e][b], its running
+// segment totals, and its column sums of q. colw: LDS [NT / 64][16 * EPL].
+// Every thread of the workgroup must call (it holds a barrier).
+template <int EPL, int NT>
+__device__ __forceinline__ void block_outputs(const ScoreArgs& a, int layer, int N, int Nb,
+                                              const float (&q)[EPL], const int* hist,
+                                              float (*colw)[kRowLanes * EPL]) {
+  constexpr int kWaves = NT / kWave;
+  const int lane = threadIdx.x & 63;
+  const int rl = lane & 15;
+  if (a.colpart != nullptr) {
+    // the wavefront's column sums of q over its 4 rows (zero for tokens past
+    // T), (row0 + row1) + (row2 + row3), by lane swaps between rows and
+    // between wave halves; every lane adds the same operands in the same order
+    float cs[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[j]),
+                                                      __float_as_uint(q[j]), false, false);
+      const float pair = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
+                                                      __float_as_uint(pair), false, false);
+      cs[j] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    }
+    if (lane < kRowLanes) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) colw[threadIdx.x >> 6][rl * EPL + j] = cs[j];
+    }
+  }
+  __syncthreads();
+  if (a.cnt != nullptr) {
+    uint16_t* out = a.cnt + (size_t)layer * Nb * gridDim.x + blockIdx.x;
+    for (int e = threadIdx.x; e < Nb; e += NT) out[(size_t)e * gridDim.x] = (uint16_t)hist[e];
+  }
+  if (a.segsum != nullptr) {
+    // running totals per segment of blocks (integer adds: any order, same sum)
+    const int nseg = (gridDim.x + kSegBlocks - 1) / kSegBlocks;
+    int32_t* seg = a.segsum + ((size_t)layer * nseg + blockIdx.x / kSegBlocks) * Nb;
+    for (int e = threadIdx.x; e < Nb; e += NT)
+      if (hist[e] != 0) atomicAdd(&seg[e], hist[e]);
+  }
+  if (a.colpart != nullptr) {
+    // the block's column sums: the wavefronts' sums in wavefront order
+    for (int e = threadIdx.x; e < N; e += NT) {
+      float acc = colw[0][e];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) acc += colw[w][e];
+      a.colpart[((size_t)layer * gridDim.x + blockIdx.x) * N + e] = acc;
+    }
+  }
+}
+
 }  // namespace moer

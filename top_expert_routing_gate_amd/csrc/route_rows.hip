@@ -87,46 +87,7 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   const RowLds rs{cand[row], slot_id[row], slot_s[row]};
   float q[EPL];
   route_row<EPL, GROUPED, MODE, LPG, S>(a, layer, t, live, v, lc, rs, hist, q);
-  if (a.colpart != nullptr) {
-    // the wavefront's column sums of q over its 4 rows (zero for tokens past
-    // T), (row0 + row1) + (row2 + row3), by lane swaps between rows and
-    // between wave halves; every lane adds the same operands in the same order
-    float cs[EPL];
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[j]),
-                                                      __float_as_uint(q[j]), false, false);
-      const float pair = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-      const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
-                                                      __float_as_uint(pair), false, false);
-      cs[j] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    }
-    if (lane < kRowLanes) {
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) colw[threadIdx.x >> 6][rl * EPL + j] = cs[j];
-    }
-  }
-  __syncthreads();
-  if (a.cnt != nullptr) {
-    uint16_t* out = a.cnt + (size_t)layer * Nb * gridDim.x + blockIdx.x;
-    for (int e = threadIdx.x; e < Nb; e += kThreads) out[(size_t)e * gridDim.x] = (uint16_t)hist[e];
-  }
-  if (a.segsum != nullptr) {
-    // running totals per segment of blocks (integer adds: any order, same sum)
-    const int nseg = (gridDim.x + kSegBlocks - 1) / kSegBlocks;
-    int32_t* seg = a.segsum + ((size_t)layer * nseg + blockIdx.x / kSegBlocks) * Nb;
-    for (int e = threadIdx.x; e < Nb; e += kThreads)
-      if (hist[e] != 0) atomicAdd(&seg[e], hist[e]);
-  }
-  if (a.colpart != nullptr) {
-    // the block's column sums: the wavefronts' sums in wavefront order
-    for (int e = threadIdx.x; e < N; e += kThreads) {
-      float acc = colw[0][e];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) acc += colw[w][e];
-      a.colpart[((size_t)layer * gridDim.x + blockIdx.x) * N + e] = acc;
-    }
-  }
+  block_outputs<EPL, kThreads>(a, layer, N, Nb, q, hist, colw);
 }
 
 template <int EPL, bool GROUPED, int LPG = 0, class S = AnyShape>
