@@ -833,7 +833,7 @@ def run_report(args):
                    f"{L * T / (med * 1e-6) / 1e6:.1f} M | {t_roof * 1e6:.2f} | "
                    f"{100 * t_roof / (med * 1e-6):.1f} | {r_all / 1e3:.1f} k ({all_cores}) | "
                    f"{r_one / 1e3:.2f} k |")
-        if name in ("tiny_softmax", "decode_layers"):
+        if name in ("tiny_softmax", "mixtral_top2", "decode_layers"):
             graph_rows += graph_timing(moer, torch, wl, desc, xd, Wd, b0.to(dev), offd, ev,
                                        pair_us, stream)
         del xd, Wd, ws, outs
@@ -841,8 +841,16 @@ def run_report(args):
             "tokens), including load statistics and the bias update.", "",
             "## HIP graph replay", "",
             "The route call (no bias update, so replays repeat the same work) captured once "
-            "and replayed; every replay's outputs equal the eager call's.", "",
-            "| case | eager median us | graph replay median us |", "|---|---|---|"] + graph_rows
+            "and replayed; every replay's outputs equal the eager call's. Host: time to "
+            "submit one call (200 in a row, no synchronisation). GPU: time per call of 200 "
+            "calls run back to back (queued behind a spin kernel, so the host cost is "
+            "hidden). Paired: one call between an event pair, the pairs queued behind the "
+            "spin (median, less an empty pair). Alone: the same with the host waiting for "
+            "each call to finish before submitting the next (median, less an empty pair).",
+            "",
+            "| case | host us eager | host us graph | GPU us/call eager | GPU us/call graph "
+            "| paired us eager | paired us graph | alone us eager | alone us graph |",
+            "|---|---|---|---|---|---|---|---|---|"] + graph_rows
     out += ["", "## Collapse workload: 100 balancing iterations", ""] + collapse_series(
         moer, torch, workloads, ev, pair_us, stream)
     out += ["", "Clocks after: " + "; ".join(_clocks())]
@@ -895,23 +903,51 @@ def graph_timing(moer, torch, wl, desc, x, W, bias, off, ev, pair_us, stream):
         reps = 200
         for _ in range(50):
             eager()
-        for i in range(reps):
-            ev.record(ev.pairs[i][0], stream)
-            eager()
-            ev.record(ev.pairs[i][1], stream)
         torch.cuda.synchronize()
-        te = [ev.elapsed_ms(i) * 1e3 - pair_us for i in range(reps)]
+        res = {}
         with torch.cuda.stream(stream):
-            for i in range(reps):
-                ev.record(ev.pairs[i][0], stream)
-                g.replay()
-                ev.record(ev.pairs[i][1], stream)
-        torch.cuda.synchronize()
-        tg = [ev.elapsed_ms(i) * 1e3 - pair_us for i in range(reps)]
+            for kind, fn in (("eager", eager), ("graph", g.replay)):
+                # host time to submit one call (no synchronisation in between)
+                t0 = time.perf_counter()
+                for _ in range(reps):
+                    fn()
+                host = (time.perf_counter() - t0) / reps * 1e6
+                torch.cuda.synchronize()
+                # GPU time per call: the stream is held by a spin kernel long
+                # enough for the host to queue every call first, so the
+                # calls run back to back whatever the host cost
+                spin = int(2.4e3 * (2.0 * host * reps + 2000.0))  # ~2.4 GHz shader clock
+                torch.cuda._sleep(spin)
+                ev.record(ev.pairs[0][0], stream)
+                for _ in range(reps):
+                    fn()
+                ev.record(ev.pairs[0][1], stream)
+                torch.cuda.synchronize()
+                b2b = ev.elapsed_ms(0) * 1e3 / reps
+                # one call between an event pair, each pair queued behind the
+                # spin as well
+                torch.cuda._sleep(spin)
+                for i in range(reps):
+                    ev.record(ev.pairs[i][0], stream)
+                    fn()
+                    ev.record(ev.pairs[i][1], stream)
+                torch.cuda.synchronize()
+                paired = statistics.median(ev.elapsed_ms(i) * 1e3 - pair_us for i in range(reps))
+                # the same pairs with the host submitting each call after the
+                # previous one has finished (what a single call sees)
+                alone = []
+                for i in range(50):
+                    ev.record(ev.pairs[i][0], stream)
+                    fn()
+                    ev.record(ev.pairs[i][1], stream)
+                    torch.cuda.synchronize()
+                    alone.append(ev.elapsed_ms(i) * 1e3 - pair_us)
+                res[kind] = (host, b2b, paired, statistics.median(alone))
         for k in eager_out:
             assert torch.equal(eager_out[k], graph_out[k]), f"graph replay differs: {k}"
-        rows.append(f"| {wl.name}, {label} ({L} x {T}) | {statistics.median(te):.1f} | "
-                    f"{statistics.median(tg):.1f} |")
+        e, gr = res["eager"], res["graph"]
+        rows.append(f"| {wl.name}, {label} ({L} x {T}) | {e[0]:.1f} | {gr[0]:.1f} | {e[1]:.1f} | "
+                    f"{gr[1]:.1f} | {e[2]:.1f} | {gr[2]:.1f} | {e[3]:.1f} | {gr[3]:.1f} |")
         del g
     return rows
 
