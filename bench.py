@@ -141,6 +141,28 @@ def summarize_trace(d, out, command, steps=None, warmup=None):
                       f"(launches {warmup + steps}..{warmup + 2 * steps - 1}): average "
                       f"{statistics.mean(ev):.2f} us, median {statistics.median(ev):.2f} us; "
                       f"value pass: average {statistics.mean(g[warmup:warmup + steps]):.2f} us."]
+        # the route steps launch each of their kernels once per step, before
+        # any variant runs: the value pass is launches [warmup, warmup + steps)
+        # of each
+        step_rows = ["", "Per route step, value pass (launches "
+                         f"{warmup}..{warmup + steps - 1} of each kernel; the table above "
+                         "also averages the variants' launches):", "",
+                     "| kernel | avg us | median us |", "|---|---|---|"]
+        for key in ("gate_gemm", "route_rows", "route_small", "layout_scatter"):
+            k = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                 for r in tr if key in r["Kernel_Name"]][warmup:warmup + steps]
+            if k:
+                step_rows.append(f"| {key} | {statistics.mean(k):.2f} | "
+                                 f"{statistics.median(k):.2f} |")
+        # gaps: first kernel start to last kernel end of each value-pass step
+        starts = [int(r["Start_Timestamp"]) for r in tr if "gate_gemm" in r["Kernel_Name"]]
+        ends = [int(r["End_Timestamp"]) for r in tr if "layout_scatter" in r["Kernel_Name"]]
+        if len(starts) >= warmup + steps and len(ends) >= warmup + steps:
+            span = [(ends[i] - starts[i]) / 1e3 for i in range(warmup, warmup + steps)]
+            step_rows += ["", f"Gate GEMM start to layout end, per value-pass step: average "
+                              f"{statistics.mean(span):.2f} us, median "
+                              f"{statistics.median(span):.2f} us."]
+        lines += step_rows
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -163,6 +185,7 @@ STAGE_ORDER = ["tiny_softmax", "mixtral_top2", "dsv3_group", "collapse_balance",
 STAGE_WARMUP, STAGE_CALLS = 5, 20
 MARKER = "balanced_indices_kernel"  # the stage run's marker launch
 STAGES = [("gate_gemm", "gate GEMM"),
+          ("route_small", "gate GEMM + selection (one launch, at most 16 experts)"),
           ("route_rows", "selection (scores, top-k, weights, entropy, histogram)"),
           ("score_topk", "selection (scores, top-k, weights, entropy, histogram)"),
           ("layout_count", "histogram of supplied ids"),
@@ -408,7 +431,8 @@ def summarize_counters(dirs, out, command):
 
 
 # kernels of one route call of the 16k-token batch
-STEP_KERNELS = ("gate_gemm", "route_rows", "layout_scatter", "zero_ints", "route_fused")
+STEP_KERNELS = ("gate_gemm", "route_rows", "layout_scatter", "zero_ints", "route_fused",
+                "route_small")
 
 
 def summarize_traffic(fetch_dir, write_dir, out, command):

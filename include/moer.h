@@ -175,7 +175,10 @@ typedef struct {
   void* ev_gemm_end;         /* GEMM: the bf16 kernel's launch records them
                                 at its own start and end (the dispatch's
                                 timestamps); other gate kernels are
-                                bracketed by records on the stream */
+                                bracketed by records on the stream. Routers
+                                of at most 16 experts whose GEMM and
+                                selection share one launch: that launch's
+                                start and end */
   moer_load_stats_t* load_stats; /* opt [L]: what moer_load_stats gives for this
                                     call's counts (fused, no extra launch) */
   float* bias_update;        /* opt [L][N]: moer_bias_update applied in place
