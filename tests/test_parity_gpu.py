@@ -149,6 +149,7 @@ def _hidden_case(wl, seed_note, sample=None, check_h=True, bias_mode="score", bi
 
 @pytest.mark.parametrize("wl", [
     WL["tiny_softmax"],
+    workloads.scaled(WL["decode_layers"], n_layers=1),
     workloads.scaled(WL["mixtral_top2"], T=1000),
     workloads.scaled(WL["dsv3_group"], T=700),
     workloads.scaled(WL["collapse_balance"], T=300),
@@ -200,6 +201,59 @@ def test_hidden_mode_small_routers(wl, split, monkeypatch):
     _hidden_case(wl, wl.name)
     if wl.N <= 12 and wl.n_layers == 1:
         _hidden_case(wl, wl.name + " logit-space bias", bias_mode="logit")
+
+
+# Batches of fewer than 64 blocks of 64 tokens (a one-layer decode batch)
+# take 16-token selection workgroups; MOER_ROUTE_TINY=0 keeps them on the
+# 64-token workgroups. Both add the same depth-range partials in the same
+# order and route every row with the same routine, so every per-token output,
+# the counts, the layout and the load statistics must be identical bit for
+# bit. The batch-mean entropy is not: its fp32 column sums of q are added per
+# histogram block, and the blocks differ (16 or 64 tokens), so only the
+# association of the same terms differs (a few ulps; both paths are held to
+# the oracle's 1e-4 elsewhere). Shapes: the one-layer decode batch (16 depth ranges
+# from the gate GEMM's small tile), DeepSeek-V3 groups, expert counts that
+# leave a row lane partly empty (200) or are not a multiple of 4 (26, with
+# shared slots and a ragged d), a softmax router, several layers.
+TINY_BATCHES = [
+    workloads.scaled(WL["decode_layers"], n_layers=1),
+    workloads.scaled(WL["dsv3_group"], T=300),
+    workloads.scaled(WL["dsv3_group"], T=77, d=1024, N=200, n_groups=1, topk_groups=1, K=5),
+    workloads.scaled(WL["dsv3_group"], T=65, d=136, N=26, n_groups=1, topk_groups=1, K=3,
+                     n_shared=2),
+    workloads.scaled(WL["mixtral_top2"], T=1000, d=256, N=64, K=4),
+    workloads.scaled(WL["decode_layers"], n_layers=3, T=100),
+]
+
+
+def _route_tiny(wl, mode, inp, s32):
+    if mode == "hidden":
+        return moer.route(inp["x"].to(DEV), inp["W"].to(DEV), K=wl.K, score_fn=wl.score_fn,
+                          n_groups=wl.n_groups, topk_groups=wl.topk_groups,
+                          n_shared=wl.n_shared, bias=inp["bias"].to(DEV), want_h=True,
+                          want_load_stats=True)
+    return moer.route(scores=torch.from_numpy(s32).to(DEV), K=wl.K, score_fn=wl.score_fn,
+                      n_groups=wl.n_groups, topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                      bias=inp["bias"].to(DEV), want_load_stats=True)
+
+
+@pytest.mark.parametrize("mode", ["hidden", "scores"])
+@pytest.mark.parametrize("wl", TINY_BATCHES,
+                         ids=lambda w: f"{w.name}-L{w.n_layers}-T{w.T}-d{w.d}-N{w.N}-G{w.n_groups}")
+def test_small_batch_selection_matches_64_token_workgroups(wl, mode, monkeypatch):
+    say(f"[tiny] {mode} {wl}")
+    inp = workloads.make_inputs(wl)
+    logits = workloads.make_logits(wl.T, wl.N, 11, n_layers=wl.n_layers)
+    s32 = np.stack([_oracle_scores(logits[l], wl.score_fn) for l in range(wl.n_layers)])
+    small = _route_tiny(wl, mode, inp, s32)
+    monkeypatch.setenv("MOER_ROUTE_TINY", "0")
+    big = _route_tiny(wl, mode, inp, s32)
+    torch.cuda.synchronize()
+    for k in small:
+        if k == "agg_entropy":
+            assert torch.allclose(small[k], big[k], rtol=0, atol=1e-5), k
+        elif torch.is_tensor(small[k]):
+            assert torch.equal(small[k], big[k]), f"{k} differs"
 
 
 @pytest.mark.timeout(600)

@@ -245,18 +245,25 @@ hipError_t launch_tile(const void* x, const void* w, float* h, int L, int T, int
   return hipGetLastError();
 }
 
-// Tile of the pipelined kernel for a router with N experts.
-bool small_n(int N) { return N <= 32; }
+// Tile of the pipelined kernel: 64 tokens x 32 experts for small routers,
+// and for batches too small to give the 128 x 256 tile 32 work items (a
+// one-layer decode batch: its one 128 x 256 tile would leave all but a few
+// CUs idle); 128 x 256 otherwise.
+bool small_tile(int L, int T, int N) {
+  return N <= 32 || (long long)L * ((T + 127) / 128) * ((N + 255) / 256) < 32;
+}
+constexpr int kMaxSplit = 16;  // depth ranges at most
 
 }  // namespace
 
 int gate_gemm_ksplit(int dtype_bf16, int L, int T, int d, int N) {
   if (!dtype_bf16 || T == 0 || d % kKStage != 0) return 1;
-  const int bt = small_n(N) ? 64 : 128;
-  const int be = small_n(N) ? 32 : 256;
+  const bool small = small_tile(L, T, N);
+  const int bt = small ? 64 : 128;
+  const int be = small ? 32 : 256;
   const long long tiles = (long long)L * ((T + bt - 1) / bt) * ((N + be - 1) / be);
   int ks = 1;
-  while (ks < 8 && tiles * ks < 256 && d % (kKStage * ks * 2) == 0) ks *= 2;
+  while (ks < kMaxSplit && tiles * ks < 256 && d % (kKStage * ks * 2) == 0) ks *= 2;
   return ks;
 }
 
@@ -279,7 +286,7 @@ hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int 
                                  int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s,
                                  hipEvent_t ev0, hipEvent_t ev1) {
   if (d % (kKStage * ksplit) == 0) {
-    if (small_n(N))
+    if (small_tile(L, T, N))
       return launch_dma<64, 32, 4, 1, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s, ev0,
                                             ev1);
     return launch_dma<128, 256, 2, 2, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s, ev0,

@@ -54,7 +54,7 @@ moer_status check_rows(int32_t n_layers, int32_t T, int32_t Kt) {
 // Workspace regions (byte offsets) for a validated descriptor.
 struct Plan {
   int Kt, Nb, nsb, nlb, ksplit;
-  int nsb_small;  // 16-token histogram blocks of the one-launch small-router kernel (0: none)
+  int nsb_small;  // 16-token histogram blocks (small routers, small batches; 0: none)
   int nseg;
   int nsync;  // fused pass counters, stored right after the segment totals
   size_t off_h, off_colpart, off_cnt, off_seg, off_colmean, total;
@@ -74,8 +74,10 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   p.nsb = (d.T + moer::kRowTokens - 1) / moer::kRowTokens;
   p.nlb = d.T > 0 ? (d.T + moer::kLayoutTokens - 1) / moer::kLayoutTokens : 1;
   p.ksplit = hidden ? moer::gate_gemm_ksplit(d.dtype == MOER_BF16, d.n_layers, d.T, d.d, d.N) : 1;
-  // routers the one-launch small kernel may take: room for its finer blocks
-  p.nsb_small = hidden && d.N <= moer::kSmallMaxExperts
+  // routers the one-launch small kernel or the small-batch selection kernel
+  // may take: room for their 16-token blocks
+  p.nsb_small = (hidden && d.N <= moer::kSmallMaxExperts) ||
+                        moer::route_rows_tiny(d.n_layers, d.T)
                     ? (d.T + moer::kSmallTokens - 1) / moer::kSmallTokens : 0;
   const size_t nsb_room = (size_t)std::max(p.nsb, p.nsb_small);
   size_t o = 0;
@@ -162,6 +164,14 @@ int fused_mode() {
 // selection launches.
 bool small_enabled() {
   const char* v = getenv("MOER_ROUTE_SMALL");
+  return v == nullptr || strcmp(v, "0") != 0;
+}
+
+// 16-token selection workgroups for small batches (route_rows_tiny), chosen
+// by the environment variable MOER_ROUTE_TINY: on (the default) unless it is
+// "0", which keeps every batch on 64-token workgroups.
+bool tiny_enabled() {
+  const char* v = getenv("MOER_ROUTE_TINY");
   return v == nullptr || strcmp(v, "0") != 0;
 }
 
@@ -399,6 +409,16 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     return ok();
   }
 
+  // Small batches: 16-token selection workgroups, whose histogram blocks
+  // carry no segment totals (the layout sums the block counts).
+  const bool rows16 = path == 1 && !capped && tiny_enabled() && moer::route_rows_tiny(L, d.T);
+  if (rows16) {
+    a.segsum = nullptr;
+    la.segsum = nullptr;
+    la.nsb = p.nsb_small;
+    la.hist_shift = moer::kSmallShift;
+  }
+
   // segment counters start at zero: cleared by the gate GEMM when the
   // pipelined bf16 kernel or the fp32 kernel runs, else by a fill kernel
   const bool gemm_clears =
@@ -430,7 +450,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
 
   if (!indices && d.T > 0) {
     if (path == 1)
-      MOER_CHECK(moer::launch_route_rows(a, L, s));
+      MOER_CHECK(moer::launch_route_rows(a, L, s, rows16));
     else
       MOER_CHECK(moer::launch_score_topk(a, L, s));
   }

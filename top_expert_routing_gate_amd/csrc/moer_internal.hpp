@@ -78,19 +78,27 @@ hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s);
 hipError_t launch_gate_gemm_f32(const float* x, const float* w, float* h, int L, int T, int d,
                                 int N, int32_t* zero, int n_zero, hipStream_t s);
 hipError_t launch_score_topk(const ScoreArgs& a, int L, hipStream_t s);
-// Row-per-token selection (writes the block histograms itself).
+// 16-token histogram blocks (the small-batch selection kernel and the
+// one-launch small-router kernel): four per 64-token layout block.
+constexpr int kSmallTokens = 16;
+constexpr int kSmallShift = 2;  // kRowTokens / kSmallTokens = 4 blocks per layout block
+constexpr int kSmallMaxExperts = 16;
+
+// Row-per-token selection (writes the block histograms itself). rows16:
+// 16-token workgroups and histogram blocks (no segment totals: ScoreArgs and
+// LayoutArgs segsum null, LayoutArgs hist_shift = kSmallShift), for batches
+// of fewer than kTinyGrid 64-token blocks (route_rows_tiny).
+constexpr int kTinyGrid = 64;
 int route_rows_epl(int N);
 bool route_rows_supports(int N, int G);
-hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s);
+bool route_rows_tiny(int L, int T);
+hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s, bool rows16);
 // Gate GEMM and selection in one launch for at most 16 experts and 4096
 // tokens (bf16 with d a multiple of 128, or fp32 with d a multiple of 64;
 // x and W_g 16-byte aligned). Its histogram blocks are kSmallTokens tokens
 // (cnt [L][Nb][ceil(T / kSmallTokens)], colpart likewise) and carry no
 // segment totals: ScoreArgs segsum null, LayoutArgs segsum null with
 // hist_shift = kSmallShift. ev0 / ev1 (optional) bracket the launch.
-constexpr int kSmallTokens = 16;
-constexpr int kSmallShift = 2;  // kRowTokens / kSmallTokens = 4 blocks per layout block
-constexpr int kSmallMaxExperts = 16;
 bool route_small_eligible(bool bf16, int T, int d, int N, int G, bool aligned);
 hipError_t launch_route_small(const ScoreArgs& a, const void* x, const void* W, int d, bool bf16,
                               int L, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);

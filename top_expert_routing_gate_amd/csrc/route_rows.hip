@@ -16,22 +16,39 @@ constexpr int kThreads = kRowTokens * kRowLanes;  // 1024: one row per token
 template <int EPL, class S>
 __device__ __forceinline__ void load_row(const ScoreArgs& a, size_t row_off, size_t split_stride,
                                          int e0, float (&v)[EPL]) {
-  // EPL consecutive experts per lane, depth-range partials added in order;
-  // 16-byte loads when the lane's range is whole and aligned
+  // EPL consecutive experts per lane, depth-range partials added in range
+  // order; 16-byte loads when the lane's range is whole and aligned. The
+  // loads of kBatch ranges are issued before any of them is added, so a
+  // router with many ranges waits for ceil(nsplit / kBatch) round trips.
+  constexpr int kBatch = EPL >= 16 ? 2 : 4;
   const int N = S::n(a);
 #pragma unroll
   for (int j = 0; j < EPL; ++j) v[j] = 0.f;
   if (e0 >= N) return;
   if (EPL % 4 == 0 && e0 + EPL <= N && (N & 3) == 0) {
-    for (int sp = 0; sp < a.nsplit; ++sp) {
-      const float4* src = reinterpret_cast<const float4*>(a.in + sp * split_stride + row_off + e0);
+    constexpr int Q = EPL / 4;
+    for (int sp0 = 0; sp0 < a.nsplit; sp0 += kBatch) {
+      float4 q[kBatch][Q];
 #pragma unroll
-      for (int j = 0; j < EPL / 4; ++j) {
-        const float4 q = src[j];
-        if (sp == 0) {
-          v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
-        } else {
-          v[4 * j] += q.x; v[4 * j + 1] += q.y; v[4 * j + 2] += q.z; v[4 * j + 3] += q.w;
+      for (int b = 0; b < kBatch; ++b) {
+        // ranges past nsplit re-read the last one (not added)
+        const int sp = min(sp0 + b, a.nsplit - 1);
+        const float4* src = reinterpret_cast<const float4*>(a.in + sp * split_stride + row_off + e0);
+#pragma unroll
+        for (int j = 0; j < Q; ++j) q[b][j] = src[j];
+      }
+      // in range order; a range past nsplit leaves v as it is (a select,
+      // not a branch, so its load stays with the others)
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const bool first = sp0 + b == 0, in = sp0 + b < a.nsplit;
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+          const float4 w = q[b][j];
+          v[4 * j] = first ? w.x : (in ? v[4 * j] + w.x : v[4 * j]);
+          v[4 * j + 1] = first ? w.y : (in ? v[4 * j + 1] + w.y : v[4 * j + 1]);
+          v[4 * j + 2] = first ? w.z : (in ? v[4 * j + 2] + w.z : v[4 * j + 2]);
+          v[4 * j + 3] = first ? w.w : (in ? v[4 * j + 3] + w.w : v[4 * j + 3]);
         }
       }
     }
@@ -90,6 +107,91 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   block_outputs<EPL, kThreads>(a, layer, N, Nb, q, hist, colw);
 }
 
+// Small batches (few 64-token blocks): 16 tokens per workgroup, so that a
+// batch of a few hundred tokens still spreads over many CUs. All 1024
+// threads first add the depth-range partials of the workgroup's 16 tokens
+// into LDS, one 4-expert group of one token each, with the loads of up to
+// eight ranges in flight at once and the ranges added in order (the sums are
+// bit for bit those of load_row); wavefronts 0-3 then route the 16 rows from
+// LDS. The histogram blocks are 16 tokens and carry no segment totals (the
+// layout kernel sums the block counts).
+template <int EPL, bool GROUPED, int MODE, int LPG, class S>
+__global__ __launch_bounds__(kThreads) void route_rows16_kernel(ScoreArgs a) {
+  constexpr int kTok = kSmallTokens;
+  constexpr int kWidth = kRowLanes * EPL;  // experts per row, N rounded up
+  constexpr int kGroups = kWidth / 4;      // 4-expert groups per row
+  constexpr int kBatch = 8;
+  static_assert(kWidth % 4 == 0, "whole 4-expert groups");
+  __shared__ Cand cand[kTok][kCandStride];
+  __shared__ int slot_id[kTok][kMaxSlots];
+  __shared__ float slot_s[kTok][kMaxSlots];
+  __shared__ int hist[kMaxBuckets];
+  constexpr int kWaves = kThreads / kWave;
+  __shared__ __attribute__((aligned(16))) float colw[kWaves][kWidth];
+  __shared__ __attribute__((aligned(16))) float hs[kTok][kWidth];
+
+  const int N = S::n(a), T = a.T;
+  const int Nb = N + S::ns(a);
+  const int layer = blockIdx.y;
+  const int rl = threadIdx.x & 15;
+  const int row = threadIdx.x >> 4;
+  const int t0 = blockIdx.x * kTok;
+
+  for (int i = threadIdx.x; i < Nb; i += kThreads) hist[i] = 0;
+  LaneConsts<EPL> lc;
+  if (row < kTok) load_lane_consts<EPL, S>(a, layer, MODE != kGiven, lc);
+  const size_t split_stride = (size_t)gridDim.y * T * N;
+  for (int i = threadIdx.x; i < kTok * kGroups; i += kThreads) {
+    const int r = i / kGroups, e = 4 * (i - r * kGroups);
+    const size_t off = ((size_t)layer * T + min(t0 + r, T - 1)) * N + e;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (e < N) {
+      for (int sp0 = 0; sp0 < a.nsplit; sp0 += kBatch) {
+        float q[kBatch][4];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const float* src = a.in + (size_t)min(sp0 + b, a.nsplit - 1) * split_stride + off;
+          if ((N & 3) == 0) {
+            const float4 f = *reinterpret_cast<const float4*>(src);
+            q[b][0] = f.x; q[b][1] = f.y; q[b][2] = f.z; q[b][3] = f.w;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[b][k] = e + k < N ? src[min(k, N - 1 - e)] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const bool first = sp0 + b == 0, in = sp0 + b < a.nsplit;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[k] = first ? q[b][k] : (in ? acc[k] + q[b][k] : acc[k]);
+        }
+      }
+    }
+    *reinterpret_cast<float4*>(&hs[r][e]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  }
+  __syncthreads();  // partial sums in LDS; histogram cleared
+
+  float q[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) q[j] = 0.f;
+  if (row < kTok) {  // wavefronts 0-3: one row per token
+    float v[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) v[j] = hs[row][rl * EPL + j];
+    const int t = t0 + row;
+    const RowLds rs{cand[row], slot_id[row], slot_s[row]};
+    route_row<EPL, GROUPED, MODE, LPG, S>(a, layer, t, t < T, v, lc, rs, hist, q);
+  }
+  block_outputs<EPL, kThreads>(a, layer, N, Nb, q, hist, colw);
+}
+
+template <int EPL, bool GROUPED>
+auto pick_kernel16(const ScoreArgs& a) {
+  if (!a.apply_score) return route_rows16_kernel<EPL, GROUPED, kGiven, 0, AnyShape>;
+  if (a.score_fn == 1) return route_rows16_kernel<EPL, GROUPED, kSigmoid, 0, AnyShape>;
+  return route_rows16_kernel<EPL, GROUPED, kSoftmax, 0, AnyShape>;
+}
+
 template <int EPL, bool GROUPED, int LPG = 0, class S = AnyShape>
 auto pick_kernel(const ScoreArgs& a) {
   if (!a.apply_score) return route_rows_kernel<EPL, GROUPED, kGiven, LPG, S>;
@@ -104,7 +206,13 @@ using DeepSeekV3Shape = RowShape<256, 8, 8, 4, 0>;
 using DecodeShape = RowShape<256, 8, 1, 1, 1>;
 
 template <int EPL>
-hipError_t launch_epl(const ScoreArgs& a, int L, hipStream_t s) {
+hipError_t launch_epl(const ScoreArgs& a, int L, bool rows16, hipStream_t s) {
+  if (rows16) {
+    const dim3 grid16((a.T + kSmallTokens - 1) / kSmallTokens, L);
+    auto k16 = a.G > 1 ? pick_kernel16<EPL, true>(a) : pick_kernel16<EPL, false>(a);
+    hipLaunchKernelGGL(k16, grid16, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((a.T + kRowTokens - 1) / kRowTokens, L);
   // the DeepSeek-V3 geometry (groups of 32 experts, 2 row lanes per group)
   // gets a kernel with the group width fixed at compile time
@@ -136,13 +244,17 @@ bool route_rows_supports(int N, int G) {
   return lpg >= 1 && lpg <= kRowLanes && (lpg & (lpg - 1)) == 0;
 }
 
-hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s) {
+bool route_rows_tiny(int L, int T) {
+  return T > 0 && (long long)L * ((T + kRowTokens - 1) / kRowTokens) < kTinyGrid;
+}
+
+hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s, bool rows16) {
   switch (route_rows_epl(a.N)) {
-    case 1: return launch_epl<1>(a, L, s);
-    case 2: return launch_epl<2>(a, L, s);
-    case 4: return launch_epl<4>(a, L, s);
-    case 8: return launch_epl<8>(a, L, s);
-    default: return launch_epl<16>(a, L, s);
+    case 1: return launch_epl<1>(a, L, rows16, s);
+    case 2: return launch_epl<2>(a, L, rows16, s);
+    case 4: return launch_epl<4>(a, L, rows16, s);
+    case 8: return launch_epl<8>(a, L, rows16, s);
+    default: return launch_epl<16>(a, L, rows16, s);
   }
 }
 
