@@ -54,7 +54,7 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   const int lane = threadIdx.x % kWave;
   const bool worker = threadIdx.x < kBalanceThreads;
   const int e_first = worker ? (int)threadIdx.x : N;
-  // round 1: total, and the largest count with the lowest expert id on ties
+  // first pass: total, and the largest count with the lowest expert id on ties
   // (packed as order-preserving count bits << 32 | ~id, so one unsigned max
   // decides both)
   long long tot = 0;
@@ -90,7 +90,7 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   }
   if (out == nullptr) return;
 
-  // round 2: entropy of the load distribution and the sum of squared deviations
+  // second pass: entropy of the load distribution and the sum of squared deviations
   const double mean = (double)tot / (double)N;
   double hpart = 0.0, vpart = 0.0;
   for (int e = e_first; e < N; e += kBalanceThreads) {
