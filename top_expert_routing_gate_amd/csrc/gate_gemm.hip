@@ -253,6 +253,13 @@ bool small_tile(int L, int T, int N) {
   return N <= 32 || (long long)L * ((T + 127) / 128) * ((N + 255) / 256) < 32;
 }
 constexpr int kMaxSplit = 16;  // depth ranges at most
+// 128 x 128 for large routers whose batch gives the 128 x 256 tile fewer
+// than 128 work items (the 64-layer decode batch): twice the tiles, so half
+// the depth ranges, and half the partial affinities written and read back.
+bool mid_tile(int L, int T, int N) {
+  return !small_tile(L, T, N) && N > 128 &&
+         (long long)L * ((T + 127) / 128) * ((N + 255) / 256) < 128;
+}
 
 }  // namespace
 
@@ -260,7 +267,7 @@ int gate_gemm_ksplit(int dtype_bf16, int L, int T, int d, int N) {
   if (!dtype_bf16 || T == 0 || d % kKStage != 0) return 1;
   const bool small = small_tile(L, T, N);
   const int bt = small ? 64 : 128;
-  const int be = small ? 32 : 256;
+  const int be = small ? 32 : (mid_tile(L, T, N) ? 128 : 256);
   const long long tiles = (long long)L * ((T + bt - 1) / bt) * ((N + be - 1) / be);
   int ks = 1;
   while (ks < kMaxSplit && tiles * ks < 256 && d % (kKStage * ks * 2) == 0) ks *= 2;
@@ -286,6 +293,9 @@ hipError_t launch_gate_gemm_bf16(const void* x, const void* w, float* part, int 
                                  int N, int ksplit, int32_t* zero, int n_zero, hipStream_t s,
                                  hipEvent_t ev0, hipEvent_t ev1) {
   if (d % (kKStage * ksplit) == 0) {
+    if (mid_tile(L, T, N))
+      return launch_dma<128, 128, 2, 2, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s, ev0,
+                                              ev1);
     if (small_tile(L, T, N))
       return launch_dma<64, 32, 4, 1, 4, 3>(x, w, part, L, T, d, N, ksplit, zero, n_zero, s, ev0,
                                             ev1);
