@@ -253,11 +253,13 @@ bool small_tile(int L, int T, int N) {
   return N <= 32 || (long long)L * ((T + 127) / 128) * ((N + 255) / 256) < 32;
 }
 constexpr int kMaxSplit = 16;  // depth ranges at most
-// 128 x 128 for large routers whose batch gives the 128 x 256 tile fewer
-// than 128 work items (the 64-layer decode batch): twice the tiles, so half
-// the depth ranges, and half the partial affinities written and read back.
+// 128 x 128 for large routers with decode-sized layers (at most two
+// 128-token tiles per layer, so W_g streams from HBM rather than being
+// re-read from L2) whose batch gives the 128 x 256 tile fewer than 128 work
+// items (the 64-layer decode batch): twice the tiles, so half the depth
+// ranges, and half the partial affinities written and read back.
 bool mid_tile(int L, int T, int N) {
-  return !small_tile(L, T, N) && N > 128 &&
+  return !small_tile(L, T, N) && N > 128 && (T + 127) / 128 <= 2 &&
          (long long)L * ((T + 127) / 128) * ((N + 255) / 256) < 128;
 }
 
