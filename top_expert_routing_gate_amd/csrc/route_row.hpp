@@ -345,15 +345,20 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     if (lpg >= 4) merge(dpp_f<kXor2>(m1), dpp_f<kXor2>(m2));
     if (lpg >= 8) merge(dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
     if (lpg >= 16) merge(dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
-    const float gs = (g < G) ? m1 + m2 : NEG_INF;
-    const int gid = g < G ? g : 0x7FFF;
-    // rank among the row's groups: rotate (score, id) by whole groups
+    // the group as one orderable word: score order bits, then the inverted
+    // group id, so one unsigned compare orders (score desc, id asc); lanes
+    // past the last group hold 0 and beat no group. (A NaN group score sorts
+    // above +inf.)
+    const unsigned ghi = g < G ? order_bits(m1 + m2, false) : 0u;
+    const unsigned glo = g < G ? (unsigned)(0xFFFF - g) : 0u;
+    const unsigned long long gkey = ((unsigned long long)ghi << 32) | glo;
+    // rank among the row's groups: rotate the words by whole groups
     int rank = 0;
 #define MOER_ROT(n)                                                                  \
     if ((n) % lpg == 0) {                                                            \
-      const float og = dpp_f<0x120 + (n)>(gs);                                       \
-      const int oid = dpp_i<0x120 + (n)>(gid);                                       \
-      rank += (oid < G && (og > gs || (og == gs && oid < gid))) ? 1 : 0;             \
+      const unsigned oh = (unsigned)dpp_i<0x120 + (n)>((int)ghi);                    \
+      const unsigned ol = (unsigned)dpp_i<0x120 + (n)>((int)glo);                    \
+      rank += ((((unsigned long long)oh << 32) | ol) > gkey) ? 1 : 0;                \
     }
     MOER_ROT(1) MOER_ROT(2) MOER_ROT(3) MOER_ROT(4) MOER_ROT(5) MOER_ROT(6) MOER_ROT(7)
     MOER_ROT(8) MOER_ROT(9) MOER_ROT(10) MOER_ROT(11) MOER_ROT(12) MOER_ROT(13) MOER_ROT(14)

@@ -27,6 +27,23 @@ __device__ __forceinline__ void load_row(const ScoreArgs& a, size_t row_off, siz
   if (e0 >= N) return;
   if (EPL % 4 == 0 && e0 + EPL <= N && (N & 3) == 0) {
     constexpr int Q = EPL / 4;
+    if constexpr (Q > 0) {
+      if (a.nsplit == 2) {  // the common split, without the tail selects
+        float4 q0[Q], q1[Q];
+        const float4* s0 = reinterpret_cast<const float4*>(a.in + row_off + e0);
+        const float4* s1 = reinterpret_cast<const float4*>(a.in + split_stride + row_off + e0);
+#pragma unroll
+        for (int j = 0; j < Q; ++j) q0[j] = s0[j];
+#pragma unroll
+        for (int j = 0; j < Q; ++j) q1[j] = s1[j];
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+          v[4 * j] = q0[j].x + q1[j].x; v[4 * j + 1] = q0[j].y + q1[j].y;
+          v[4 * j + 2] = q0[j].z + q1[j].z; v[4 * j + 3] = q0[j].w + q1[j].w;
+        }
+        return;
+      }
+    }
     for (int sp0 = 0; sp0 < a.nsplit; sp0 += kBatch) {
       float4 q[kBatch][Q];
 #pragma unroll
