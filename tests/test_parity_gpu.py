@@ -204,18 +204,23 @@ def test_hidden_mode_small_routers(wl, split, monkeypatch):
 
 
 # Batches of fewer than 64 blocks of 64 tokens (a one-layer decode batch)
-# take 16-token selection workgroups; MOER_ROUTE_TINY=0 keeps them on the
-# 64-token workgroups. Both add the same depth-range partials in the same
-# order and route every row with the same routine, so every per-token output,
-# the counts, the layout and the load statistics must be identical bit for
-# bit. The batch-mean entropy is not: its fp32 column sums of q are added per
-# histogram block, and the blocks differ (16 or 64 tokens), so only the
-# association of the same terms differs (a few ulps; both paths are held to
-# the oracle's 1e-4 elsewhere). Shapes: the one-layer decode batch (16 depth ranges
-# from the gate GEMM's small tile), DeepSeek-V3 groups, expert counts that
-# leave a row lane partly empty (200) or are not a multiple of 4 (26, with
-# shared slots and a ragged d), a softmax router, several layers.
+# take 16-token selection workgroups, batches of 64 to 255 blocks (the
+# 64-layer decode batch, 8192 tokens) 32-token ones; MOER_ROUTE_TINY=0
+# keeps them on the 64-token workgroups. Both add the same depth-range
+# partials in the same order and route every row with the same routine, so
+# every per-token output, the counts, the layout and the load statistics
+# must be identical bit for bit. The batch-mean entropy is not: its fp32
+# column sums of q are added per histogram block, and the blocks differ
+# (16, 32 or 64 tokens), so only the association of the same terms differs
+# (a few ulps; both paths are held to the oracle's 1e-4 elsewhere). Shapes:
+# the 64-layer decode batch and an 8192-token DeepSeek-V3 batch (32-token
+# workgroups), the one-layer decode batch (16 depth ranges from the gate
+# GEMM's small tile), DeepSeek-V3 groups, expert counts that leave a row
+# lane partly empty (200) or are not a multiple of 4 (26, with shared slots
+# and a ragged d), a softmax router, several layers.
 TINY_BATCHES = [
+    WL["decode_layers"],
+    workloads.scaled(WL["dsv3_group"], T=8192, d=1024),
     workloads.scaled(WL["decode_layers"], n_layers=1),
     workloads.scaled(WL["dsv3_group"], T=300),
     workloads.scaled(WL["dsv3_group"], T=77, d=1024, N=200, n_groups=1, topk_groups=1, K=5),

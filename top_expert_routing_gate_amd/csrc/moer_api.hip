@@ -74,10 +74,10 @@ Plan make_plan(const moer_route_desc& d, bool hidden, bool want_agg) {
   p.nsb = (d.T + moer::kRowTokens - 1) / moer::kRowTokens;
   p.nlb = d.T > 0 ? (d.T + moer::kLayoutTokens - 1) / moer::kLayoutTokens : 1;
   p.ksplit = hidden ? moer::gate_gemm_ksplit(d.dtype == MOER_BF16, d.n_layers, d.T, d.d, d.N) : 1;
-  // routers the one-launch small kernel or the small-batch selection kernel
-  // may take: room for their 16-token blocks
+  // routers the one-launch small kernel or the few-token selection kernel may
+  // take: room for their blocks of 16 (or 32) tokens
   p.nsb_small = (hidden && d.N <= moer::kSmallMaxExperts) ||
-                        moer::route_rows_tiny(d.n_layers, d.T)
+                        moer::route_rows_tokens(d.n_layers, d.T) < moer::kRowTokens
                     ? (d.T + moer::kSmallTokens - 1) / moer::kSmallTokens : 0;
   const size_t nsb_room = (size_t)std::max(p.nsb, p.nsb_small);
   size_t o = 0;
@@ -167,9 +167,10 @@ bool small_enabled() {
   return v == nullptr || strcmp(v, "0") != 0;
 }
 
-// 16-token selection workgroups for small batches (route_rows_tiny), chosen
-// by the environment variable MOER_ROUTE_TINY: on (the default) unless it is
-// "0", which keeps every batch on 64-token workgroups.
+// 16- or 32-token selection workgroups for small batches
+// (route_rows_tokens), chosen by the environment variable MOER_ROUTE_TINY:
+// on (the default) unless it is "0", which keeps every batch on 64-token
+// workgroups.
 bool tiny_enabled() {
   const char* v = getenv("MOER_ROUTE_TINY");
   return v == nullptr || strcmp(v, "0") != 0;
@@ -409,14 +410,15 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     return ok();
   }
 
-  // Small batches: 16-token selection workgroups, whose histogram blocks
-  // carry no segment totals (the layout sums the block counts).
-  const bool rows16 = path == 1 && !capped && tiny_enabled() && moer::route_rows_tiny(L, d.T);
-  if (rows16) {
+  // Small batches: 16- or 32-token selection workgroups, whose histogram
+  // blocks carry no segment totals (the layout sums the block counts).
+  int rows = moer::kRowTokens;
+  if (path == 1 && !capped && tiny_enabled()) rows = moer::route_rows_tokens(L, d.T);
+  if (rows < moer::kRowTokens) {
     a.segsum = nullptr;
     la.segsum = nullptr;
-    la.nsb = p.nsb_small;
-    la.hist_shift = moer::kSmallShift;
+    la.nsb = (d.T + rows - 1) / rows;
+    la.hist_shift = rows == moer::kSmallTokens ? moer::kSmallShift : 1;
   }
 
   // segment counters start at zero: cleared by the gate GEMM when the
@@ -450,7 +452,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
 
   if (!indices && d.T > 0) {
     if (path == 1)
-      MOER_CHECK(moer::launch_route_rows(a, L, s, rows16));
+      MOER_CHECK(moer::launch_route_rows(a, L, s, rows));
     else
       MOER_CHECK(moer::launch_score_topk(a, L, s));
   }

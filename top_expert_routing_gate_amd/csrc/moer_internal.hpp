@@ -84,15 +84,17 @@ constexpr int kSmallTokens = 16;
 constexpr int kSmallShift = 2;  // kRowTokens / kSmallTokens = 4 blocks per layout block
 constexpr int kSmallMaxExperts = 16;
 
-// Row-per-token selection (writes the block histograms itself). rows16:
-// 16-token workgroups and histogram blocks (no segment totals: ScoreArgs and
-// LayoutArgs segsum null, LayoutArgs hist_shift = kSmallShift), for batches
-// of fewer than kTinyGrid 64-token blocks (route_rows_tiny).
+// Row-per-token selection (writes the block histograms itself). rows: the
+// tokens per workgroup and histogram block, route_rows_tokens(L, T): 64, or
+// 16 / 32 for batches of fewer than kTinyGrid / kFewGrid 64-token blocks;
+// blocks of 16 or 32 tokens carry no segment totals (ScoreArgs and LayoutArgs
+// segsum null, LayoutArgs hist_shift = log2(64 / rows)).
 constexpr int kTinyGrid = 64;
+constexpr int kFewGrid = 256;
 int route_rows_epl(int N);
 bool route_rows_supports(int N, int G);
-bool route_rows_tiny(int L, int T);
-hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s, bool rows16);
+int route_rows_tokens(int L, int T);
+hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s, int rows);
 // Gate GEMM and selection in one launch for at most 16 experts and 4096
 // tokens (bf16 with d a multiple of 128, or fp32 with d a multiple of 64;
 // x and W_g 16-byte aligned). Its histogram blocks are kSmallTokens tokens

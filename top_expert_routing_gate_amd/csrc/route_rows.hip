@@ -124,17 +124,19 @@ __global__ __launch_bounds__(kThreads) void route_rows_kernel(ScoreArgs a) {
   block_outputs<EPL, kThreads>(a, layer, N, Nb, q, hist, colw);
 }
 
-// Small batches (few 64-token blocks): 16 tokens per workgroup, so that a
-// batch of a few hundred tokens still spreads over many CUs. All 1024
-// threads first add the depth-range partials of the workgroup's 16 tokens
-// into LDS, one 4-expert group of one token each, with the loads of up to
-// eight ranges in flight at once and the ranges added in order (the sums are
-// bit for bit those of load_row); wavefronts 0-3 then route the 16 rows from
-// LDS. The histogram blocks are 16 tokens and carry no segment totals (the
-// layout kernel sums the block counts).
-template <int EPL, bool GROUPED, int MODE, int LPG, class S>
-__global__ __launch_bounds__(kThreads) void route_rows16_kernel(ScoreArgs a) {
-  constexpr int kTok = kSmallTokens;
+// Small and mid-sized batches (fewer than 256 blocks of 64 tokens, so fewer
+// 64-token workgroups than CUs): TOK = 16 or 32 tokens per workgroup, so the
+// batch spreads over more CUs. All 1024 threads first add the depth-range
+// partials of the workgroup's tokens into LDS, one 4-expert group of one
+// token each, with the loads of up to eight ranges in flight at once and the
+// ranges added in order (the sums are bit for bit those of load_row); the
+// first TOK rows (TOK / 4 wavefronts) then route from LDS. The histogram
+// blocks are TOK tokens and carry no segment totals (the layout kernel sums
+// the block counts).
+template <int EPL, bool GROUPED, int MODE, int LPG, class S, int TOK>
+__global__ __launch_bounds__(kThreads) void route_rows_few_kernel(ScoreArgs a) {
+  constexpr int kTok = TOK;
+  static_assert(TOK == 16 || TOK == 32, "16 or 32 tokens per workgroup");
   constexpr int kWidth = kRowLanes * EPL;  // experts per row, N rounded up
   constexpr int kGroups = kWidth / 4;      // 4-expert groups per row
   constexpr int kBatch = 8;
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void route_rows16_kernel(ScoreArgs a) {
   float q[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) q[j] = 0.f;
-  if (row < kTok) {  // wavefronts 0-3: one row per token
+  if (row < kTok) {  // the first kTok / 4 wavefronts: one row per token
     float v[EPL];
 #pragma unroll
     for (int j = 0; j < EPL; ++j) v[j] = hs[row][rl * EPL + j];
@@ -202,11 +204,11 @@ __global__ __launch_bounds__(kThreads) void route_rows16_kernel(ScoreArgs a) {
   block_outputs<EPL, kThreads>(a, layer, N, Nb, q, hist, colw);
 }
 
-template <int EPL, bool GROUPED>
-auto pick_kernel16(const ScoreArgs& a) {
-  if (!a.apply_score) return route_rows16_kernel<EPL, GROUPED, kGiven, 0, AnyShape>;
-  if (a.score_fn == 1) return route_rows16_kernel<EPL, GROUPED, kSigmoid, 0, AnyShape>;
-  return route_rows16_kernel<EPL, GROUPED, kSoftmax, 0, AnyShape>;
+template <int EPL, bool GROUPED, int TOK>
+auto pick_kernel_few(const ScoreArgs& a) {
+  if (!a.apply_score) return route_rows_few_kernel<EPL, GROUPED, kGiven, 0, AnyShape, TOK>;
+  if (a.score_fn == 1) return route_rows_few_kernel<EPL, GROUPED, kSigmoid, 0, AnyShape, TOK>;
+  return route_rows_few_kernel<EPL, GROUPED, kSoftmax, 0, AnyShape, TOK>;
 }
 
 template <int EPL, bool GROUPED, int LPG = 0, class S = AnyShape>
@@ -223,11 +225,13 @@ using DeepSeekV3Shape = RowShape<256, 8, 8, 4, 0>;
 using DecodeShape = RowShape<256, 8, 1, 1, 1>;
 
 template <int EPL>
-hipError_t launch_epl(const ScoreArgs& a, int L, bool rows16, hipStream_t s) {
-  if (rows16) {
-    const dim3 grid16((a.T + kSmallTokens - 1) / kSmallTokens, L);
-    auto k16 = a.G > 1 ? pick_kernel16<EPL, true>(a) : pick_kernel16<EPL, false>(a);
-    hipLaunchKernelGGL(k16, grid16, dim3(kThreads), 0, s, a);
+hipError_t launch_epl(const ScoreArgs& a, int L, int rows, hipStream_t s) {
+  if (rows == 16 || rows == 32) {
+    const dim3 grid_few((a.T + rows - 1) / rows, L);
+    auto kf = rows == 16
+                  ? (a.G > 1 ? pick_kernel_few<EPL, true, 16>(a) : pick_kernel_few<EPL, false, 16>(a))
+                  : (a.G > 1 ? pick_kernel_few<EPL, true, 32>(a) : pick_kernel_few<EPL, false, 32>(a));
+    hipLaunchKernelGGL(kf, grid_few, dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid((a.T + kRowTokens - 1) / kRowTokens, L);
@@ -261,17 +265,18 @@ bool route_rows_supports(int N, int G) {
   return lpg >= 1 && lpg <= kRowLanes && (lpg & (lpg - 1)) == 0;
 }
 
-bool route_rows_tiny(int L, int T) {
-  return T > 0 && (long long)L * ((T + kRowTokens - 1) / kRowTokens) < kTinyGrid;
+int route_rows_tokens(int L, int T) {
+  const long long blocks = T > 0 ? (long long)L * ((T + kRowTokens - 1) / kRowTokens) : kFewGrid;
+  return blocks < kTinyGrid ? 16 : blocks < kFewGrid ? 32 : kRowTokens;
 }
 
-hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s, bool rows16) {
+hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s, int rows) {
   switch (route_rows_epl(a.N)) {
-    case 1: return launch_epl<1>(a, L, rows16, s);
-    case 2: return launch_epl<2>(a, L, rows16, s);
-    case 4: return launch_epl<4>(a, L, rows16, s);
-    case 8: return launch_epl<8>(a, L, rows16, s);
-    default: return launch_epl<16>(a, L, rows16, s);
+    case 1: return launch_epl<1>(a, L, rows, s);
+    case 2: return launch_epl<2>(a, L, rows, s);
+    case 4: return launch_epl<4>(a, L, rows, s);
+    case 8: return launch_epl<8>(a, L, rows, s);
+    default: return launch_epl<16>(a, L, rows, s);
   }
 }
 
