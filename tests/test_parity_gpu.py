@@ -217,7 +217,8 @@ def test_hidden_mode_small_routers(wl, split, monkeypatch):
 # workgroups), the one-layer decode batch (16 depth ranges from the gate
 # GEMM's small tile), DeepSeek-V3 groups, expert counts that leave a row
 # lane partly empty (200) or are not a multiple of 4 (26, with shared slots
-# and a ragged d), a softmax router, several layers.
+# and a ragged d), a softmax router, several layers, one token, one-lane
+# groups (16 groups of 16), three experts.
 TINY_BATCHES = [
     WL["decode_layers"],
     workloads.scaled(WL["dsv3_group"], T=8192, d=1024),
@@ -228,6 +229,9 @@ TINY_BATCHES = [
                      n_shared=2),
     workloads.scaled(WL["mixtral_top2"], T=1000, d=256, N=64, K=4),
     workloads.scaled(WL["decode_layers"], n_layers=3, T=100),
+    workloads.scaled(WL["dsv3_group"], T=1, d=128),
+    workloads.scaled(WL["dsv3_group"], T=130, d=256, n_groups=16, topk_groups=4),
+    workloads.scaled(WL["mixtral_top2"], T=5, d=128, N=3, K=3),
 ]
 
 

@@ -63,7 +63,6 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
   constexpr int kQuads = kMaxExperts / 4;        // 64 expert quads
   constexpr int kGroups = kThreads / kQuads;     // 4 row groups
   __shared__ float4 part[kGroups][kQuads];
-  __shared__ float red[kThreads];
   const int qd = threadIdx.x % kQuads;
   const int rg = threadIdx.x / kQuads;
   const float* cp = a.colpart + (size_t)layer * a.nsb * a.N;
@@ -101,38 +100,26 @@ __device__ void batch_mean_entropy(const LayoutArgs& a, int layer) {
   }
   part[rg][qd] = acc;
   __syncthreads();
-  float me[4] = {0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-  if (rg == 0) {
-    float4 tot = part[0][qd];
-    for (int g = 1; g < kGroups; ++g) {
-      tot.x += part[g][qd].x; tot.y += part[g][qd].y;
-      tot.z += part[g][qd].z; tot.w += part[g][qd].w;
-    }
-    const float invT = a.T > 0 ? 1.f / (float)a.T : 0.f;
-    me[0] = tot.x * invT; me[1] = tot.y * invT; me[2] = tot.z * invT; me[3] = tot.w * invT;
-    z = me[0] + me[1] + me[2] + me[3];
+  // the row groups' sums in group order, then the rest in wavefront 0 alone
+  // (lane = expert quad): sums over its 64 lanes by xor butterflies
+  // (wave_allreduce), which leave the same value in every lane
+  if (rg != 0) return;
+  float4 tot = part[0][qd];
+  for (int g = 1; g < kGroups; ++g) {
+    tot.x += part[g][qd].x; tot.y += part[g][qd].y;
+    tot.z += part[g][qd].z; tot.w += part[g][qd].w;
   }
-  red[threadIdx.x] = z;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  const float Z = red[0];
-  __syncthreads();
+  const float invT = a.T > 0 ? 1.f / (float)a.T : 0.f;
+  const float me[4] = {tot.x * invT, tot.y * invT, tot.z * invT, tot.w * invT};
+  auto add = [](float x, float y) { return x + y; };
+  const float Z = wave_allreduce(me[0] + me[1] + me[2] + me[3], add);
   float hpart = 0.f;
   for (int k = 0; k < 4; ++k) {
     const float q = Z > 0.f ? me[k] / Z : 0.f;
     hpart -= q > 0.f ? q * log2f(q) : 0.f;
   }
-  red[threadIdx.x] = hpart;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) a.agg_entropy[layer] = a.T > 0 ? red[0] : 0.f;
+  const float H = wave_allreduce(hpart, add);
+  if (threadIdx.x == 0) a.agg_entropy[layer] = a.T > 0 ? H : 0.f;
 }
 
 // Load statistics and the sign-step bias update of this call's routed counts
