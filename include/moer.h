@@ -228,7 +228,16 @@ size_t moer_route_workspace_bytes(const moer_route_desc* desc);
  * Workspace: device memory of at least moer_route_workspace_bytes(desc)
  * bytes, any contents; it is clobbered. Returns MOER_OK or an error status
  * (MOER_EINVAL also for a pointer below 16-byte alignment where the field
- * above asks for it). */
+ * above asks for it).
+ * Kernel choice (results are the same up to the rounding of h, bit for bit
+ * where only the selection kernel differs); environment variables, read at
+ * every call, override it for testing and profiling:
+ *   MOER_ROUTE_SMALL=0  routers of at most 16 experts use the separate gate
+ *                       GEMM and selection launches instead of one launch;
+ *   MOER_ROUTE_TINY=0   batches of fewer than 256 blocks of 64 tokens use
+ *                       64-token selection workgroups instead of 16 or 32;
+ *   MOER_ROUTE_FUSED=1|2|3  the co-resident fused pass for the large bf16
+ *                       routers it takes (off by default: slower here). */
 moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io,
                        void* workspace, size_t workspace_bytes, void* stream);
 
