@@ -167,6 +167,16 @@ bool small_enabled() {
   return v == nullptr || strcmp(v, "0") != 0;
 }
 
+// One workgroup per layer that also writes the layout outputs, for layers of
+// at most moer::kWholeTokens tokens and a short depth on the one-launch
+// small-router kernel (moer::route_layer_eligible),
+// chosen by the environment variable MOER_ROUTE_WHOLE: on (the default)
+// unless it is "0", which keeps the layout launch.
+bool whole_enabled() {
+  const char* v = getenv("MOER_ROUTE_WHOLE");
+  return v == nullptr || strcmp(v, "0") != 0;
+}
+
 // 16- or 32-token selection workgroups for small batches
 // (route_rows_tokens), chosen by the environment variable MOER_ROUTE_TINY:
 // on (the default) unless it is "0", which keeps every batch on 64-token
@@ -403,10 +413,14 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     la.segsum = nullptr;
     la.nsb = p.nsb_small;
     la.hist_shift = moer::kSmallShift;
+    // a layer of at most kWholeTokens tokens: one workgroup does the layout too
+    const bool whole =
+        moer::route_layer_eligible(d.dtype == MOER_BF16, d.T, d.d) && whole_enabled();
     MOER_CHECK(moer::launch_route_small(a, io->x, io->w_gate, d.d, d.dtype == MOER_BF16, L, s,
                                         static_cast<hipEvent_t>(io->ev_gemm_begin),
-                                        static_cast<hipEvent_t>(io->ev_gemm_end)));
-    MOER_CHECK(moer::launch_layout(la, L, s));
+                                        static_cast<hipEvent_t>(io->ev_gemm_end),
+                                        whole ? &la : nullptr));
+    if (!whole) MOER_CHECK(moer::launch_layout(la, L, s));
     return ok();
   }
 

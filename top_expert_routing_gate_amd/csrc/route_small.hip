@@ -28,9 +28,17 @@
 // few-thousand-token batches these routers see). Its histogram blocks are
 // therefore 16 tokens and carry no running segment totals: the layout kernel
 // sums the block counts itself, so no counter needs clearing first.
+//
+// A layer of at most kWholeTokens tokens takes one workgroup for the whole
+// call (route_layer_kernel): it routes all its tokens at once, and with the
+// whole layer's histogram in its own LDS it then does the layout kernel's
+// work as well (counts, offsets, the stable permutation and its inverse, the
+// entropy of the batch mean of q, the load statistics and the bias update),
+// so the call is one launch.
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include "load_balance.hpp"
 #include "route_row.hpp"
 
 namespace moer {
@@ -157,6 +165,175 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(ScoreArgs a, cons
   block_outputs<1, kThreads>(a, layer, N, Nb, q, hist, colw);
 }
 
+constexpr int kMaxBucketsSmall = 2 * kSmallMaxN;  // N <= 16 plus at most 15 shared slots
+constexpr int kWholeChunks = kWholeTokens * kMaxSlots / 64;  // 64-slot chunks of a layer
+
+// The layout of a layer routed by one workgroup (route_layer_kernel), from
+// its LDS histogram and chosen slots (hist, slot_id: complete after the
+// caller's barrier); qsum: this thread's q. The same outputs as the layout
+// kernel (layout.hip, layout_block.hpp, load_balance.hpp), computed the same
+// way:
+//  - counts = the histogram; offsets = its exclusive prefix;
+//  - perm / inv_perm: the stable order by (expert, token, slot), slot i of
+//    the layer at offset[e] + the earlier slots of expert e, counted with
+//    per-64-slot membership bitmaps (popcounts of the lower bits);
+//  - the entropy of the batch mean of q: column sums of q per wavefront by
+//    lane swaps, the wavefronts added in order, then the entropy in
+//    wavefront 0 with xor butterflies;
+//  - load statistics and the sign-step bias update (block_load_balance).
+__device__ void whole_layer_layout(const ScoreArgs& a, const LayoutArgs& la, int layer,
+                                   float qsum, const int* hist,
+                                   const int (*slot_id)[kMaxSlots]) {
+  __shared__ unsigned long long bits[kWholeChunks][kMaxBucketsSmall];
+  __shared__ int pos0[kWholeChunks][kMaxBucketsSmall];  // first position of chunk c's slots of e
+  __shared__ int off[kMaxBucketsSmall + 1];
+  __shared__ float colw[kWaves][kSmallMaxN];
+  __shared__ BalanceScratch bal;
+  const int N = a.N, T = a.T, Nb = la.Nb, Kt = la.Kt;
+  const int M = T * Kt;  // <= kThreads
+  const int i = threadIdx.x;
+  const int lane = i & 63;
+  const size_t lbase = (size_t)layer * M;
+
+  for (int k = i; k < kWholeChunks * kMaxBucketsSmall; k += kThreads)
+    (&bits[0][0])[k] = 0ull;
+  // the wavefront's column sums of q over its 4 rows (as in block_outputs)
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(qsum), __float_as_uint(qsum),
+                                                    false, false);
+    const float pair = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair),
+                                                    false, false);
+    if (lane < kSmallMaxN) colw[i >> 6][lane] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  }
+  if (i == 0) {  // offsets: exclusive prefix of the counts
+    int run = 0;
+    for (int e = 0; e < Nb; ++e) {
+      off[e] = run;
+      run += hist[e];
+    }
+    off[Nb] = run;
+  }
+  // slot i of the layer (token i / Kt, slot i % Kt): the id route_row wrote
+  int e_i = -1;
+  if (i < M) {
+    const int t = i / Kt, k = i - t * Kt;
+    e_i = k < a.K ? min(max(slot_id[t][k], 0), N - 1) : N + (k - a.K);
+  }
+  __syncthreads();
+  if (e_i >= 0) atomicOr(&bits[i >> 6][e_i], 1ull << (i & 63));
+  if (i < Nb) {
+    la.counts[(size_t)layer * Nb + i] = hist[i];
+    la.offsets[(size_t)layer * (Nb + 1) + i] = off[i];
+  }
+  if (i == 0) la.offsets[(size_t)layer * (Nb + 1) + Nb] = off[Nb];
+  __syncthreads();
+  const int nchunk = (M + 63) / 64;
+  if (i < Nb) {
+    int run = off[i];
+    for (int c = 0; c < nchunk; ++c) {
+      pos0[c][i] = run;
+      run += __popcll(bits[c][i]);
+    }
+  }
+  __syncthreads();
+  if (e_i >= 0) {
+    const int c = i >> 6;
+    const int pos = pos0[c][e_i] + __popcll(bits[c][e_i] & ((1ull << (i & 63)) - 1ull));
+    la.perm[lbase + pos] = i;
+    if (la.inv_perm != nullptr) la.inv_perm[lbase + i] = pos;
+  }
+  if (la.agg_entropy != nullptr && i < kWave) {
+    // batch-mean entropy in wavefront 0: lane = expert
+    float tot = 0.f;
+    if (lane < N) {
+      tot = colw[0][lane];
+      for (int w = 1; w < kWaves; ++w) tot += colw[w][lane];
+    }
+    const float me = lane < N ? tot * (T > 0 ? 1.f / (float)T : 0.f) : 0.f;
+    auto add = [](float x, float y) { return x + y; };
+    const float Z = wave_allreduce(me, add);
+    const float qm = Z > 0.f ? me / Z : 0.f;
+    const float H = wave_allreduce(qm > 0.f ? -qm * log2f(qm) : 0.f, add);
+    if (i == 0) la.agg_entropy[layer] = T > 0 ? H : 0.f;
+  }
+  if (la.stats != nullptr || la.bias_inout != nullptr)
+    block_load_balance(hist, N, la.stats != nullptr ? la.stats + layer : nullptr,
+                       la.bias_inout != nullptr ? la.bias_inout + (size_t)layer * N : nullptr,
+                       la.bias_step, bal);
+}
+
+// One workgroup per layer of at most kWholeTokens tokens and a short depth
+// (at most kWholeSteps steps, so each depth part is at most one step). At
+// more tokens one CU routing them all takes longer than 16-token workgroups
+// on several CUs plus the layout launch (measured: even at 48, behind at 64).
+// Wavefront w forms depth parts w / 4, w / 4 + 4, ... of token block w % 4:
+// each (block, part) with the same steps, in the same order, as the 16-token
+// kernel, and the parts are added in the same order, so every h is bit for
+// bit the one the 16-token kernel forms; the blocks' loads go out together.
+// Every token is then routed at once (one 16-lane row each), and the
+// workgroup does the layout.
+template <bool BF16, bool GROUPED, int MODE>
+__global__ __launch_bounds__(kThreads) void route_layer_kernel(ScoreArgs a, const void* x,
+                                                               const void* W, int d,
+                                                               LayoutArgs la) {
+  __shared__ Cand cand[kWholeTokens][kCandStride];
+  __shared__ int slot_id[kWholeTokens][kMaxSlots];
+  __shared__ float slot_s[kWholeTokens][kMaxSlots];
+  __shared__ int hist[kMaxBuckets];
+  __shared__ __attribute__((aligned(16))) float part_h[kWaves][kWholeTokens][kSmallMaxN];
+  static_assert(kThreads / kRowLanes >= kWholeTokens, "one row per token of the layer");
+
+  const int N = a.N, T = a.T;
+  const int Nb = N + a.n_shared;
+  const int layer = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int r = threadIdx.x & 15;    // token row of the MFMA block / row lane = expert
+  const int row = threadIdx.x >> 4;  // routing row = token
+  const int ntb = (T + kTok - 1) / kTok;
+
+  for (int i = threadIdx.x; i < Nb; i += kThreads) hist[i] = 0;
+  LaneConsts<1> lc;
+  load_lane_consts<1>(a, layer, true, lc);
+  {
+    const size_t esz = BF16 ? 2 : 4;
+    const uint4* wrow = r < N ? reinterpret_cast<const uint4*>(static_cast<const char*>(W) +
+                                                               ((size_t)layer * N + r) * d * esz)
+                              : nullptr;
+    const int g = (threadIdx.x & 63) >> 4;
+    const int tb = wave & 3;
+    if (tb < ntb) {  // ntb <= kWholeTokens / 16 <= 4
+      // tokens past T read row T - 1 (their results are never stored)
+      const int tt = min(tb * kTok + r, T - 1);
+      const uint4* xrow = reinterpret_cast<const uint4*>(static_cast<const char*>(x) +
+                                                         ((size_t)layer * T + tt) * d * esz);
+#pragma unroll
+      for (int p = wave >> 2; p < kWaves; p += 4) {
+        const sm_floatx4 acc = part_affinities<BF16>(xrow, wrow, d, p);
+        *reinterpret_cast<sm_floatx4*>(&part_h[p][tb * kTok + r][4 * g]) = acc;
+      }
+    }
+  }
+  __syncthreads();  // every part stored; the histogram cleared
+
+  float q[1] = {0.f};
+  if (row < ntb * kTok) {  // the wavefronts of the token blocks (rows past T route, unused)
+    float v[1] = {0.f};
+#pragma unroll
+    for (int p = 0; p < kWaves; ++p) v[0] += part_h[p][row][r];
+    const RowLds rs{cand[row], slot_id[row], slot_s[row]};
+    route_row<1, GROUPED, MODE>(a, layer, row, row < T, v, lc, rs, hist, q);
+  }
+  __syncthreads();  // every row routed: histogram and slots complete
+  whole_layer_layout(a, la, layer, q[0], hist, slot_id);
+}
+
+template <bool BF16, bool GROUPED>
+auto pick_layer(const ScoreArgs& a) {
+  return a.score_fn == 1 ? route_layer_kernel<BF16, GROUPED, kSigmoid>
+                         : route_layer_kernel<BF16, GROUPED, kSoftmax>;
+}
+
 template <bool BF16, bool GROUPED>
 auto pick(const ScoreArgs& a) {
   return a.score_fn == 1 ? route_small_kernel<BF16, GROUPED, kSigmoid>
@@ -164,6 +341,11 @@ auto pick(const ScoreArgs& a) {
 }
 
 }  // namespace
+
+bool route_layer_eligible(bool bf16, int T, int d) {
+  return T >= 1 && T <= kWholeTokens &&
+         d <= kWholeSteps * (bf16 ? StepOf<true>::kDepth : StepOf<false>::kDepth);
+}
 
 bool route_small_eligible(bool bf16, int T, int d, int N, int G, bool aligned) {
   if (T < 1 || T > kSmallMaxBlocks * kTok || N > kSmallMaxN || !route_rows_supports(N, G) ||
@@ -173,7 +355,17 @@ bool route_small_eligible(bool bf16, int T, int d, int N, int G, bool aligned) {
 }
 
 hipError_t launch_route_small(const ScoreArgs& a, const void* x, const void* W, int d, bool bf16,
-                              int L, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                              int L, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                              const LayoutArgs* whole) {
+  if (whole != nullptr) {
+    if (!route_layer_eligible(bf16, a.T, d) || whole->Nb > kMaxBucketsSmall ||
+        a.T * whole->Kt > kThreads)
+      return hipErrorInvalidValue;
+    auto k = bf16 ? (a.G > 1 ? pick_layer<true, true>(a) : pick_layer<true, false>(a))
+                  : (a.G > 1 ? pick_layer<false, true>(a) : pick_layer<false, false>(a));
+    hipExtLaunchKernelGGL(k, dim3(1, L), dim3(kThreads), 0, s, ev0, ev1, 0, a, x, W, d, *whole);
+    return hipGetLastError();
+  }
   const dim3 grid((a.T + kTok - 1) / kTok, L);
   auto k = bf16 ? (a.G > 1 ? pick<true, true>(a) : pick<true, false>(a))
                 : (a.G > 1 ? pick<false, true>(a) : pick<false, false>(a));
