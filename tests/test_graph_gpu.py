@@ -9,8 +9,10 @@ everything is synchronised; then each replay's outputs are compared with the
 eager call's bit for bit. No bias update is asked for, so every call does the
 same work. Shapes: the DeepSeek-V3 router (split-K GEMM, 64-token
 selection), a one-layer decode batch (small GEMM tile, 16-token selection),
-the top-2-of-8 router (one-launch GEMM + selection), several layers, and a
-capacity-limited route (its rounds of proposals, ranking and re-layout).
+the top-2-of-8 router (one-launch GEMM + selection), the same router at 20
+tokens (one workgroup per layer that also writes the layout), several
+layers, and a capacity-limited route (its rounds of proposals, ranking and
+re-layout).
 """
 import pytest
 import torch
@@ -26,6 +28,7 @@ CASES = [
     ("dsv3", workloads.scaled(WL["dsv3_group"], T=2048), 0),
     ("decode_one_layer", workloads.scaled(WL["decode_layers"], n_layers=1), 0),
     ("mixtral", workloads.scaled(WL["mixtral_top2"], T=1024), 0),
+    ("mixtral_whole_layer", workloads.scaled(WL["mixtral_top2"], T=20, d=256), 0),
     ("decode_layers", workloads.scaled(WL["decode_layers"], n_layers=4, T=100), 0),
     ("capacity", workloads.scaled(WL["collapse_balance"], T=1024, d=1024), 20),
 ]
