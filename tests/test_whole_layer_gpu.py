@@ -1,9 +1,11 @@
-"""Layers of at most 32 tokens with a short depth on routers with at most 16
-experts (GPU): one workgroup per layer forms the affinities, routes every
-token and writes the layout outputs itself (counts, offsets, perm, inv_perm,
-the batch-mean entropy, load statistics and the in-place bias update), so
-the call is one launch. MOER_ROUTE_WHOLE=0 keeps the separate layout launch
-after the 16-token workgroups.
+"""Small layers on routers with at most 16 experts (GPU): one workgroup per
+layer forms the affinities, routes every token (rows of 4, 8 or 16 lanes, the
+fewest that hold the router's experts) and writes the layout outputs itself
+(counts, offsets, perm, inv_perm, the batch-mean entropy, load statistics and
+the in-place bias update), so the call is one launch. It takes layers of at
+most 64 tokens (at most 8 experts) or 32 (at most 16) with a short depth;
+MOER_ROUTE_WHOLE=0 keeps the separate layout launch after the 16-token
+workgroups.
 
 Bars:
 - against the CPU oracle on the same inputs: h within 1e-3, selections equal
@@ -13,15 +15,20 @@ Bars:
   1e-9 relative) and the sign-step bias update bit-exact from the GPU's
   counts, over three consecutive calls that update the bias in place;
 - against the two-launch path: every output bit for bit, except the
-  batch-mean entropy (its fp32 column sums of q are associated per pass of
-  16 tokens instead of per 16-token block, so a few ulps may differ).
+  batch-mean entropy (within 1e-5: its column sums are associated per
+  workgroup). Narrower rows change no per-token result: a row holds all of
+  the router's experts (N <= RL, K <= N), so each lane holds at most one
+  chosen slot, and a 16-lane row's extra lanes add exact zeros to the same
+  butterfly sums.
 
-Shapes: the fp32 toy router at 32 tokens (4 experts, top-1 softmax), one
-token, every slot a shared one but one (16 slots: 512 layout entries), a
+Shapes: the fp32 toy router itself (64 tokens, 4 experts, top-1 softmax:
+4-lane rows), one token (5 experts: 8-lane rows), 64 tokens of 4 experts
+with 15 shared slots (1024 layout entries, the most one workgroup takes), a
 bf16 top-2-of-8 router over three layers at the deepest short depth (512),
-expert groups with shared slots, ragged batches (17 and 31 tokens), a
-softmax router with 9 experts; and two shapes past the limits (64 tokens;
-depth 1024), which keep the two launches whatever the switch says.
+expert groups in 4-, 8- and 16-lane rows, 16 experts with shared slots, ragged
+batches (17 and 31 tokens), a softmax router with 9 experts; and two shapes
+past the limits (64 tokens of 16 experts; depth 1024), which keep the two
+launches whatever the switch says.
 """
 import numpy as np
 import pytest
@@ -36,15 +43,18 @@ DEV = torch.device("cuda:0")
 WL = workloads.WORKLOADS
 
 SHAPES = [
-    workloads.scaled(WL["tiny_softmax"], T=32),
+    WL["tiny_softmax"],
     workloads.scaled(WL["mixtral_top2"], T=1, d=384, N=5, K=3),
-    workloads.scaled(WL["tiny_softmax"], T=32, d=128, N=16, K=1, n_shared=15),
-    workloads.scaled(WL["mixtral_top2"], T=32, d=512, n_layers=3),
+    workloads.scaled(WL["tiny_softmax"], T=64, d=128, N=4, K=1, n_shared=15),
+    workloads.scaled(WL["mixtral_top2"], T=64, d=512, n_layers=3),
+    workloads.scaled(WL["mixtral_top2"], T=48, d=256, N=8, K=2, n_groups=4, topk_groups=2),
+    workloads.scaled(WL["tiny_softmax"], T=40, d=64, N=4, K=1, n_groups=2, topk_groups=1),
     workloads.scaled(WL["mixtral_top2"], T=24, d=256, N=16, K=4, n_groups=4, topk_groups=2,
                      n_shared=2),
+    workloads.scaled(WL["tiny_softmax"], T=32, d=128, N=16, K=1, n_shared=15),
     workloads.scaled(WL["tiny_softmax"], T=17, d=64, N=3, K=2, n_shared=1),
     workloads.scaled(WL["tiny_softmax"], T=31, d=192, N=9, K=2),
-    WL["tiny_softmax"],
+    workloads.scaled(WL["mixtral_top2"], T=64, d=256, N=16, K=2),
     workloads.scaled(WL["mixtral_top2"], T=20, d=1024),
 ]
 STEPS = 3

@@ -48,18 +48,25 @@ __device__ __forceinline__ V wave_allreduce(V v, Op op) {
 // wave, then the four wave results in wave order: fixed, so deterministic.
 // The first 256 threads of the workgroup do the work; a larger workgroup's
 // other threads only take part in its barriers (same results at any size).
+// NW = 1: one wavefront alone (any one: lane = expert), for N <= 64, with no
+// barrier; the results are bit for bit those of NW = 4 (there the other
+// three waves hold no expert and add exact zeros).
+template <int NW = kBalanceWaves>
 __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_stats_t* out,
                                           float* bias, float u, BalanceScratch& sh) {
+  static_assert(NW == 1 || NW == kBalanceWaves, "one wave or the whole balance group");
+  constexpr int kStride = NW == 1 ? kWave : kBalanceThreads;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const bool worker = threadIdx.x < kBalanceThreads;
-  const int e_first = worker ? (int)threadIdx.x : N;
+  const int tid = NW == 1 ? lane : (int)threadIdx.x;
+  const bool worker = tid < kStride;
+  const int e_first = worker ? tid : N;
   // first pass: total, and the largest count with the lowest expert id on ties
   // (packed as order-preserving count bits << 32 | ~id, so one unsigned max
   // decides both)
   long long tot = 0;
   unsigned long long best = 0;
-  for (int e = e_first; e < N; e += kBalanceThreads) {
+  for (int e = e_first; e < N; e += kStride) {
     tot += c[e];
     const unsigned ord = (unsigned)c[e] ^ 0x80000000u;
     const unsigned long long key =
@@ -68,21 +75,23 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   }
   tot = wave_allreduce(tot, [](long long x, long long y) { return x + y; });
   best = wave_allreduce(best, [](unsigned long long x, unsigned long long y) { return x > y ? x : y; });
-  if (worker && lane == 0) {
-    sh.tot[wave] = tot;
-    sh.best[wave] = best;
-  }
-  __syncthreads();
-  tot = sh.tot[0];
-  best = sh.best[0];
+  if constexpr (NW > 1) {
+    if (worker && lane == 0) {
+      sh.tot[wave] = tot;
+      sh.best[wave] = best;
+    }
+    __syncthreads();
+    tot = sh.tot[0];
+    best = sh.best[0];
 #pragma unroll
-  for (int w = 1; w < kBalanceWaves; ++w) {
-    tot += sh.tot[w];
-    best = sh.best[w] > best ? sh.best[w] : best;
+    for (int w = 1; w < kBalanceWaves; ++w) {
+      tot += sh.tot[w];
+      best = sh.best[w] > best ? sh.best[w] : best;
+    }
   }
 
   if (bias != nullptr) {
-    for (int e = e_first; e < N; e += kBalanceThreads) {
+    for (int e = e_first; e < N; e += kStride) {
       const long long diff = tot - (long long)N * c[e];
       const float step = diff > 0 ? u : (diff < 0 ? -u : 0.f);
       bias[e] = bias[e] + step;
@@ -93,7 +102,7 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   // second pass: entropy of the load distribution and the sum of squared deviations
   const double mean = (double)tot / (double)N;
   double hpart = 0.0, vpart = 0.0;
-  for (int e = e_first; e < N; e += kBalanceThreads) {
+  for (int e = e_first; e < N; e += kStride) {
     const double v = (double)c[e];
     if (tot > 0 && c[e] > 0) {
       const double q = v / (double)tot;
@@ -103,17 +112,23 @@ __device__ inline void block_load_balance(const int32_t* c, int N, moer_load_sta
   }
   hpart = wave_allreduce(hpart, [](double x, double y) { return x + y; });
   vpart = wave_allreduce(vpart, [](double x, double y) { return x + y; });
-  if (worker && lane == 0) {
-    sh.h[wave] = hpart;
-    sh.v[wave] = vpart;
+  if constexpr (NW > 1) {
+    if (worker && lane == 0) {
+      sh.h[wave] = hpart;
+      sh.v[wave] = vpart;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double H = sh.h[0], var = sh.v[0];
+  if (tid == 0) {
+    double H = hpart, var = vpart;
+    if constexpr (NW > 1) {
+      H = sh.h[0];
+      var = sh.v[0];
 #pragma unroll
-    for (int w = 1; w < kBalanceWaves; ++w) {
-      H += sh.h[w];
-      var += sh.v[w];
+      for (int w = 1; w < kBalanceWaves; ++w) {
+        H += sh.h[w];
+        var += sh.v[w];
+      }
     }
     const long long mx = (long long)(int)((unsigned)(best >> 32) ^ 0x80000000u);
     const int am = (int)(0xFFFFFFFFu - (unsigned)(best & 0xFFFFFFFFu));

@@ -415,7 +415,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
     la.hist_shift = moer::kSmallShift;
     // a layer of at most kWholeTokens tokens: one workgroup does the layout too
     const bool whole =
-        moer::route_layer_eligible(d.dtype == MOER_BF16, d.T, d.d) && whole_enabled();
+        moer::route_layer_eligible(d.dtype == MOER_BF16, d.T, d.d, d.N) && whole_enabled();
     MOER_CHECK(moer::launch_route_small(a, io->x, io->w_gate, d.d, d.dtype == MOER_BF16, L, s,
                                         static_cast<hipEvent_t>(io->ev_gemm_begin),
                                         static_cast<hipEvent_t>(io->ev_gemm_end),

@@ -102,14 +102,16 @@ hipError_t launch_route_rows(const ScoreArgs& a, int L, hipStream_t s, int rows)
 // segment totals: ScoreArgs segsum null, LayoutArgs segsum null with
 // hist_shift = kSmallShift. ev0 / ev1 (optional) bracket the launch.
 // With whole != nullptr (route_layer_eligible: layers of at most
-// kWholeTokens tokens and at most kWholeSteps depth steps of 128 (bf16) or 64
+// kWholeTokens tokens for routers of at most 8 experts, kWholeTokensWide for
+// at most 16, and at most kWholeSteps depth steps of 128 (bf16) or 64
 // (fp32); no capacity limit): one workgroup per layer that also writes the
 // layout outputs of *whole (counts, offsets, perm, inv_perm, batch-mean
 // entropy, load statistics, bias update), so no layout launch follows.
-constexpr int kWholeTokens = 32;
+constexpr int kWholeTokens = 64;
+constexpr int kWholeTokensWide = 32;
 constexpr int kWholeSteps = 4;
 bool route_small_eligible(bool bf16, int T, int d, int N, int G, bool aligned);
-bool route_layer_eligible(bool bf16, int T, int d);
+bool route_layer_eligible(bool bf16, int T, int d, int N);
 hipError_t launch_route_small(const ScoreArgs& a, const void* x, const void* W, int d, bool bf16,
                               int L, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                               const LayoutArgs* whole = nullptr);

@@ -48,7 +48,7 @@ constexpr int kRowLanes = 16;
 constexpr int kCandCap = 32;                // candidates ranked in LDS per token
 constexpr int kCandStride = kCandCap + 1;   // entries per row; the pad staggers banks
 
-// ---- DPP helpers (row = 16 lanes) -------------------------------------------
+// ---- DPP helpers ------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
@@ -66,42 +66,70 @@ __device__ __forceinline__ int shr_zero(int v) {
 
 constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kXor3 = 0x1B;        // quad_perm [3,2,1,0]
 constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kMirror = 0x140;     // lane i <-> 15-i within 16
 
-// All 16 lanes of a row receive max / min / sum of the row (bitwise equal in
-// every lane: each step combines a lane with a partner that combines the same
-// two operands).
+// Rows of RL lanes: 16 (one token per 16-lane DPP row), 8 or 4 (two or four
+// tokens per DPP row; only the one-workgroup small-router kernel, whose
+// rows hold at most RL experts, uses them). Every lane of a row receives
+// max / min / sum of the row (bitwise equal in every lane: each step
+// combines a lane with a partner that combines the same two operands).
+template <int RL = kRowLanes>
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp_f<kXor1>(v));
   v = fmaxf(v, dpp_f<kXor2>(v));
-  v = fmaxf(v, dpp_f<kHalfMirror>(v));
-  return fmaxf(v, dpp_f<kMirror>(v));
+  if constexpr (RL >= 8) v = fmaxf(v, dpp_f<kHalfMirror>(v));
+  if constexpr (RL == 16) v = fmaxf(v, dpp_f<kMirror>(v));
+  return v;
 }
+template <int RL = kRowLanes>
 __device__ __forceinline__ float row_min(float v) {
   v = fminf(v, dpp_f<kXor1>(v));
   v = fminf(v, dpp_f<kXor2>(v));
-  v = fminf(v, dpp_f<kHalfMirror>(v));
-  return fminf(v, dpp_f<kMirror>(v));
+  if constexpr (RL >= 8) v = fminf(v, dpp_f<kHalfMirror>(v));
+  if constexpr (RL == 16) v = fminf(v, dpp_f<kMirror>(v));
+  return v;
 }
+template <int RL = kRowLanes>
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp_f<kXor1>(v);
   v += dpp_f<kXor2>(v);
-  v += dpp_f<kHalfMirror>(v);
-  return v + dpp_f<kMirror>(v);
+  if constexpr (RL >= 8) v += dpp_f<kHalfMirror>(v);
+  if constexpr (RL == 16) v += dpp_f<kMirror>(v);
+  return v;
 }
+template <int RL = kRowLanes>
 __device__ __forceinline__ int row_max_i(int v) {
   v = max(v, dpp_i<kXor1>(v));
   v = max(v, dpp_i<kXor2>(v));
-  v = max(v, dpp_i<kHalfMirror>(v));
-  return max(v, dpp_i<kMirror>(v));
+  if constexpr (RL >= 8) v = max(v, dpp_i<kHalfMirror>(v));
+  if constexpr (RL == 16) v = max(v, dpp_i<kMirror>(v));
+  return v;
 }
-// inclusive prefix sum over the row
+// inclusive prefix sum over the row. In 4- and 8-lane rows a shift that
+// would cross into the previous token adds nothing; each shift is taken
+// with every lane active (a DPP read from a lane that EXEC disables returns
+// 0) and masked afterwards.
+template <int RL = kRowLanes>
 __device__ __forceinline__ int row_scan(int v) {
-  v += shr_zero<1>(v);
-  v += shr_zero<2>(v);
-  v += shr_zero<4>(v);
-  return v + shr_zero<8>(v);
+  if constexpr (RL == 16) {
+    v += shr_zero<1>(v);
+    v += shr_zero<2>(v);
+    v += shr_zero<4>(v);
+    return v + shr_zero<8>(v);
+  } else {
+    const int sub = threadIdx.x & (RL - 1);
+    const int d1 = shr_zero<1>(v);
+    v += sub >= 1 ? d1 : 0;
+    const int d2 = shr_zero<2>(v);
+    v += sub >= 2 ? d2 : 0;
+    if constexpr (RL == 8) {
+      const int d4 = shr_zero<4>(v);
+      v += sub >= 4 ? d4 : 0;
+    }
+    return v;
+  }
 }
 // row maximum of 64-bit words held as (hi, lo) halves
 template <int CTRL>
@@ -113,13 +141,30 @@ __device__ __forceinline__ void max_step_u64(unsigned& hi, unsigned& lo) {
     lo = ol;
   }
 }
+template <int RL = kRowLanes>
 __device__ __forceinline__ unsigned long long row_max_u64(unsigned long long v) {
   unsigned hi = (unsigned)(v >> 32), lo = (unsigned)v;
   max_step_u64<kXor1>(hi, lo);
   max_step_u64<kXor2>(hi, lo);
-  max_step_u64<kHalfMirror>(hi, lo);
-  max_step_u64<kMirror>(hi, lo);
+  if constexpr (RL >= 8) max_step_u64<kHalfMirror>(hi, lo);
+  if constexpr (RL == 16) max_step_u64<kMirror>(hi, lo);
   return ((unsigned long long)hi << 32) | lo;
+}
+// Every other lane of a 4- or 8-lane row once: xor 1, 2, 3 inside the quad,
+// then (8 lanes) the other quad through the half mirror (lane i <-> 7 - i)
+// and xor 1, 2, 3 of that. out[0 .. RL-2] receive v from those lanes.
+template <int RL>
+__device__ __forceinline__ void row_partners(int v, int (&out)[RL - 1]) {
+  out[0] = dpp_i<kXor1>(v);
+  out[1] = dpp_i<kXor2>(v);
+  out[2] = dpp_i<kXor3>(v);
+  if constexpr (RL == 8) {
+    const int m = dpp_i<kHalfMirror>(v);
+    out[3] = m;
+    out[4] = dpp_i<kXor1>(m);
+    out[5] = dpp_i<kXor2>(m);
+    out[6] = dpp_i<kXor3>(m);
+  }
 }
 
 // Orderable encoding: larger word <=> larger key, then smaller expert id.
@@ -201,11 +246,11 @@ struct LaneConsts {
   float bias[EPL];
   float offset[EPL];
 };
-template <int EPL, class S = AnyShape>
+template <int EPL, class S = AnyShape, int RL = kRowLanes>
 __device__ __forceinline__ void load_lane_consts(const ScoreArgs& a, int layer, bool with_offset,
                                                  LaneConsts<EPL>& c) {
   const int N = S::n(a);
-  const int e0 = (threadIdx.x & 15) * EPL;
+  const int e0 = (threadIdx.x & (RL - 1)) * EPL;
   const float* b = a.bias != nullptr ? a.bias + (size_t)layer * N : nullptr;
   const float* o = with_offset ? a.offset : nullptr;
   auto fill = [&](const float* src, float (&dst)[EPL]) {
@@ -238,22 +283,22 @@ __device__ __forceinline__ void load_lane_consts(const ScoreArgs& a, int layer, 
 // the clearing made visible by a barrier, before the call). q: this lane's
 // q = s / sum s (0 when dead). All 16 lanes of the row must call together;
 // rows are independent.
-template <int EPL, bool GROUPED, int MODE, int LPG = 0, class S = AnyShape>
+template <int EPL, bool GROUPED, int MODE, int LPG = 0, class S = AnyShape, int RL = kRowLanes>
 __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, bool live,
                                           float (&v)[EPL], const LaneConsts<EPL>& lc,
                                           const RowLds& rs, int* hist, float (&q)[EPL]) {
   const int N = S::n(a), K = S::k(a), T = a.T;
   const int G = S::g(a), Gk = S::gk(a);
   const int Kt = K + S::ns(a);
-  const int rl = threadIdx.x & 15;  // lane within the row
+  const int rl = threadIdx.x & (RL - 1);  // lane within the row
   const int e0 = rl * EPL;
   const bool full = e0 + EPL <= N;  // every expert of this lane exists
   const float NEG_INF = -__builtin_inff();
   const size_t row_off = ((size_t)layer * T + (live ? t : 0)) * N;
 
-  if (rl < kMaxSlots) {
-    rs.slot_id[rl] = 0;
-    rs.slot_s[rl] = 0.f;
+  for (int sl = rl; sl < kMaxSlots; sl += RL) {
+    rs.slot_id[sl] = 0;
+    rs.slot_s[sl] = 0.f;
   }
   // 1. affinities (+ offset) and scores
   if (MODE != kGiven) {
@@ -272,11 +317,11 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     float lm = NEG_INF;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) lm = fmaxf(lm, (full || e0 + j < N) ? v[j] : NEG_INF);
-    m = row_max(lm);
+    m = row_max<RL>(lm);
     float z = 0.f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) z += (full || e0 + j < N) ? exp2_hw((v[j] - m) * kLog2e) : 0.f;
-    inv_z = rcp_hw(row_sum(z));
+    inv_z = rcp_hw(row_sum<RL>(z));
   }
   // scores, keys, and each expert's entropy term s*log2(s) (from quantities
   // the score already has where possible)
@@ -306,8 +351,8 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     ssum += s[j];
     slog += ent[j];
   }
-  ssum = row_sum(ssum);
-  slog = row_sum(slog);
+  ssum = row_sum<RL>(ssum);
+  slog = row_sum<RL>(slog);
   if (MODE == kSoftmax) slog += log2_hw(inv_z) * ssum;
   // hardware reciprocal and log2 (about 1 ulp each), well inside the 1e-4
   // bit entropy tolerance
@@ -332,7 +377,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   bool eligible = true;
   float group_m2 = NEG_INF;  // second largest key of this lane's group
   if (GROUPED) {
-    const int lpg = LPG > 0 ? LPG : (N / G) / EPL;  // lanes per group (power of two, <= 16)
+    const int lpg = LPG > 0 ? LPG : (N / G) / EPL;  // lanes per group (power of two, <= RL)
     const int g = rl / lpg;
     float m1 = lt1, m2 = lt2;
     // merge the group's lanes (lanes of a group are aligned, lpg a power of 2)
@@ -343,8 +388,8 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     };
     if (lpg >= 2) merge(dpp_f<kXor1>(m1), dpp_f<kXor1>(m2));
     if (lpg >= 4) merge(dpp_f<kXor2>(m1), dpp_f<kXor2>(m2));
-    if (lpg >= 8) merge(dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
-    if (lpg >= 16) merge(dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
+    if (RL >= 8 && lpg >= 8) merge(dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
+    if (RL == 16 && lpg >= 16) merge(dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
     // the group as one orderable word: score order bits, then the inverted
     // group id, so one unsigned compare orders (score desc, id asc); lanes
     // past the last group hold 0 and beat no group. (A NaN group score sorts
@@ -352,19 +397,31 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     const unsigned ghi = g < G ? order_bits(m1 + m2, false) : 0u;
     const unsigned glo = g < G ? (unsigned)(0xFFFF - g) : 0u;
     const unsigned long long gkey = ((unsigned long long)ghi << 32) | glo;
-    // rank among the row's groups: rotate the words by whole groups
     int rank = 0;
+    if constexpr (RL == 16) {
+      // rank among the row's groups: rotate the words by whole groups
 #define MOER_ROT(n)                                                                  \
-    if ((n) % lpg == 0) {                                                            \
-      const unsigned oh = (unsigned)dpp_i<0x120 + (n)>((int)ghi);                    \
-      const unsigned ol = (unsigned)dpp_i<0x120 + (n)>((int)glo);                    \
-      rank += ((((unsigned long long)oh << 32) | ol) > gkey) ? 1 : 0;                \
-    }
-    MOER_ROT(1) MOER_ROT(2) MOER_ROT(3) MOER_ROT(4) MOER_ROT(5) MOER_ROT(6) MOER_ROT(7)
-    MOER_ROT(8) MOER_ROT(9) MOER_ROT(10) MOER_ROT(11) MOER_ROT(12) MOER_ROT(13) MOER_ROT(14)
-    MOER_ROT(15)
+      if ((n) % lpg == 0) {                                                          \
+        const unsigned oh = (unsigned)dpp_i<0x120 + (n)>((int)ghi);                  \
+        const unsigned ol = (unsigned)dpp_i<0x120 + (n)>((int)glo);                  \
+        rank += ((((unsigned long long)oh << 32) | ol) > gkey) ? 1 : 0;              \
+      }
+      MOER_ROT(1) MOER_ROT(2) MOER_ROT(3) MOER_ROT(4) MOER_ROT(5) MOER_ROT(6) MOER_ROT(7)
+      MOER_ROT(8) MOER_ROT(9) MOER_ROT(10) MOER_ROT(11) MOER_ROT(12) MOER_ROT(13) MOER_ROT(14)
+      MOER_ROT(15)
 #undef MOER_ROT
-    eligible = g < G && rank < Gk;
+      eligible = g < G && rank < Gk;
+    } else {
+      // every other lane of the row once: a better group is counted once per
+      // lane it spans (lpg), the own group's lanes never (equal words)
+      int ph[RL - 1], pl[RL - 1];
+      row_partners<RL>((int)ghi, ph);
+      row_partners<RL>((int)glo, pl);
+#pragma unroll
+      for (int i = 0; i < RL - 1; ++i)
+        rank += ((((unsigned long long)(unsigned)ph[i] << 32) | (unsigned)pl[i]) > gkey) ? 1 : 0;
+      eligible = g < G && rank < Gk * lpg;
+    }
     group_m2 = m2;
   }
 
@@ -398,23 +455,29 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   if (GROUPED && 2 * Gk == K) {
     // the kept groups' two largest keys are exactly K such experts: lo is
     // the smallest of them (the groups' second keys)
-    lo = row_min(eligible ? group_m2 : __builtin_inff());
+    lo = row_min<RL>(eligible ? group_m2 : __builtin_inff());
   } else {
     // the K-th largest of the eligible lanes' two largest keys (up to 32)
     const float l1 = eligible ? lt1 : NEG_INF, l2 = eligible ? lt2 : NEG_INF;
     int c1 = 1 + (l2 >= l1 ? 1 : 0), c2 = 2;  // values >= l1 / >= l2, own pair included
-#define MOER_CGE(n)                                          \
-    {                                                        \
-      const float o1 = dpp_f<0x120 + (n)>(l1);               \
-      const float o2 = dpp_f<0x120 + (n)>(l2);               \
-      c1 += (o1 >= l1 ? 1 : 0) + (o2 >= l1 ? 1 : 0);         \
-      c2 += (o1 >= l2 ? 1 : 0) + (o2 >= l2 ? 1 : 0);         \
-    }
-    MOER_CGE(1) MOER_CGE(2) MOER_CGE(3) MOER_CGE(4) MOER_CGE(5) MOER_CGE(6) MOER_CGE(7)
-    MOER_CGE(8) MOER_CGE(9) MOER_CGE(10) MOER_CGE(11) MOER_CGE(12) MOER_CGE(13) MOER_CGE(14)
-    MOER_CGE(15)
+    auto count_ge = [&](float o1, float o2) {
+      c1 += (o1 >= l1 ? 1 : 0) + (o2 >= l1 ? 1 : 0);
+      c2 += (o1 >= l2 ? 1 : 0) + (o2 >= l2 ? 1 : 0);
+    };
+    if constexpr (RL == 16) {
+#define MOER_CGE(n) count_ge(dpp_f<0x120 + (n)>(l1), dpp_f<0x120 + (n)>(l2));
+      MOER_CGE(1) MOER_CGE(2) MOER_CGE(3) MOER_CGE(4) MOER_CGE(5) MOER_CGE(6) MOER_CGE(7)
+      MOER_CGE(8) MOER_CGE(9) MOER_CGE(10) MOER_CGE(11) MOER_CGE(12) MOER_CGE(13) MOER_CGE(14)
+      MOER_CGE(15)
 #undef MOER_CGE
-    lo = row_max(fmaxf(c1 >= K ? l1 : NEG_INF, c2 >= K ? l2 : NEG_INF));
+    } else {
+      int p1[RL - 1], p2[RL - 1];
+      row_partners<RL>(__float_as_int(l1), p1);
+      row_partners<RL>(__float_as_int(l2), p2);
+#pragma unroll
+      for (int i = 0; i < RL - 1; ++i) count_ge(__int_as_float(p1[i]), __int_as_float(p2[i]));
+    }
+    lo = row_max<RL>(fmaxf(c1 >= K ? l1 : NEG_INF, c2 >= K ? l2 : NEG_INF));
   }
 
   // candidates: eligible keys >= lo (lo is finite: at least K finite keys
@@ -426,8 +489,8 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
     for (int j = 0; j < EPL; ++j) bits |= key[j] >= lo_f ? 1u << j : 0u;
   }
   const int mine = __builtin_popcount(bits);
-  const int incl = row_scan(mine);
-  const int count = row_max_i(incl);
+  const int incl = row_scan<RL>(mine);
+  const int count = row_max_i<RL>(incl);
   // A row's candidates and slots are private to its wavefront, and a
   // wavefront's LDS operations complete in order: no barrier is needed.
   if (count <= kCandCap) {
@@ -451,7 +514,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
           ++pos;
         }
     }
-    for (int c = rl; c < count; c += kRowLanes) {
+    for (int c = rl; c < count; c += RL) {
       const unsigned long long my = cand_word(rs.cand[c]);
       int r = 0;
 #pragma unroll 4
@@ -476,7 +539,7 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
           bj = j;
         }
       }
-      const unsigned long long win = row_max_u64(best);
+      const unsigned long long win = row_max_u64<RL>(best);
       if (bj >= 0 && best == win) {  // expert ids are unique: one owner lane
         taken |= 1u << bj;
         rs.slot_id[r] = e0 + bj;
@@ -489,24 +552,61 @@ __device__ __forceinline__ void route_row(const ScoreArgs& a, int layer, int t, 
   }
 
   // 5. weights over the chosen slots, then the outputs and the histogram
-  int my_e = 0;
-  float my_s = 0.f;
-  if (rl < K) {
-    my_e = min(max(rs.slot_id[rl], 0), N - 1);  // in range even for non-finite input
-    my_s = rs.slot_s[rl];
-  }
-  const float zsel = row_sum(rl < K ? my_s : 0.f);
-  if (live && rl < Kt) {
-    const size_t o = ((size_t)layer * T + t) * Kt + rl;
-    if (rl < K) {
-      a.idx[o] = my_e;
-      a.w[o] = zsel > 0.f ? my_s / zsel : 1.f / (float)K;
-      atomicAdd(&hist[my_e], 1);
-    } else {
-      a.idx[o] = N + (rl - K);
-      a.w[o] = 1.f;
-      atomicAdd(&hist[N + (rl - K)], 1);
+  // (lane rl takes slots rl, rl + RL, ...: one slot per lane in 16-lane rows)
+  constexpr int kSlotsPerLane = kMaxSlots / RL;
+  int my_e[kSlotsPerLane];
+  float my_s[kSlotsPerLane];
+  float zpart = 0.f;
+#pragma unroll
+  for (int h = 0; h < kSlotsPerLane; ++h) {
+    const int sl = rl + h * RL;
+    my_e[h] = 0;
+    my_s[h] = 0.f;
+    if (sl < K) {
+      my_e[h] = min(max(rs.slot_id[sl], 0), N - 1);  // in range even for non-finite input
+      my_s[h] = rs.slot_s[sl];
+      zpart = h == 0 ? my_s[h] : zpart + my_s[h];
     }
+  }
+  const float zsel = row_sum<RL>(zpart);
+  if (live) {
+#pragma unroll
+    for (int h = 0; h < kSlotsPerLane; ++h) {
+      const int sl = rl + h * RL;
+      if (sl >= Kt) continue;
+      const size_t o = ((size_t)layer * T + t) * Kt + sl;
+      if (sl < K) {
+        a.idx[o] = my_e[h];
+        a.w[o] = zsel > 0.f ? my_s[h] / zsel : 1.f / (float)K;
+        atomicAdd(&hist[my_e[h]], 1);
+      } else {
+        a.idx[o] = N + (sl - K);
+        a.w[o] = 1.f;
+        atomicAdd(&hist[N + (sl - K)], 1);
+      }
+    }
+  }
+}
+
+// The column sums of q over the 64 / RL rows of this wavefront (zero for
+// rows past T), left in lanes 0 .. RL-1 (lane rl: experts rl*EPL ..): in
+// 4- and 8-lane rows first the tokens of each 16-lane DPP row (rotations by
+// 8, then 4), then (row0 + row1) + (row2 + row3) of the DPP rows by lane
+// swaps between rows and between wave halves. Every lane adds its operands
+// in a fixed order, so the sums are deterministic.
+template <int EPL, int RL = kRowLanes>
+__device__ __forceinline__ void wave_column_sums(const float (&q)[EPL], float (&cs)[EPL]) {
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    float x = q[j];
+    if constexpr (RL <= 8) x += dpp_f<0x128>(x);  // row_ror:8
+    if constexpr (RL == 4) x += dpp_f<0x124>(x);  // row_ror:4
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    const float pair = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair),
+                                                    false, false);
+    cs[j] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
   }
 }
 
@@ -523,19 +623,9 @@ __device__ __forceinline__ void block_outputs(const ScoreArgs& a, int layer, int
   const int lane = threadIdx.x & 63;
   const int rl = lane & 15;
   if (a.colpart != nullptr) {
-    // the wavefront's column sums of q over its 4 rows (zero for tokens past
-    // T), (row0 + row1) + (row2 + row3), by lane swaps between rows and
-    // between wave halves; every lane adds the same operands in the same order
+    // the wavefront's column sums of q over its 4 rows (zero for tokens past T)
     float cs[EPL];
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[j]),
-                                                      __float_as_uint(q[j]), false, false);
-      const float pair = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-      const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
-                                                      __float_as_uint(pair), false, false);
-      cs[j] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    }
+    wave_column_sums<EPL>(q, cs);
     if (lane < kRowLanes) {
 #pragma unroll
       for (int j = 0; j < EPL; ++j) colw[threadIdx.x >> 6][rl * EPL + j] = cs[j];

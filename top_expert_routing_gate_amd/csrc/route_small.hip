@@ -177,10 +177,12 @@ constexpr int kWholeChunks = kWholeTokens * kMaxSlots / 64;  // 64-slot chunks o
 //  - perm / inv_perm: the stable order by (expert, token, slot), slot i of
 //    the layer at offset[e] + the earlier slots of expert e, counted with
 //    per-64-slot membership bitmaps (popcounts of the lower bits);
-//  - the entropy of the batch mean of q: column sums of q per wavefront by
-//    lane swaps, the wavefronts added in order, then the entropy in
-//    wavefront 0 with xor butterflies;
-//  - load statistics and the sign-step bias update (block_load_balance).
+//  - the entropy of the batch mean of q: column sums of q per wavefront
+//    (wave_column_sums), the wavefronts added in order, then the entropy in
+//    one wavefront with xor butterflies;
+//  - load statistics and the sign-step bias update (block_load_balance, in
+//    one wavefront).
+template <int RL>
 __device__ void whole_layer_layout(const ScoreArgs& a, const LayoutArgs& la, int layer,
                                    float qsum, const int* hist,
                                    const int (*slot_id)[kMaxSlots]) {
@@ -197,14 +199,12 @@ __device__ void whole_layer_layout(const ScoreArgs& a, const LayoutArgs& la, int
 
   for (int k = i; k < kWholeChunks * kMaxBucketsSmall; k += kThreads)
     (&bits[0][0])[k] = 0ull;
-  // the wavefront's column sums of q over its 4 rows (as in block_outputs)
+  // the wavefront's column sums of q over its 64 / RL rows (lane = expert)
   {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(qsum), __float_as_uint(qsum),
-                                                    false, false);
-    const float pair = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair),
-                                                    false, false);
-    if (lane < kSmallMaxN) colw[i >> 6][lane] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const float qv[1] = {qsum};
+    float cs[1];
+    wave_column_sums<1, RL>(qv, cs);
+    if (lane < RL) colw[i >> 6][lane] = cs[0];
   }
   if (i == 0) {  // offsets: exclusive prefix of the counts
     int run = 0;
@@ -243,8 +243,11 @@ __device__ void whole_layer_layout(const ScoreArgs& a, const LayoutArgs& la, int
     la.perm[lbase + pos] = i;
     if (la.inv_perm != nullptr) la.inv_perm[lbase + i] = pos;
   }
-  if (la.agg_entropy != nullptr && i < kWave) {
-    // batch-mean entropy in wavefront 0: lane = expert
+  // after the last barrier, beside the scatter: the batch-mean entropy in the
+  // last wavefront, the load statistics and bias update in the one before
+  // (one wave each, no barrier; at most 16 experts, lane = expert)
+  const int wave = i >> 6;
+  if (la.agg_entropy != nullptr && wave == kWaves - 1) {
     float tot = 0.f;
     if (lane < N) {
       tot = colw[0][lane];
@@ -255,25 +258,27 @@ __device__ void whole_layer_layout(const ScoreArgs& a, const LayoutArgs& la, int
     const float Z = wave_allreduce(me, add);
     const float qm = Z > 0.f ? me / Z : 0.f;
     const float H = wave_allreduce(qm > 0.f ? -qm * log2f(qm) : 0.f, add);
-    if (i == 0) la.agg_entropy[layer] = T > 0 ? H : 0.f;
+    if (lane == 0) la.agg_entropy[layer] = T > 0 ? H : 0.f;
   }
-  if (la.stats != nullptr || la.bias_inout != nullptr)
-    block_load_balance(hist, N, la.stats != nullptr ? la.stats + layer : nullptr,
-                       la.bias_inout != nullptr ? la.bias_inout + (size_t)layer * N : nullptr,
-                       la.bias_step, bal);
+  if ((la.stats != nullptr || la.bias_inout != nullptr) && wave == kWaves - 2)
+    block_load_balance<1>(hist, N, la.stats != nullptr ? la.stats + layer : nullptr,
+                          la.bias_inout != nullptr ? la.bias_inout + (size_t)layer * N : nullptr,
+                          la.bias_step, bal);
 }
 
-// One workgroup per layer of at most kWholeTokens tokens and a short depth
-// (at most kWholeSteps steps, so each depth part is at most one step). At
-// more tokens one CU routing them all takes longer than 16-token workgroups
-// on several CUs plus the layout launch (measured: even at 48, behind at 64).
-// Wavefront w forms depth parts w / 4, w / 4 + 4, ... of token block w % 4:
-// each (block, part) with the same steps, in the same order, as the 16-token
-// kernel, and the parts are added in the same order, so every h is bit for
-// bit the one the 16-token kernel forms; the blocks' loads go out together.
-// Every token is then routed at once (one 16-lane row each), and the
-// workgroup does the layout.
-template <bool BF16, bool GROUPED, int MODE>
+// One workgroup per layer of at most kWholeTokens tokens (kWholeTokensWide
+// for more than 8 experts) and a short depth (at most kWholeSteps steps, so
+// each depth part is at most one step). Wavefront w forms depth parts w / 4,
+// w / 4 + 4, ... of token block w % 4: each (block, part) with the same
+// steps, in the same order, as the 16-token kernel, and the parts are added
+// in the same order, so every h is bit for bit the one the 16-token kernel
+// forms; the blocks' loads go out together. Every token is then routed at
+// once, in rows of RL lanes, the fewest that hold the router's N experts (4,
+// 8 or 16): T * RL / 64 of the workgroup's wavefronts route. Then the
+// workgroup does the layout. Measured against 16-token workgroups on several
+// CUs plus the layout launch: ahead up to 64 tokens in 4- and 8-lane rows,
+// up to 32 in 16-lane rows.
+template <bool BF16, bool GROUPED, int MODE, int RL>
 __global__ __launch_bounds__(kThreads) void route_layer_kernel(ScoreArgs a, const void* x,
                                                                const void* W, int d,
                                                                LayoutArgs la) {
@@ -282,19 +287,20 @@ __global__ __launch_bounds__(kThreads) void route_layer_kernel(ScoreArgs a, cons
   __shared__ float slot_s[kWholeTokens][kMaxSlots];
   __shared__ int hist[kMaxBuckets];
   __shared__ __attribute__((aligned(16))) float part_h[kWaves][kWholeTokens][kSmallMaxN];
-  static_assert(kThreads / kRowLanes >= kWholeTokens, "one row per token of the layer");
+  static_assert(kThreads / RL >= kWholeTokens, "one row per token of the layer");
 
   const int N = a.N, T = a.T;
   const int Nb = N + a.n_shared;
   const int layer = blockIdx.y;
   const int wave = threadIdx.x >> 6;
-  const int r = threadIdx.x & 15;    // token row of the MFMA block / row lane = expert
-  const int row = threadIdx.x >> 4;  // routing row = token
+  const int r = threadIdx.x & 15;     // token row of the MFMA block
+  const int row = threadIdx.x / RL;   // routing row = token
+  const int rl = threadIdx.x & (RL - 1);  // row lane = expert
   const int ntb = (T + kTok - 1) / kTok;
 
   for (int i = threadIdx.x; i < Nb; i += kThreads) hist[i] = 0;
   LaneConsts<1> lc;
-  load_lane_consts<1>(a, layer, true, lc);
+  load_lane_consts<1, AnyShape, RL>(a, layer, true, lc);
   {
     const size_t esz = BF16 ? 2 : 4;
     const uint4* wrow = r < N ? reinterpret_cast<const uint4*>(static_cast<const char*>(W) +
@@ -320,18 +326,24 @@ __global__ __launch_bounds__(kThreads) void route_layer_kernel(ScoreArgs a, cons
   if (row < ntb * kTok) {  // the wavefronts of the token blocks (rows past T route, unused)
     float v[1] = {0.f};
 #pragma unroll
-    for (int p = 0; p < kWaves; ++p) v[0] += part_h[p][row][r];
+    for (int p = 0; p < kWaves; ++p) v[0] += part_h[p][row][rl];
     const RowLds rs{cand[row], slot_id[row], slot_s[row]};
-    route_row<1, GROUPED, MODE>(a, layer, row, row < T, v, lc, rs, hist, q);
+    route_row<1, GROUPED, MODE, 0, AnyShape, RL>(a, layer, row, row < T, v, lc, rs, hist, q);
   }
   __syncthreads();  // every row routed: histogram and slots complete
-  whole_layer_layout(a, la, layer, q[0], hist, slot_id);
+  whole_layer_layout<RL>(a, la, layer, q[0], hist, slot_id);
 }
 
+template <bool BF16, bool GROUPED, int RL>
+auto pick_layer_rl(const ScoreArgs& a) {
+  return a.score_fn == 1 ? route_layer_kernel<BF16, GROUPED, kSigmoid, RL>
+                         : route_layer_kernel<BF16, GROUPED, kSoftmax, RL>;
+}
 template <bool BF16, bool GROUPED>
 auto pick_layer(const ScoreArgs& a) {
-  return a.score_fn == 1 ? route_layer_kernel<BF16, GROUPED, kSigmoid>
-                         : route_layer_kernel<BF16, GROUPED, kSoftmax>;
+  return a.N <= 4 ? pick_layer_rl<BF16, GROUPED, 4>(a)
+                  : (a.N <= 8 ? pick_layer_rl<BF16, GROUPED, 8>(a)
+                              : pick_layer_rl<BF16, GROUPED, 16>(a));
 }
 
 template <bool BF16, bool GROUPED>
@@ -342,8 +354,8 @@ auto pick(const ScoreArgs& a) {
 
 }  // namespace
 
-bool route_layer_eligible(bool bf16, int T, int d) {
-  return T >= 1 && T <= kWholeTokens &&
+bool route_layer_eligible(bool bf16, int T, int d, int N) {
+  return T >= 1 && T <= (N <= 8 ? kWholeTokens : kWholeTokensWide) && N <= kSmallMaxN &&
          d <= kWholeSteps * (bf16 ? StepOf<true>::kDepth : StepOf<false>::kDepth);
 }
 
@@ -358,8 +370,8 @@ hipError_t launch_route_small(const ScoreArgs& a, const void* x, const void* W, 
                               int L, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                               const LayoutArgs* whole) {
   if (whole != nullptr) {
-    if (!route_layer_eligible(bf16, a.T, d) || whole->Nb > kMaxBucketsSmall ||
-        a.T * whole->Kt > kThreads)
+    if (!route_layer_eligible(bf16, a.T, d, a.N) || whole->Nb > kMaxBucketsSmall ||
+        a.T * whole->Kt > kWholeTokens * kMaxSlots)
       return hipErrorInvalidValue;
     auto k = bf16 ? (a.G > 1 ? pick_layer<true, true>(a) : pick_layer<true, false>(a))
                   : (a.G > 1 ? pick_layer<false, true>(a) : pick_layer<false, false>(a));
