@@ -236,10 +236,11 @@ size_t moer_route_workspace_bytes(const moer_route_desc* desc);
  *                       GEMM and selection launches instead of one launch;
  *   MOER_ROUTE_TINY=0   batches of fewer than 256 blocks of 64 tokens use
  *                       64-token selection workgroups instead of 16 or 32;
- *   MOER_ROUTE_WHOLE=0  layers of at most 32 tokens on routers of at most 16
- *                       experts with d at most 512 (bf16) or 256 (fp32) keep
- *                       a separate layout launch instead of one workgroup
- *                       per layer that also writes the layout outputs;
+ *   MOER_ROUTE_WHOLE=0  layers of at most 64 tokens (routers of at most 8
+ *                       experts) or 32 (at most 16) with d at most 512 (bf16)
+ *                       or 256 (fp32) keep a separate layout launch instead
+ *                       of one workgroup per layer that also writes the
+ *                       layout outputs;
  *   MOER_ROUTE_FUSED=1|2|3  the co-resident fused pass for the large bf16
  *                       routers it takes (off by default: slower here). */
 moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io,
