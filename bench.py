@@ -186,6 +186,8 @@ STAGE_WARMUP, STAGE_CALLS = 5, 20
 MARKER = "balanced_indices_kernel"  # the stage run's marker launch
 STAGES = [("gate_gemm", "gate GEMM"),
           ("route_small", "gate GEMM + selection (one launch, at most 16 experts)"),
+          ("route_layer", "the whole call in one workgroup per layer (GEMM, selection, layout, "
+                          "statistics, bias update)"),
           ("route_rows", "selection (scores, top-k, weights, entropy, histogram)"),
           ("score_topk", "selection (scores, top-k, weights, entropy, histogram)"),
           ("layout_count", "histogram of supplied ids"),
@@ -432,7 +434,7 @@ def summarize_counters(dirs, out, command):
 
 # kernels of one route call of the 16k-token batch
 STEP_KERNELS = ("gate_gemm", "route_rows", "layout_scatter", "zero_ints", "route_fused",
-                "route_small")
+                "route_small", "route_layer")
 
 
 def summarize_traffic(fetch_dir, write_dir, out, command):
