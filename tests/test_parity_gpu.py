@@ -311,12 +311,16 @@ def test_ties_and_signed_zero_scores():
     workloads.scaled(WL["dsv3_group"], T=515),
     workloads.scaled(WL["decode_layers"], T=200, n_layers=2),
     workloads.scaled(WL["mixtral_top2"], T=300),
-], ids=lambda w: w.name)
+    WL["dsv3_group"],
+    workloads.scaled(WL["dsv3_group"], n_groups=1, topk_groups=1),
+], ids=lambda w: f"{w.name}-T{w.T}-G{w.n_groups}")
 def test_heavy_ties_quantized_scores(wl):
     """Scores drawn from a handful of values, so most tokens have dozens of
     exactly tied keys (more than the kernels rank in LDS, which sends them to
     the row-maximum rounds): ids and layout must still match the oracle bit
-    for bit under (key desc, id asc)."""
+    for bit under (key desc, id asc). The 16k-token batches take the 64-token
+    selection kernels (the DeepSeek-V3 shape's own, and the generic one
+    without groups); the smaller ones the 16- and 32-token kernels."""
     g = torch.Generator().manual_seed(77)
     L, T, N = wl.n_layers, wl.T, wl.N
     levels = torch.tensor([0.125, 0.25, 0.5, 0.75])
@@ -785,6 +789,7 @@ def _check_consistent(out, wl):
     workloads.scaled(WL["dsv3_group"], T=700),
     workloads.scaled(WL["decode_layers"], n_layers=2, T=130),
     workloads.scaled(WL["dsv3_group"], T=200, N=96, n_groups=8, topk_groups=4, K=6),
+    WL["dsv3_group"],
 ], ids=lambda w: f"{w.name}-T{w.T}-N{w.N}")
 def test_non_finite_scores_stay_in_range(wl, capacity):
     say(f"[non-finite scores] {wl} capacity={capacity}")
