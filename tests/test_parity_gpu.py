@@ -810,8 +810,23 @@ def test_non_finite_scores_stay_in_range(wl, capacity):
         assert _np(out["counts"])[:, :wl.N].max() <= cap
 
 
-def test_non_finite_hidden_states_stay_in_range():
-    wl = workloads.scaled(WL["dsv3_group"], T=300, d=512)
+# Hidden-state paths: the 256-expert GEMM + selection; the one-launch kernel
+# of routers with at most 16 experts (16-token workgroups); the one-workgroup
+# layer kernel in rows of 8, 4 and 16 lanes (the last one grouped, with
+# shared slots).
+SMALL_PATHS = [
+    workloads.scaled(WL["dsv3_group"], T=300, d=512),
+    workloads.scaled(WL["mixtral_top2"], T=300, d=512),
+    workloads.scaled(WL["mixtral_top2"], T=40, d=256),
+    WL["tiny_softmax"],
+    workloads.scaled(WL["mixtral_top2"], T=24, d=256, N=16, K=4, n_groups=4, topk_groups=2,
+                     n_shared=2),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL_PATHS,
+                         ids=lambda w: f"{w.name}-T{w.T}-d{w.d}-N{w.N}-G{w.n_groups}")
+def test_non_finite_hidden_states_stay_in_range(wl):
     say(f"[non-finite hidden] {wl}")
     inp = workloads.make_inputs(wl)
     x = inp["x"].clone()
@@ -819,10 +834,45 @@ def test_non_finite_hidden_states_stay_in_range():
     x[0, 9, :] = float("nan")
     x[0, 11, 3] = -float("inf")
     out = moer.route(x.to(DEV), inp["W"].to(DEV), K=wl.K, score_fn=wl.score_fn,
-                     n_groups=wl.n_groups, topk_groups=wl.topk_groups,
-                     bias=inp["bias"].to(DEV), want_h=True)
+                     n_groups=wl.n_groups, topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                     bias=inp["bias"].to(DEV), want_h=True, want_load_stats=True)
     torch.cuda.synchronize()
     _check_consistent(out, wl)
+    # the rows without a non-finite element route as they do without the others
+    clean = moer.route(inp["x"].to(DEV), inp["W"].to(DEV), K=wl.K, score_fn=wl.score_fn,
+                       n_groups=wl.n_groups, topk_groups=wl.topk_groups, n_shared=wl.n_shared,
+                       bias=inp["bias"].to(DEV), want_h=True)
+    torch.cuda.synchronize()
+    keep = np.ones(wl.T, dtype=bool)
+    keep[[5, 9, 11]] = False
+    for k in ("h", "topk_idx", "topk_w", "tok_entropy"):
+        assert torch.equal(out[k][0].cpu()[keep], clean[k][0].cpu()[keep]), k
+
+
+@pytest.mark.parametrize("wl", SMALL_PATHS[1:],
+                         ids=lambda w: f"{w.name}-T{w.T}-d{w.d}-N{w.N}-G{w.n_groups}")
+def test_hidden_mode_small_routers_workspace_contents_do_not_matter(wl):
+    # the one-launch small-router kernels and their layout take the caller's
+    # workspace as scratch too: zero-filled and random bytes give the same bits
+    say(f"[small-router workspace] {wl}")
+    inp = workloads.make_inputs(wl)
+    off = None if inp["offset"] is None else inp["offset"].to(DEV)
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    runs = []
+    for fill in ("zeros", "random"):
+        ws = torch.zeros(16 << 20, dtype=torch.uint8, device=DEV)  # ample for these shapes
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, (ws.numel(),), dtype=torch.uint8, generator=gen))
+        bias = inp["bias"].float().to(DEV)
+        out = moer.route(inp["x"].to(DEV), inp["W"].to(DEV), K=wl.K, score_fn=wl.score_fn,
+                         n_groups=wl.n_groups, topk_groups=wl.topk_groups,
+                         n_shared=wl.n_shared, bias=bias, logit_offset=off, want_h=True,
+                         want_load_stats=True, bias_update=bias, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append({k: v.cpu().clone() for k, v in out.items() if torch.is_tensor(v)})
+        runs[-1]["bias"] = bias.cpu()
+    for k in runs[0]:
+        assert torch.equal(runs[0][k], runs[1][k]), f"{k} depends on the workspace"
 
 
 @pytest.mark.parametrize("case", ["capacity", "indices", "decode_layers", "any_groups"])

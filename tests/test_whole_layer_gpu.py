@@ -144,3 +144,26 @@ def test_one_workgroup_layer_matches_oracle_and_two_launches(wl, monkeypatch):
             nb = oracle.bias_update(b.copy(), counts[:wl.N], U)
             assert (_np(b_whole[step + 1][l]) == nb).all(), (step, l, "bias update")
 
+
+# The optional outputs left out (no entropies, no inverse permutation, no
+# affinities): the kernels skip those stores, and every output still asked for
+# keeps its bits. The one-workgroup layer kernel in 4- and 16-lane rows, and
+# the 16-token one-launch kernel with its layout launch.
+@pytest.mark.parametrize("wl", [
+    WL["tiny_softmax"],
+    workloads.scaled(WL["mixtral_top2"], T=24, d=256, N=16, K=4, n_groups=4, topk_groups=2,
+                     n_shared=2),
+    workloads.scaled(WL["mixtral_top2"], T=300, d=512),
+], ids=lambda w: f"{w.name}-T{w.T}-N{w.N}")
+def test_optional_outputs_left_out(wl):
+    say(f"[whole layer, outputs left out] {wl}")
+    inp = workloads.make_inputs(wl)
+    kw = dict(K=wl.K, score_fn=wl.score_fn, n_groups=wl.n_groups, topk_groups=wl.topk_groups,
+              n_shared=wl.n_shared, bias=inp["bias"].float().to(DEV))
+    x, W = inp["x"].to(DEV), inp["W"].to(DEV)
+    full = moer.route(x, W, want_h=True, want_load_stats=True, **kw)
+    bare = moer.route(x, W, want_entropy=False, want_inv_perm=False, **kw)
+    torch.cuda.synchronize()
+    assert "tok_entropy" not in bare and "inv_perm" not in bare
+    for k in ("topk_idx", "topk_w", "counts", "offsets", "perm"):
+        assert torch.equal(bare[k], full[k]), k
