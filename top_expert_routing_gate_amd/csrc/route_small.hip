@@ -10,18 +10,23 @@
 // Affinities h = x W_g^T ("MoE Routing Entropy vs Expert Saturation",
 // Mathematics): the 16 wavefronts take 16 depth parts (steps dealt
 // round-robin) of the same 16 x 16 block and each issues MFMAs with W_g rows
-// as the A operand (16 expert rows, zero past N) and x rows as B, from
-// operands loaded straight into registers, every load of a part in flight
-// before its first MFMA (up to two steps at a time). One load instruction
-// covers 64 contiguous bytes of each of the 16 rows. The 16 parts are added
-// in part order through LDS.
+// as the A operand (16 expert rows, zero past N) and x rows as B, every load
+// of a part in flight before its first MFMA (up to two steps at a time). A
+// step is 256 bytes of each row. Its loads cover whole 128-byte lines, four
+// rows of 256 bytes per instruction, into registers; the wavefront then
+// passes them through its own LDS tile to the MFMA fragment layout (one row
+// per lane, 64 bytes of it per instruction). Loaded in that layout directly,
+// each instruction would touch sixteen half lines, and a CU's loads would
+// take about twice as long. The tiles take 128 KB of LDS, so a CU holds one
+// workgroup at a time. The 16 parts are added in part order through LDS.
 //  - bf16: a step is 128 deep, four v_mfma_f32_16x16x32_bf16 (bf16 products
 //    are exact in fp32 and accumulate in fp32);
 //  - fp32: a step is 64 deep, sixteen v_mfma_f32_16x16x4f32.
-// The lane's 8-element (bf16) or 4-element (fp32) group g of load i feeds
-// the MFMA k-slot g of MFMA i (bf16), or component c of it the k-slot g of
-// MFMA (i, c) (fp32): A and B take the same depth for every k-slot, so each
-// step's MFMAs together sum its depth range once.
+// The lane's 8-element (bf16) or 4-element (fp32) group g of fragment i
+// (16-byte chunk 4i + g of its row) feeds the MFMA k-slot g of MFMA i
+// (bf16), or component c of it the k-slot g of MFMA (i, c) (fp32): A and B
+// take the same depth for every k-slot, so each step's MFMAs together sum
+// its depth range once.
 //
 // The selection is the same as in the standalone kernel; only its workgroup
 // holds 16 tokens (so a launch of T / 16 workgroups fills the chip for the
@@ -97,8 +102,115 @@ __device__ __forceinline__ void mfma_step(const uint4 (&xv)[4], const uint4 (&wv
   }
 }
 
+// One step's whole-line loads: load i is row 4i + lane/16, chunk lane%16 of
+// the step's 256 bytes, at a base the whole wavefront shares (the step's
+// first byte in the block's first row) plus the lane's 32-bit offset ox[i] /
+// ow[i]. W_g takes the first NW loads (NW * 4 >= N rows). Rows past the
+// last (x rows past rows_x, W_g rows past N within those loads) read the
+// last row again, so no branch surrounds a load and nothing uses a loaded
+// value before the tile write: the loads stay in flight together, and the
+// waits before the tile writes count them exactly. The tile reads zero the
+// W_g rows past N.
+struct StepLines {  // named fields, so the values stay in registers
+  uint4 x0, x1, x2, x3, w0, w1, w2, w3;
+};
+template <int NW>
+__device__ __forceinline__ StepLines load_lines(const char* xs, const char* ws,
+                                                const uint32_t (&ox)[4],
+                                                const uint32_t (&ow)[4]) {
+  const auto ld = [](const char* p) { return *reinterpret_cast<const uint4*>(p); };
+  StepLines L{};
+  L.x0 = ld(xs + ox[0]);
+  L.x1 = ld(xs + ox[1]);
+  L.x2 = ld(xs + ox[2]);
+  L.x3 = ld(xs + ox[3]);
+  L.w0 = ld(ws + ow[0]);
+  if constexpr (NW > 1) L.w1 = ld(ws + ow[1]);
+  if constexpr (NW > 2) L.w2 = ld(ws + ow[2]);
+  if constexpr (NW > 3) L.w3 = ld(ws + ow[3]);
+  return L;
+}
+
+// The wavefront's LDS tile for one step: 16 rows x 16 chunks of 16 bytes, x
+// rows (tokens) then W_g rows (experts). Chunk c of row r sits at chunk
+// c ^ r of the row, so the whole-line writes (16 lanes: one row, every
+// chunk) and the fragment reads (16 lanes: every row, one chunk) both fall
+// on distinct banks.
+constexpr int kTileChunks = 16 * 16;
+struct StepTile {
+  uint4 x[kTileChunks];
+  uint4 w[kTileChunks];
+};
+
+// One step through the tile: the lane's whole-line chunks (load i: row
+// 4i + lane/16, chunk lane%16) are written to the tile, and the fragments
+// read back are exactly those load_step would have loaded (MFMA i, k-slot g:
+// chunk 4i + g of row lane%16), so the MFMAs and h are the same bit for bit.
+// W_g rows past N are read as zero (the tile holds a repeat of row N - 1
+// there, or nothing). Rows of the tile are private to the
+// wavefront, and its LDS operations complete in order: no barrier.
+template <bool BF16, int NW>
+__device__ __forceinline__ void staged_mfma_step(const StepLines L, int N, StepTile& tile,
+                                                 sm_floatx4& acc) {
+  const int lane = threadIdx.x & 63;
+  const int a = lane >> 4, kc = lane & 15;  // as loaded: row 4i + a, chunk kc
+  const int r = lane & 15, g = lane >> 4;   // as used: row r, k-slot g
+  const uint4 xl[4] = {L.x0, L.x1, L.x2, L.x3}, wl[4] = {L.w0, L.w1, L.w2, L.w3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + a;
+    tile.x[row * 16 + (kc ^ row)] = xl[i];
+    if (i < NW) tile.w[row * 16 + (kc ^ row)] = wl[i];  // later loads hold no row below N
+  }
+  uint4 xv[4], wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = (4 * i + g) ^ r;
+    xv[i] = tile.x[r * 16 + c];
+    wv[i] = r < N ? tile.w[r * 16 + c] : uint4{0u, 0u, 0u, 0u};
+  }
+  // (the next step's tile writes stay after these reads: the compiler cannot
+  // tell the lane-dependent addresses apart, and the LDS keeps the order)
+  mfma_step<BF16>(xv, wv, acc);
+}
+
+// part_affinities with whole-line loads staged through the wavefront's LDS
+// tile. xblk: the first of the block's rows_x token rows (later rows read
+// the last one; their results are never stored); wblk: W_g's N rows; rowb:
+// bytes per row. NW: W_g load instructions per step (4 * NW >= N); ALL_TWO:
+// every pass of every wavefront has two steps (the step count a multiple of
+// 2 * kWaves), so the second step's loads need no condition either.
+template <bool BF16, int NW, bool ALL_TWO>
+__device__ __forceinline__ sm_floatx4 part_affinities_staged(const char* xblk, int rows_x,
+                                                             const char* wblk, int N,
+                                                             size_t rowb, int d, int w,
+                                                             StepTile& tile) {
+  const int nsteps = d / StepOf<BF16>::kDepth;
+  const int lane = threadIdx.x & 63;
+  uint32_t ox[4], ow[4];  // 16 rows of at most 2^27 bytes (checked by the host)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    ox[i] = (uint32_t)(min(row, rows_x - 1) * rowb) + (uint32_t)(lane & 15) * 16u;
+    ow[i] = (uint32_t)(min(row, N - 1) * rowb) + (uint32_t)(lane & 15) * 16u;
+  }
+  sm_floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = w; s < nsteps; s += 2 * kWaves) {
+    const bool two = ALL_TWO || s + kWaves < nsteps;  // the same for the whole wavefront
+    const size_t s1 = (size_t)s * 256, s2 = (size_t)(s + kWaves) * 256;
+    const StepLines l0 = load_lines<NW>(xblk + s1, wblk + s1, ox, ow);
+    const StepLines l1 = two ? load_lines<NW>(xblk + s2, wblk + s2, ox, ow) : StepLines{};
+    __builtin_amdgcn_sched_barrier(0);  // both steps' loads before any tile work
+    staged_mfma_step<BF16, NW>(l0, N, tile, acc);
+    if (two) staged_mfma_step<BF16, NW>(l1, N, tile, acc);
+  }
+  return acc;
+}
+
 // The wavefront's 16x16 block over depth part w (steps w, w + 16, ...): lane
-// l holds experts 4*(l/16) .. +3 of token l%16.
+// l holds experts 4*(l/16) .. +3 of token l%16. Operands loaded straight in
+// the fragment layout (the one-workgroup layer kernel, whose parts are at
+// most one step).
 template <bool BF16>
 __device__ __forceinline__ sm_floatx4 part_affinities(const uint4* xrow, const uint4* wrow, int d,
                                                       int w) {
@@ -124,7 +236,9 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(ScoreArgs a, cons
   __shared__ float slot_s[kTok][kMaxSlots];
   __shared__ int hist[kMaxBuckets];
   __shared__ __attribute__((aligned(16))) float colw[kWaves][kRowLanes];
-  __shared__ __attribute__((aligned(16))) float part_h[kWaves][kTok][kSmallMaxN];
+  // each wavefront's step tile; afterwards its part of h (16 x 16 fp32)
+  __shared__ StepTile tiles[kWaves];
+  static_assert(sizeof(StepTile) >= kTok * kSmallMaxN * sizeof(float), "part fits the tile");
 
   const int N = a.N, T = a.T;
   const int Nb = N + a.n_shared;
@@ -140,16 +254,32 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(ScoreArgs a, cons
 
   {
     // tokens past T read row T - 1 (their results are never stored)
-    const int tt = min(t0 + r, T - 1);
     const size_t esz = BF16 ? 2 : 4;
-    const uint4* xrow = reinterpret_cast<const uint4*>(static_cast<const char*>(x) +
-                                                       ((size_t)layer * T + tt) * d * esz);
-    const uint4* wrow = r < N ? reinterpret_cast<const uint4*>(static_cast<const char*>(W) +
-                                                               ((size_t)layer * N + r) * d * esz)
-                              : nullptr;
-    const sm_floatx4 acc = part_affinities<BF16>(xrow, wrow, d, wave);
+    const char* xblk = static_cast<const char*>(x) + ((size_t)layer * T + t0) * d * esz;
+    const char* wblk = static_cast<const char*>(W) + (size_t)layer * N * d * esz;
+    // the part index as a wavefront-uniform value, so each step's base is too
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int rows = min(kTok, T - t0);
+    const size_t rowb = (size_t)d * esz;
+    const bool all_two = (d / StepOf<BF16>::kDepth) % (2 * kWaves) == 0;
+    sm_floatx4 acc;
+#define MOER_PARTS(NW)                                                                          \
+    acc = all_two ? part_affinities_staged<BF16, NW, true>(xblk, rows, wblk, N, rowb, d, wu,    \
+                                                           tiles[wu])                           \
+                  : part_affinities_staged<BF16, NW, false>(xblk, rows, wblk, N, rowb, d, wu,   \
+                                                            tiles[wu]);
+    if (N <= 4) {
+      MOER_PARTS(1)
+    } else if (N <= 8) {
+      MOER_PARTS(2)
+    } else {
+      MOER_PARTS(4)
+    }
+#undef MOER_PARTS
     const int g = (threadIdx.x & 63) >> 4;
-    *reinterpret_cast<sm_floatx4*>(&part_h[wave][r][4 * g]) = acc;
+    // the part goes where this wavefront's tile was (its own reads are done)
+    float(*part)[kSmallMaxN] = reinterpret_cast<float(*)[kSmallMaxN]>(&tiles[wave]);
+    *reinterpret_cast<sm_floatx4*>(&part[r][4 * g]) = acc;
   }
   __syncthreads();  // every part stored; the histogram cleared
 
@@ -157,7 +287,8 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(ScoreArgs a, cons
   if (row < kTok) {  // wavefronts 0-3: one row per token
     float v[1] = {0.f};
 #pragma unroll
-    for (int p = 0; p < kWaves; ++p) v[0] += part_h[p][row][r];
+    for (int p = 0; p < kWaves; ++p)
+      v[0] += reinterpret_cast<const float(*)[kSmallMaxN]>(&tiles[p])[row][r];
     const int t = t0 + row;
     const RowLds rs{cand[row], slot_id[row], slot_s[row]};
     route_row<1, GROUPED, MODE>(a, layer, t, t < T, v, lc, rs, hist, q);
@@ -363,6 +494,8 @@ bool route_small_eligible(bool bf16, int T, int d, int N, int G, bool aligned) {
   if (T < 1 || T > kSmallMaxBlocks * kTok || N > kSmallMaxN || !route_rows_supports(N, G) ||
       d < 1 || !aligned)
     return false;
+  // the staged loads address a block's 16 rows with 32-bit offsets
+  if ((long long)kTok * d * (bf16 ? 2 : 4) > (1LL << 31)) return false;
   return d % (bf16 ? StepOf<true>::kDepth : StepOf<false>::kDepth) == 0;
 }
 
