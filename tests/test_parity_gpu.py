@@ -188,6 +188,12 @@ SMALL_ROUTERS = [
     workloads.scaled(WL["tiny_softmax"], T=70, d=2052, N=9, K=2),
     workloads.scaled(WL["tiny_softmax"], T=65, d=12, N=3, K=2, n_shared=1),
     workloads.scaled(WL["mixtral_top2"], T=5000, d=512),
+    # the one-launch kernel's operand loads: one W_g load per step with every
+    # pass two steps (4 experts, 32 steps); two W_g loads with only some
+    # wavefronts taking a second step (24 steps bf16, 20 steps fp32); ragged
+    workloads.scaled(WL["mixtral_top2"], T=333, d=4096, N=4, K=1),
+    workloads.scaled(WL["mixtral_top2"], T=97, d=3072, N=7, K=2),
+    workloads.scaled(WL["tiny_softmax"], T=90, d=1280, N=6, K=2),
 ]
 
 
