@@ -226,7 +226,10 @@ __device__ void scatter_block(const LayoutArgs& a, int layer, int blk, ScatterLd
       const int c = i >> 6;
       const unsigned long long below = sl.bits[c][e] & ((1ull << (i & 63)) - 1ull);
       const int pos = sl.total[e] + sl.pre[e] + sl.chunk_pre[c][e] + __popcll(below);
-      a.perm[lbase + pos] = flat;
+      // pos < T * Kt whenever the block counts agree with the ids; the guard
+      // keeps a disagreement (a block-count mismatch between kernels) inside
+      // the layer's rows, where the parity checks see it
+      if ((unsigned)pos < (unsigned)(a.T * a.Kt)) a.perm[lbase + pos] = flat;
       if (a.inv_perm != nullptr) a.inv_perm[lbase + flat] = pos;
     } else if (a.inv_perm != nullptr) {
       a.inv_perm[lbase + flat] = -1;

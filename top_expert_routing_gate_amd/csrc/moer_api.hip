@@ -411,7 +411,7 @@ moer_status moer_route(const moer_route_desc* desc, const moer_route_io* io, voi
                                  aligned16(io->x) && aligned16(io->w_gate))) {
     a.segsum = nullptr;  // the layout sums the block counts itself
     la.segsum = nullptr;
-    la.nsb = p.nsb_small;
+    la.nsb = (d.T + moer::kSmallTokens - 1) / moer::kSmallTokens;  // its 16-token blocks
     la.hist_shift = moer::kSmallShift;
     // a layer of at most kWholeTokens tokens: one workgroup does the layout too
     const bool whole =
