@@ -3,8 +3,9 @@ scratch is the library's static per-GPU array) against moer_route with a
 caller workspace, through the C ABI: every output bitwise equal, on calls in
 a row, each with a smaller batch than the one before (so each runs on the
 previous call's leftover scratch contents): the 16k-token batch, a 3-layer
-decode batch, and a 20-token top-2-of-8 batch (one workgroup per layer that
-also writes the layout)."""
+decode batch, a 300-token top-2-of-8 batch (the one-launch small-router
+kernel and its layout launch) and a 20-token one (one workgroup per layer
+that also writes the layout)."""
 import numpy as np
 import pytest
 import torch
@@ -62,8 +63,11 @@ def _both(wl):
 def test_noalloc_matches_workspace_route_on_two_calls(order):
     first = workloads.WORKLOADS["collapse_balance"]                        # 16384 tokens
     second = workloads.scaled(workloads.WORKLOADS["decode_layers"], n_layers=3, T=100)
-    third = workloads.scaled(workloads.WORKLOADS["mixtral_top2"], T=20, d=256)
-    for wl in (first, second, third):
+    # a small router: the 16-token one-launch kernel, then a layer short
+    # enough for one workgroup
+    third = workloads.scaled(workloads.WORKLOADS["mixtral_top2"], T=300, d=512)
+    fourth = workloads.scaled(workloads.WORKLOADS["mixtral_top2"], T=20, d=256)
+    for wl in (first, second, third, fourth):
         print(f"[noalloc] {wl.name} L={wl.n_layers} T={wl.T}", flush=True)
         a, b = _both(wl)
         for k in a:
